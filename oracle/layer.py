@@ -1,0 +1,76 @@
+"""Oracle: the whole MoE layer for m tokens, composed from the C stages.
+
+TEST INFRASTRUCTURE ONLY. Per token (each token is independent, so m > 1 and
+prefill are defined exactly as m = 1 repeated):
+  1. q8_1 of the bf16 input row                       [moe_v41.rs, module doc]
+  2. router logits, scores, top-k, weights, header   [moe_v41.rs, fn route_from_logits]
+  3. per picked expert in plan order (ascending id):
+     Q2_K gate/up GEMV, clamped SwiGLU, q8_1, Q3_K down GEMV
+  4. acc = sum over the plan of w*y (f32, in plan order), then + shared expert
+     output, out = bf16(acc)                           [moe_v41.rs, fn shared_side]
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+from . import (bf16_to_f32, combine, expert, header_fields, q8_1, router_logits, select, shared)
+
+
+class ExpertCache:
+    """Host copies of the experts' raw blocks, generated on demand from the spec."""
+
+    def __init__(self, spec: synth.LayerSpec):
+        self.spec = spec
+        self._c = {}
+
+    def __call__(self, e: int):
+        if e not in self._c:
+            self._c[e] = tuple(synth.expert_blocks(self.spec, e, w) for w in ("gate", "up", "down"))
+        return self._c[e]
+
+
+def route(spec: synth.LayerSpec, x_bf16: np.ndarray, gate_w=None, bias=None) -> dict:
+    gate_w = synth.gate_w(spec) if gate_w is None else gate_w
+    bias = synth.bias(spec) if bias is None else bias
+    logits = router_logits(x_bf16, gate_w)
+    hdr, sc = select(spec.shape, logits, bias)
+    return {"logits": logits, "scores": sc, "header": hdr}
+
+
+def layer_forward(spec: synth.LayerSpec, x_bf16: np.ndarray, *, with_shared: bool = True, experts=None,
+                  gate_w=None, bias=None, shared_w=None, keep_experts: bool = True) -> dict:
+    """Full layer for the bf16 rows x [m, dim]. Returns per-token results."""
+    s = spec.shape
+    x_bf16 = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, s.dim)
+    m = x_bf16.shape[0]
+    experts = experts or ExpertCache(spec)
+    r = route(spec, x_bf16, gate_w, bias)
+    status, picks, wts, plan = header_fields(r["header"], s.topk)
+    if with_shared:
+        shared_w = shared_w or tuple(synth.shared_w(spec, w) for w in ("w1", "w3", "w2"))
+    out = dict(r)
+    out.update(xq=[], xd16=[], tok=[], y_routed=np.empty((m, s.dim), np.float32),
+               out_f32=np.empty((m, s.dim), np.float32), out_bf16=np.empty((m, s.dim), np.uint16), shared=[])
+    for t in range(m):
+        xq, xd = q8_1(bf16_to_f32(x_bf16[t]))
+        out["xq"].append(xq)
+        out["xd16"].append(xd)
+        # plan-order weights: the pick-order weights permuted to ascending id
+        order = np.argsort(picks[t], kind="stable")
+        ids = picks[t][order]
+        assert np.array_equal(ids, plan[t])
+        w_plan = wts[t][order]
+        per = []
+        for e in ids:
+            per.append(expert(s, xq, xd, *experts(int(e))))
+        ys = np.stack([p["y"] for p in per])
+        out["y_routed"][t], _ = combine(ys, w_plan)
+        sd = None
+        if with_shared:
+            sh = shared(s, x_bf16[t], *shared_w)
+            out["shared"].append(sh)
+            sd = sh["sd"]
+        out["out_f32"][t], out["out_bf16"][t] = combine(ys, w_plan, sd)
+        out["tok"].append({"ids": ids, "w_plan": w_plan, "experts": per if keep_experts else None})
+    return out
