@@ -1,0 +1,207 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) MoE decode library (libmoe.so).
+ *
+ * The method: the DeepSeek-V4.1-Flash MoE layer at decode as described on
+ * the spark_model documentation pages [moe_v41.rs, module doc]:
+ *   router   logits = bf16 x . bf16 gate weight, f32 accumulation;
+ *            score = sqrt(softplus(logit / temp)); the top-k by
+ *            score + correction bias; weights = the unbiased scores of the
+ *            picks, renormalised and scaled by route_scale
+ *            [moe_v41.rs, fn softplus, fn route_from_logits];
+ *   experts  each pick: gate/up GEMVs on raw Q2_K blocks against the q8_1
+ *            input, a clamped SwiGLU, q8_1 again, a down GEMV on raw Q3_K
+ *            blocks [moe_v41.rs, module doc; Kernels];
+ *   combine  a weighted sum of the expert outputs plus the resident bf16
+ *            shared expert [moe_v41.rs, module doc; fn shared_side].
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The
+ *     library allocates nothing on these paths and keeps no state between
+ *     calls beyond what the caller's workspace holds.
+ *   - bf16 and fp16 values are passed as their uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns; nothing synchronises. Errors found on
+ *     the device (non-finite ranking keys, invalid picks) are reported in the
+ *     header's status word and in the workspace status word, visible once
+ *     the caller synchronises.
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code; moe_last_error()
+ *     gives a thread-local message for the last failing call.
+ *   - Supported shapes: n_routed <= 1024, 1 <= topk <= 8, dim and inter
+ *     multiples of 256 with dim/256 and inter/256 powers of two <= 64 (the
+ *     K-quant kernels give each 256-weight super-block of a row to one lane),
+ *     dim a multiple of 512 is not required. Anything else: MOE_EUNSUPPORTED.
+ *   - Calls that share one workspace on one stream run in order; calls that
+ *     overlap on different streams must use different workspaces.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* null pointer, m out of range, bad cfg value */
+#define MOE_EUNSUPPORTED (-2)  /* shape outside the supported set above        */
+#define MOE_EWORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes   */
+#define MOE_EHIP (-4)          /* a HIP launch or attribute call failed        */
+
+/* Header status bits (word 0 of a token's header). */
+#define MOE_STATUS_MISS 1        /* an expert was not resident (never set: all experts resident) */
+#define MOE_STATUS_NAN_KEY 2     /* a ranking key score+bias was NaN (the pages' "finite scores") */
+#define MOE_STATUS_BAD_PICK 4    /* moe_experts_decode: a pick outside [0,n_routed) or repeated    */
+
+/* Layer configuration [moe_v41.rs, struct MoeV41Cfg]. max_tokens is not a
+ * field: the workspace is sized per call through moe_workspace_bytes. */
+typedef struct moe_cfg {
+  int32_t dim;            /* model width                                   */
+  int32_t inter;          /* expert hidden width                           */
+  int32_t n_routed;       /* routed experts (384)                          */
+  int32_t topk;           /* experts per token (6)                         */
+  int32_t norm_topk_prob; /* 1: renormalise the picked scores              */
+  float gate_temp;        /* logits are divided by this before softplus    */
+  float route_scale;      /* weights are multiplied by this                */
+  float swiglu_limit;     /* SwiGLU clamp L                                */
+} moe_cfg;
+
+/* The resident routed experts: expert e's blocks start at base + e*stride.
+ * Inside: gate (w1) and up (w3) at gate_off / up_off, Q2_K [inter rows]
+ * [dim/256 super-blocks of 84 B], row-major; down (w2) at down_off, Q3_K
+ * [dim rows][inter/256 super-blocks of 110 B]. The raw GGUF blocks are read
+ * as they are (no repacking). base must be 16-byte aligned; stride and the
+ * offsets multiples of 4 [moe_v41.rs, module doc; device_route.rs, fn arena_of]. */
+typedef struct moe_experts {
+  const void* base;
+  uint64_t stride;
+  uint64_t gate_off;
+  uint64_t up_off;
+  uint64_t down_off;
+} moe_experts;
+
+/* One layer's resident weights [moe_v41.rs, struct MoeV41LayerWeights]:
+ * gate_w bf16 [n_routed][dim]; bias f32 [n_routed] (correction bias);
+ * shared expert bf16 sh_w1 [inter][dim], sh_w3 [inter][dim], sh_w2 [dim][inter]. */
+typedef struct moe_layer {
+  const uint16_t* gate_w;
+  const float* bias;
+  moe_experts experts;
+  const uint16_t* sh_w1;
+  const uint16_t* sh_w3;
+  const uint16_t* sh_w2;
+} moe_layer;
+
+/* Words of one token's routing header: 1 + 3*topk int32
+ * [device_route.rs, module doc; fn header_words; fn parse_header]:
+ *   [0]                  status bits (MOE_STATUS_*)
+ *   [1 .. topk]          the picks, in pick (rank) order
+ *   [1+topk .. 2*topk]   the f32 bits of the pick-order weights
+ *   [1+2topk .. 3*topk]  the plan: the picks in ascending expert id
+ *                        (the pages' plan slots; all experts are resident, so
+ *                        an expert's slot is its id) */
+int32_t moe_header_words(const moe_cfg* cfg);
+
+/* Bytes of workspace the calls below need for up to max_m tokens (>= 1).
+ * Returns 0 for an invalid or unsupported cfg. The workspace must be
+ * 256-byte aligned device memory; its contents need no initialisation. */
+size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m);
+
+/* Offsets (bytes from the workspace start) of the intermediate results, for
+ * inspection after a call has completed [the pages' workspace buffers,
+ * moe_v41.rs, struct MoeV41]. Pair p = one (expert, token) of the plan, in
+ * ascending expert id, then ascending token. */
+typedef struct moe_ws_layout {
+  uint64_t total;
+  uint64_t xq;       /* int8  [max_m][dim]        q8_1 codes of x                  */
+  uint64_t xd;       /* fp16  [max_m][dim/32]     q8_1 scales of x                 */
+  uint64_t xs;       /* int32 [max_m][dim/16]     sums of 16 consecutive codes     */
+  uint64_t logits;   /* f32   [max_m][n_routed]                                    */
+  uint64_t scores;   /* f32   [max_m][n_routed]   sqrt(softplus(logit/temp))       */
+  uint64_t plan;     /* int32 plan words (n_u, per-expert and per-pair tables)     */
+  uint64_t g;        /* f32   [pairs][inter]      gate GEMV                        */
+  uint64_t u;        /* f32   [pairs][inter]      up GEMV                          */
+  uint64_t h;        /* f32   [pairs][inter]      clamped SwiGLU                   */
+  uint64_t hq;       /* int8  [pairs][inter]      q8_1 codes of h                  */
+  uint64_t hd;       /* fp16  [pairs][inter/32]   q8_1 scales of h                 */
+  uint64_t hs;       /* int32 [pairs][inter/16]   sums of 16 consecutive codes     */
+  uint64_t y;        /* f32   [pairs][dim]        down GEMV                        */
+  uint64_t sg;       /* f32   [max_m][inter]      shared gate                      */
+  uint64_t su;       /* f32   [max_m][inter]      shared up                        */
+  uint64_t sh;       /* bf16  [max_m][inter]      shared SwiGLU, rounded to bf16   */
+  uint64_t sd;       /* f32   [max_m][dim]        shared down                      */
+  uint64_t yr;       /* f32   [max_m][dim]        routed sum (layer forward)       */
+  uint64_t status;   /* int32 [4] device status words (word 0: OR of MOE_STATUS_*) */
+  int32_t max_pairs; /* max_m * topk                                              */
+  int32_t plan_words;
+} moe_ws_layout;
+
+int moe_workspace_layout(const moe_cfg* cfg, int32_t max_m, moe_ws_layout* out);
+
+/* Route m tokens (A1-A3): router logits, scores, the top-k selection and
+ * the header [moe_v41.rs, fn route_from_logits; device_route.rs, module doc].
+ *   x       bf16 [m][dim]
+ *   gate_w  bf16 [n_routed][dim]
+ *   bias    f32  [n_routed]
+ *   logits  f32  [m][n_routed] output, may be NULL (always also in the workspace)
+ *   header  int32 [m][moe_header_words] output
+ * The logits of a token depend only on that token's row: they are identical
+ * for any m. Also writes the q8_1 of x into the workspace. */
+int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uint16_t* gate_w, const float* bias,
+                     float* logits, int32_t* header, void* ws, size_t ws_bytes, void* stream);
+
+/* The routed experts of m <= 8 tokens (A4-A6 and the routed half of A7):
+ * for every pick in the headers, gate/up on Q2_K, clamped SwiGLU, q8_1,
+ * down on Q3_K; then per token y_routed = the sum over its picks in plan
+ * order (ascending id) of weight * y, in f32 starting from +0. Experts
+ * picked by several tokens are read once for all of them.
+ *   x        bf16 [m][dim]  (quantised to q8_1 again here)
+ *   header   int32 [m][moe_header_words] (as written by moe_route_select)
+ *   y_routed f32  [m][dim] output
+ * A pick outside [0, n_routed) or repeated within a token zeroes that
+ * token's output and sets MOE_STATUS_BAD_PICK in the workspace status. */
+int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const int32_t* header,
+                       const moe_experts* experts, float* y_routed, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer for m <= 8 tokens (A1-A7): route, routed experts, shared
+ * expert (bf16 SwiGLU MLP, its SwiGLU output rounded to bf16), and
+ * out = acc + shared where acc is the routed sum; the shared output is added
+ * after the routed experts [moe_v41.rs, fn shared_side].
+ *   x        bf16 [m][dim]
+ *   out_bf16 bf16 [m][dim] output (round to nearest even of out_f32)
+ *   out_f32  f32  [m][dim] output, may be NULL
+ *   header   int32 [m][moe_header_words] output, may be NULL */
+int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
+                      float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream);
+
+/* The score chain of A3 alone on device data: out[i] = sqrt(softplus(
+ * logits[i] / temp)) with correctly rounded exp, log1p, division and sqrt
+ * [moe_v41.rs, fn softplus, fn route_from_logits]. flags bit 0 forces the
+ * extended-precision path of exp/log1p for every element (checking only). */
+int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream);
+
+/* The same score chain computed on the host CPU by the library's own code
+ * (the device functions compiled for the host); for checking the library's
+ * arithmetic where no GPU is present. All pointers are host pointers. */
+int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags);
+
+/* The clamped SwiGLU of the library on the host: out[i] = silu(min(g,L)) *
+ * clamp(u,-L,L) (checking only, host pointers). */
+int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, float* out);
+
+/* Kernel timing hook: the next launch of kernel `which` (MOE_K_*) on the
+ * calling thread is bracketed by hipEventRecord(begin) / (end) on its
+ * stream. One-shot; pass NULL events to clear. For measurement only. */
+#define MOE_K_GATEUP 1
+#define MOE_K_DOWN 2
+#define MOE_K_ROUTER 3
+int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end);
+
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

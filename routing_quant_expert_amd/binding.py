@@ -1,0 +1,157 @@
+"""ctypes binding of libmoe.so (include/moe.h). Argument marshalling only:
+device tensors are passed as raw pointers with the caller's current HIP
+stream; every computation runs in the library's kernels. There is no
+fallback: if the library is missing the import of a call fails loudly."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_STATUS_MISS = 1
+MOE_STATUS_NAN_KEY = 2
+MOE_STATUS_BAD_PICK = 4
+MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER = 1, 2, 3
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libmoe error {code}: {msg}")
+        self.code = code
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_routed", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32), ("gate_temp", ctypes.c_float),
+                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("stride", ctypes.c_uint64), ("gate_off", ctypes.c_uint64),
+                ("up_off", ctypes.c_uint64), ("down_off", ctypes.c_uint64)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("gate_w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("experts", Experts),
+                ("sh_w1", ctypes.c_void_p), ("sh_w3", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p)]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("total", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u",
+                                                 "h", "hq", "hd", "hs", "y", "sg", "su", "sh", "sd", "yr",
+                                                 "status")] + [("max_pairs", ctypes.c_int32),
+                                                               ("plan_words", ctypes.c_int32)]
+
+
+_lib = None
+_VP = ctypes.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_header_words.restype = ctypes.c_int32
+        L.moe_header_words.argtypes = [ctypes.POINTER(Cfg)]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32]
+        L.moe_workspace_layout.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32, ctypes.POINTER(WsLayout)]
+        L.moe_route_select.argtypes = [ctypes.POINTER(Cfg), _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                       ctypes.c_size_t, _VP]
+        L.moe_experts_decode.argtypes = [ctypes.POINTER(Cfg), _VP, ctypes.c_int32, _VP, ctypes.POINTER(Experts),
+                                         _VP, _VP, ctypes.c_size_t, _VP]
+        L.moe_layer_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), _VP, ctypes.c_int32, _VP, _VP,
+                                        _VP, _VP, ctypes.c_size_t, _VP]
+        L.moe_scores.argtypes = [_VP, ctypes.c_int64, ctypes.c_float, _VP, ctypes.c_int32, _VP]
+        L.moe_scores_host.argtypes = [_VP, ctypes.c_int64, ctypes.c_float, _VP, ctypes.c_int32]
+        L.moe_swiglu_host.argtypes = [_VP, _VP, ctypes.c_int64, ctypes.c_float, _VP]
+        L.moe_time_next_launch.argtypes = [ctypes.c_int32, _VP, _VP]
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(code: int):
+    if code != 0:
+        raise MoeError(code, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+
+
+def cfg_from_shape(shape) -> Cfg:
+    return Cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, int(shape.norm_topk_prob), shape.gate_temp,
+               shape.route_scale, shape.swiglu_limit)
+
+
+def header_words(cfg: Cfg) -> int:
+    return int(lib().moe_header_words(ctypes.byref(cfg)))
+
+
+def workspace_bytes(cfg: Cfg, max_m: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(cfg), max_m))
+
+
+def workspace_layout(cfg: Cfg, max_m: int) -> dict:
+    L = WsLayout()
+    _check(lib().moe_workspace_layout(ctypes.byref(cfg), max_m, ctypes.byref(L)))
+    return {n: getattr(L, n) for n, _ in WsLayout._fields_}
+
+
+def route_select(cfg: Cfg, x, gate_w, bias, header, ws, logits=None, stream=None):
+    m = x.shape[0]
+    _check(lib().moe_route_select(ctypes.byref(cfg), _ptr(x), m, _ptr(gate_w), _ptr(bias), _ptr(logits),
+                                  _ptr(header), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def experts_decode(cfg: Cfg, x, header, experts: Experts, y_routed, ws, stream=None):
+    m = x.shape[0]
+    _check(lib().moe_experts_decode(ctypes.byref(cfg), _ptr(x), m, _ptr(header), ctypes.byref(experts),
+                                    _ptr(y_routed), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer_forward(cfg: Cfg, layer: Layer, x, out_bf16, ws, out_f32=None, header=None, stream=None):
+    m = x.shape[0]
+    _check(lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(layer), _ptr(x), m, _ptr(out_bf16),
+                                   _ptr(out_f32), _ptr(header), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def scores(logits, temp: float, out, flags: int = 0, stream=None):
+    _check(lib().moe_scores(_ptr(logits), logits.numel(), ctypes.c_float(temp), _ptr(out), flags, _stream(stream)))
+
+
+def scores_host(logits: np.ndarray, temp: float, flags: int = 0) -> np.ndarray:
+    a = np.ascontiguousarray(logits, np.float32)
+    out = np.empty_like(a)
+    _check(lib().moe_scores_host(a.ctypes.data, a.size, ctypes.c_float(temp), out.ctypes.data, flags))
+    return out
+
+
+def swiglu_host(g: np.ndarray, u: np.ndarray, limit: float) -> np.ndarray:
+    g = np.ascontiguousarray(g, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    out = np.empty_like(g)
+    _check(lib().moe_swiglu_host(g.ctypes.data, u.ctypes.data, g.size, ctypes.c_float(limit), out.ctypes.data))
+    return out
+
+
+def time_next_launch(which: int, ev_begin, ev_end):
+    """Bracket the next launch of kernel `which` with two torch.cuda.Event objects."""
+    b = None if ev_begin is None else ctypes.c_void_p(ev_begin.cuda_event)
+    e = None if ev_end is None else ctypes.c_void_p(ev_end.cuda_event)
+    _check(lib().moe_time_next_launch(which, b, e))

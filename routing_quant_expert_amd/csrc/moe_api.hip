@@ -1,0 +1,248 @@
+// The C ABI (include/moe.h): argument checks, the workspace layout and the
+// launch sequences of the entry points.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "moe_internal.h"
+#include "moe_math.h"
+
+namespace moe {
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_ev_begin[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local hipEvent_t g_ev_end[4] = {nullptr, nullptr, nullptr, nullptr};
+
+int fail(int code, const char* fmt, const char* a = "", long long b = 0) {
+  char buf[512];
+  snprintf(buf, sizeof buf, fmt, a, b);
+  g_err = buf;
+  return code;
+}
+
+bool pow2_upto64(int v) { return v >= 1 && v <= 64 && (v & (v - 1)) == 0; }
+
+int check_cfg(const moe_cfg* c) {
+  if (!c) return fail(MOE_EINVAL, "cfg is NULL%s%lld");
+  if (!(c->gate_temp > 0.0f) || !std::isfinite(c->gate_temp) || !std::isfinite(c->route_scale) ||
+      !(c->swiglu_limit > 0.0f) || (c->norm_topk_prob != 0 && c->norm_topk_prob != 1))
+    return fail(MOE_EINVAL, "cfg value out of range (gate_temp > 0, finite route_scale, swiglu_limit > 0, norm 0/1)%s%lld");
+  if (c->dim % 256 || c->inter % 256 || !pow2_upto64(c->dim / 256) || !pow2_upto64(c->inter / 256))
+    return fail(MOE_EUNSUPPORTED, "dim and inter must be 256 * a power of two <= 64 %s(dim %lld)", "", c->dim);
+  if (c->topk < 1 || c->topk > kMaxTopk || c->n_routed < c->topk || c->n_routed > kMaxRouted)
+    return fail(MOE_EUNSUPPORTED, "need 1 <= topk <= 8 and topk <= n_routed <= 1024%s (n_routed %lld)", "", c->n_routed);
+  return MOE_OK;
+}
+
+uint64_t take(uint64_t& total, uint64_t bytes) {
+  uint64_t off = total;
+  total = (total + bytes + 255) & ~(uint64_t)255;
+  return off;
+}
+
+int check_ws(const moe_cfg& c, int m, void* ws, size_t ws_bytes, moe_ws_layout* L) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL%s%lld");
+  if ((uintptr_t)ws & 255) return fail(MOE_EINVAL, "workspace must be 256-byte aligned%s%lld");
+  layout_of(c, m, L);
+  if (ws_bytes < L->total)
+    return fail(MOE_EWORKSPACE, "workspace too small%s: need %lld bytes", "", (long long)L->total);
+  return MOE_OK;
+}
+
+bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_EHIP, "HIP error in %s: code %lld", where, (long long)e);
+}
+
+int check_experts(const moe_experts* ex) {
+  if (!ex || !ex->base) return fail(MOE_EINVAL, "experts / experts->base is NULL%s%lld");
+  if (!a16(ex->base) || (ex->stride & 3) || (ex->gate_off & 3) || (ex->up_off & 3) || (ex->down_off & 3))
+    return fail(MOE_EINVAL, "expert arena: base must be 16-byte aligned, stride and offsets multiples of 4%s%lld");
+  return MOE_OK;
+}
+
+}  // namespace
+
+bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
+  const uint64_t m = max_m, P = (uint64_t)max_m * c.topk;
+  uint64_t t = 0;
+  L->xq = take(t, m * c.dim);
+  L->xd = take(t, m * (c.dim / 32) * 2);
+  L->xs = take(t, m * (c.dim / 16) * 4);
+  L->logits = take(t, m * c.n_routed * 4);
+  L->scores = take(t, m * c.n_routed * 4);
+  L->plan_words = PlanView::words((int)P, max_m, c.topk);
+  L->plan = take(t, (uint64_t)L->plan_words * 4);
+  L->g = take(t, P * c.inter * 4);
+  L->u = take(t, P * c.inter * 4);
+  L->h = take(t, P * c.inter * 4);
+  L->hq = take(t, P * c.inter);
+  L->hd = take(t, P * (c.inter / 32) * 2);
+  L->hs = take(t, P * (c.inter / 16) * 4);
+  L->y = take(t, P * c.dim * 4);
+  L->sg = take(t, m * c.inter * 4);
+  L->su = take(t, m * c.inter * 4);
+  L->sh = take(t, m * c.inter * 2);
+  L->sd = take(t, m * c.dim * 4);
+  L->yr = take(t, m * c.dim * 4);
+  L->status = take(t, 16 + m * (1 + 3 * c.topk) * 4);   // status words, then a header scratch
+  L->total = t;
+  L->max_pairs = (int32_t)P;
+  return true;
+}
+
+Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m) {
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  Ws w;
+  w.xq = reinterpret_cast<int8_t*>(b + L.xq);
+  w.xd = reinterpret_cast<uint16_t*>(b + L.xd);
+  w.xs = reinterpret_cast<int32_t*>(b + L.xs);
+  w.logits = reinterpret_cast<float*>(b + L.logits);
+  w.scores = reinterpret_cast<float*>(b + L.scores);
+  w.plan = PlanView{reinterpret_cast<int32_t*>(b + L.plan), L.max_pairs, max_m, c.topk};
+  w.g = reinterpret_cast<float*>(b + L.g);
+  w.u = reinterpret_cast<float*>(b + L.u);
+  w.h = reinterpret_cast<float*>(b + L.h);
+  w.hq = reinterpret_cast<int8_t*>(b + L.hq);
+  w.hd = reinterpret_cast<uint16_t*>(b + L.hd);
+  w.hs = reinterpret_cast<int32_t*>(b + L.hs);
+  w.y = reinterpret_cast<float*>(b + L.y);
+  w.sg = reinterpret_cast<float*>(b + L.sg);
+  w.su = reinterpret_cast<float*>(b + L.su);
+  w.sh = reinterpret_cast<uint16_t*>(b + L.sh);
+  w.sd = reinterpret_cast<float*>(b + L.sd);
+  w.yr = reinterpret_cast<float*>(b + L.yr);
+  w.status = reinterpret_cast<int32_t*>(b + L.status);
+  return w;
+}
+
+void timed_begin(int which, hipStream_t s) {
+  if (which >= 1 && which <= 3 && g_ev_begin[which]) hipEventRecord(g_ev_begin[which], s);
+}
+
+void timed_end(int which, hipStream_t s) {
+  if (which >= 1 && which <= 3 && g_ev_end[which]) {
+    hipEventRecord(g_ev_end[which], s);
+    g_ev_begin[which] = g_ev_end[which] = nullptr;
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_header_words(const moe_cfg* cfg) { return cfg ? 1 + 3 * cfg->topk : 0; }
+
+size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m) {
+  if (check_cfg(cfg) != MOE_OK || max_m < 1) return 0;
+  moe_ws_layout L;
+  layout_of(*cfg, max_m, &L);
+  return L.total;
+}
+
+int moe_workspace_layout(const moe_cfg* cfg, int32_t max_m, moe_ws_layout* out) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!out || max_m < 1) return fail(MOE_EINVAL, "layout output NULL or max_m < 1%s%lld");
+  layout_of(*cfg, max_m, out);
+  return MOE_OK;
+}
+
+int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uint16_t* gate_w, const float* bias,
+                     float* logits, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!x || !gate_w || !bias || !header) return fail(MOE_EINVAL, "x, gate_w, bias and header must be non-NULL%s%lld");
+  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  if (!a16(x) || !a16(gate_w)) return fail(MOE_EINVAL, "x and gate_w must be 16-byte aligned%s%lld");
+  moe_ws_layout L;
+  if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
+  Ws w = ws_view(ws, L, *cfg, m);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_quant_x(x, m, cfg->dim, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if ((e = launch_router(x, m, gate_w, *cfg, w, logits, s)) != hipSuccess) return hip_fail(e, "router");
+  if ((e = launch_select(bias, m, *cfg, w, header, s)) != hipSuccess) return hip_fail(e, "select");
+  return MOE_OK;
+}
+
+int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const int32_t* header,
+                       const moe_experts* experts, float* y_routed, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!x || !header || !y_routed) return fail(MOE_EINVAL, "x, header and y_routed must be non-NULL%s%lld");
+  if (m < 1 || m > kMaxDecodeTokens) return fail(MOE_EINVAL, "decode needs 1 <= m <= 8%s (m %lld)", "", m);
+  if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
+  if (int r = check_experts(experts)) return r;
+  moe_ws_layout L;
+  if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
+  Ws w = ws_view(ws, L, *cfg, m);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_quant_x(x, m, cfg->dim, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
+  if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
+  if ((e = launch_down(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_combine(m, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess) return hip_fail(e, "combine");
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
+                      float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!layer || !x || !out_bf16 || !layer->gate_w || !layer->bias || !layer->sh_w1 || !layer->sh_w2 || !layer->sh_w3)
+    return fail(MOE_EINVAL, "layer weights, x and out_bf16 must be non-NULL%s%lld");
+  if (m < 1 || m > kMaxDecodeTokens) return fail(MOE_EINVAL, "decode needs 1 <= m <= 8%s (m %lld)", "", m);
+  if (!a16(x) || !a16(layer->gate_w) || !a16(layer->sh_w1) || !a16(layer->sh_w2) || !a16(layer->sh_w3))
+    return fail(MOE_EINVAL, "x and the bf16 weights must be 16-byte aligned%s%lld");
+  if (int r = check_experts(&layer->experts)) return r;
+  moe_ws_layout L;
+  if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
+  Ws w = ws_view(ws, L, *cfg, m);
+  int32_t* hdr = header ? header : w.status + 4;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_quant_x(x, m, cfg->dim, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if ((e = launch_router(x, m, layer->gate_w, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router");
+  if ((e = launch_select(layer->bias, m, *cfg, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = launch_plan(hdr, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
+  if ((e = launch_shared_gu(x, m, layer->sh_w1, layer->sh_w3, *cfg, w, s)) != hipSuccess)
+    return hip_fail(e, "shared_gu");
+  if ((e = launch_gateup(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
+  if ((e = launch_down(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_shared_down(m, layer->sh_w2, *cfg, w, s)) != hipSuccess) return hip_fail(e, "shared_down");
+  if ((e = launch_combine(m, *cfg, w, w.sd, out_f32, out_bf16, s)) != hipSuccess) return hip_fail(e, "combine");
+  return MOE_OK;
+}
+
+int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream) {
+  if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
+  hipError_t e = launch_scores(logits, n, temp, out, flags, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "scores");
+}
+
+int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags) {
+  if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
+  for (int64_t i = 0; i < n; ++i) out[i] = score_of(logits[i], temp, (flags & 1) != 0);
+  return MOE_OK;
+}
+
+int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, float* out) {
+  if (n < 0 || (n > 0 && (!g || !u || !out))) return fail(MOE_EINVAL, "bad swiglu arguments%s%lld");
+  for (int64_t i = 0; i < n; ++i) out[i] = swiglu(g[i], u[i], limit);
+  return MOE_OK;
+}
+
+int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end) {
+  if (which < 1 || which > 3) return fail(MOE_EINVAL, "unknown kernel id%s %lld", "", which);
+  g_ev_begin[which] = (hipEvent_t)ev_begin;
+  g_ev_end[which] = (hipEvent_t)ev_end;
+  return MOE_OK;
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal declarations shared by the library's translation units:
+// workspace layout, plan tables and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxDecodeTokens = 8;   // the union-of-experts decode path
+constexpr int kMaxTopk = 8;
+constexpr int kMaxRouted = 1024;
+constexpr int kQ2KBytes = 84;
+constexpr int kQ3KBytes = 110;
+
+// Plan tables inside the workspace (int32 words):
+//   [0] n_u (distinct experts), [1] n_pairs,
+//   then max_pairs entries each of u_expert, u_first, u_npairs, pair_tok,
+//   pair_expert, pair_w (f32 bits), then tok_pairs [max_m][topk] (pair index
+//   of each of a token's picks in ascending expert id; -1 = none).
+struct PlanView {
+  int32_t* base;
+  int max_pairs, max_m, topk;
+  __host__ __device__ int32_t* n_u() const { return base; }
+  __host__ __device__ int32_t* n_pairs() const { return base + 1; }
+  __host__ __device__ int32_t* u_expert() const { return base + 2; }
+  __host__ __device__ int32_t* u_first() const { return base + 2 + max_pairs; }
+  __host__ __device__ int32_t* u_npairs() const { return base + 2 + 2 * max_pairs; }
+  __host__ __device__ int32_t* pair_tok() const { return base + 2 + 3 * max_pairs; }
+  __host__ __device__ int32_t* pair_expert() const { return base + 2 + 4 * max_pairs; }
+  __host__ __device__ float* pair_w() const { return reinterpret_cast<float*>(base + 2 + 5 * max_pairs); }
+  __host__ __device__ int32_t* tok_pairs() const { return base + 2 + 6 * max_pairs; }
+  static int words(int max_pairs, int max_m, int topk) { return 2 + 6 * max_pairs + max_m * topk; }
+};
+
+// Device-side view of the workspace for one call.
+struct Ws {
+  int8_t* xq;
+  uint16_t* xd;
+  int32_t* xs;
+  float* logits;
+  float* scores;
+  PlanView plan;
+  float* g;
+  float* u;
+  float* h;
+  int8_t* hq;
+  uint16_t* hd;
+  int32_t* hs;
+  float* y;
+  float* sg;
+  float* su;
+  uint16_t* sh;
+  float* sd;
+  float* yr;
+  int32_t* status;
+};
+
+bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L);
+Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m);
+
+// ---- launchers (each returns hipError_t of the launch) ----
+hipError_t launch_quant_x(const uint16_t* x, int m, int dim, const Ws& w, hipStream_t s);
+hipError_t launch_router(const uint16_t* x, int m, const uint16_t* gate_w, const moe_cfg& c, const Ws& w,
+                         float* logits_out, hipStream_t s);
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s);
+hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
+                          hipStream_t s);
+hipError_t launch_shared_gu(const uint16_t* x, int m, const uint16_t* w1, const uint16_t* w3, const moe_cfg& c,
+                            const Ws& w, hipStream_t s);
+hipError_t launch_shared_down(int m, const uint16_t* w2, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
+
+// Timing hook (moe_time_next_launch): brackets the next launch of `which`.
+void timed_begin(int which, hipStream_t s);
+void timed_end(int which, hipStream_t s);
+
+}  // namespace moe

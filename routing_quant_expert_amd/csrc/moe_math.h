@@ -1,0 +1,214 @@
+// Correctly rounded f32 exp and log1p, and the f32 helpers of the score and
+// SwiGLU chains. Every function is __host__ __device__: the device build is
+// the product; the host build lets the CPU tests check the same code.
+//
+// Method (own design; the pages only ask that the device selection equal the
+// host reference bit for bit [device_route.rs, module doc]; read here as
+// "every elementary step correctly rounded to f32"):
+//  * fast path: evaluate in float64 with the platform's exp/log1p (error well
+//    under 2 float64 ulps), round to f32, and accept unless the float64 value
+//    lies within 2^-47 (relative) of the midpoint between two f32 neighbours
+//    (Ziv's rounding test: A. Ziv, "Fast evaluation of elementary
+//    mathematical functions with correctly rounded last bit", ACM TOMS 1991);
+//  * slow path: double-double arithmetic (Dekker 1971 products and Knuth's
+//    two-sum): exp by Cody-Waite reduction x = k ln2 + r with ln2 in three
+//    parts, exp(r/256) by its Taylor series to degree 9, then eight
+//    squarings (relative error below 2^-95); log1p by one Newton step on
+//    y - log1p(x) from the float64 estimate, which doubles its precision.
+//    The double-double value is then rounded to f32 exactly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct dd {
+  double hi, lo;
+};
+
+__host__ __device__ inline dd two_sum(double a, double b) {
+  double s = a + b;
+  double bb = s - a;
+  double e = (a - (s - bb)) + (b - bb);
+  return {s, e};
+}
+
+__host__ __device__ inline dd quick_two_sum(double a, double b) {  // |a| >= |b|
+  double s = a + b;
+  return {s, b - (s - a)};
+}
+
+__host__ __device__ inline dd two_prod(double a, double b) {
+  double p = a * b;
+  return {p, __builtin_fma(a, b, -p)};
+}
+
+__host__ __device__ inline dd dd_add(dd a, dd b) {
+  dd s = two_sum(a.hi, b.hi);
+  dd t = two_sum(a.lo, b.lo);
+  s.lo += t.hi;
+  s = quick_two_sum(s.hi, s.lo);
+  s.lo += t.lo;
+  return quick_two_sum(s.hi, s.lo);
+}
+
+__host__ __device__ inline dd dd_mul(dd a, dd b) {
+  dd p = two_prod(a.hi, b.hi);
+  p.lo += a.hi * b.lo + a.lo * b.hi;
+  return quick_two_sum(p.hi, p.lo);
+}
+
+// 1/n! as a double-double, from exact integers: hi = RN(1/f), lo = RN(residual/f).
+__host__ __device__ inline dd inv_factorial(int n) {
+  double f = 1.0;
+  for (int i = 2; i <= n; ++i) f *= (double)i;  // exact for n <= 18
+  double hi = 1.0 / f;
+  double lo = __builtin_fma(-hi, f, 1.0) / f;
+  return {hi, lo};
+}
+
+// exp(x) for a double x in [-746, 710] as a double-double (relative error < 2^-95).
+__host__ __device__ inline dd exp_dd(double x) {
+  const double kInvLn2 = 0x1.71547652b82fep+0;
+  const double kL1 = 0x1.62e42fefa3800p-1;   // ln2 to 42 bits: k*kL1 exact for |k| < 2^11
+  const double kL2 = 0x1.ef35793c76730p-45;
+  const double kL3 = 0x1.f97b57a079a19p-103;
+  double k = rint(x * kInvLn2);
+  double r1 = x - k * kL1;                    // exact (Sterbenz)
+  dd t = two_prod(k, kL2);
+  dd r = two_sum(r1, -t.hi);
+  r.lo += -t.lo - k * kL3;
+  r = quick_two_sum(r.hi, r.lo);
+  dd rs = {r.hi * 0x1p-8, r.lo * 0x1p-8};     // |rs| < 0.00136
+  dd p = inv_factorial(9);
+  for (int n = 8; n >= 0; --n) p = dd_add(dd_mul(p, rs), inv_factorial(n));
+  for (int i = 0; i < 8; ++i) p = dd_mul(p, p);
+  int ki = (int)k;
+  return {ldexp(p.hi, ki), ldexp(p.lo, ki)};
+}
+
+// An f32 value as a double, with the infinity that rounding overflows to
+// standing for 2^128 (so that the midpoint above FLT_MAX is finite).
+__host__ __device__ inline double f32_as_double(float f) {
+  return isinf(f) ? copysign(0x1p128, (double)f) : (double)f;
+}
+
+__host__ __device__ inline float next_toward(float f, double y) {
+  uint32_t b = __builtin_bit_cast(uint32_t, f);
+  double fd = f32_as_double(f);
+  if (y > fd) return (f >= 0.0f) ? __builtin_bit_cast(float, b + 1u) : (b == 0x80000000u ? __builtin_bit_cast(float, 1u) : __builtin_bit_cast(float, b - 1u));
+  return (f > 0.0f) ? __builtin_bit_cast(float, b - 1u) : (b == 0u ? __builtin_bit_cast(float, 0x80000001u) : __builtin_bit_cast(float, b + 1u));
+}
+
+// Midpoint between f and its neighbour toward y (exact in double).
+__host__ __device__ inline double midpoint_toward(float f, double y) {
+  float nb = next_toward(f, y);
+  return 0.5 * (f32_as_double(f) + f32_as_double(nb));
+}
+
+// Ziv's test: true when the double estimate y (relative error < 2^-50) may
+// round differently from the exact value.
+__host__ __device__ inline bool near_midpoint(double y) {
+  float f = (float)y;
+  double fd = f32_as_double(f);
+  if (fd == y) return false;
+  double mid = midpoint_toward(f, y);
+  return fabs(y - mid) <= 0x1p-47 * fabs(y);
+}
+
+// Correct f32 rounding of a normalised double-double.
+__host__ __device__ inline float round_dd_to_f32(dd v) {
+  float f = (float)v.hi;
+  double fd = f32_as_double(f);
+  if (fd == v.hi) {
+    // hi is an f32; the tail is far below half an f32 ulp
+    return f;
+  }
+  double mid = midpoint_toward(f, v.hi);
+  if (v.hi != mid) return f;   // |hi - mid| >= one double ulp > |lo|
+  // hi sits exactly on the midpoint: the tail decides
+  float nb = next_toward(f, v.hi);
+  bool toward_nb_side = (v.lo > 0.0) == (f32_as_double(nb) > fd);
+  if (v.lo == 0.0) return (__builtin_bit_cast(uint32_t, f) & 1u) ? nb : f;
+  return toward_nb_side ? nb : f;
+}
+
+// RN32(exp(x)) for any f32 x.
+__host__ __device__ inline float exp_cr(float x, bool force_slow = false) {
+  if (isnan(x)) return x;
+  if (x > 89.0f) return __builtin_inff();
+  if (x < -104.0f) return 0.0f;   // exp(x) < 2^-150: rounds to +0
+  double y = exp((double)x);
+  if (!force_slow && !near_midpoint(y)) return (float)y;
+  return round_dd_to_f32(exp_dd((double)x));
+}
+
+// RN32(log1p(x)) for f32 x >= -1 (NaN for x < -1).
+__host__ __device__ inline float log1p_cr(float x, bool force_slow = false) {
+  if (isnan(x) || isinf(x)) return x > 0.0f ? x : (isnan(x) ? x : __builtin_nanf(""));
+  if (x < -1.0f) return __builtin_nanf("");
+  if (x == -1.0f) return -__builtin_inff();
+  if (fabsf(x) < 0x1p-24f) return x;   // |log1p(x) - x| < x^2/2: x is the nearest f32
+  double y0 = log1p((double)x);
+  if (!force_slow && !near_midpoint(y0)) return (float)y0;
+  // Newton on f(y) = (1+x) e^-y - 1: y1 = y0 + (1+x) e^-y0 - 1
+  dd u = two_sum(1.0, (double)x);
+  dd e = exp_dd(-y0);
+  dd p = dd_mul(u, e);
+  dd r = dd_add(p, dd{-1.0, 0.0});
+  dd y = dd_add(dd{y0, 0.0}, r);
+  return round_dd_to_f32(y);
+}
+
+// 16-byte streaming load (non-temporal: read once, do not keep in the caches).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_nt16(const void* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// f32 operations that must not be contracted into FMAs.
+__host__ __device__ inline float fmul(float a, float b) { return a * b; }
+__host__ __device__ inline float fadd(float a, float b) { return a + b; }
+
+// score = sqrt(softplus(logit / temp)), softplus(z) = z > 20 ? z : log1p(exp(z))
+// [moe_v41.rs, fn softplus, fn route_from_logits]. sqrt and the division are
+// correctly rounded in f32: through float64 (53 >= 2*24+2, so the double
+// rounding is harmless).
+__host__ __device__ inline float score_of(float logit, float temp, bool force_slow = false) {
+  float z = (float)((double)logit / (double)temp);
+  float sp = z > 20.0f ? z : log1p_cr(exp_cr(z, force_slow), force_slow);
+  return (float)sqrt((double)sp);
+}
+
+// Clamped SwiGLU: silu(min(g, L)) * clamp(u, -L, L), silu(z) = z / (1 + exp(-z)).
+__host__ __device__ inline float swiglu(float g, float u, float L) {
+  float zg = g > L ? L : g;
+  float e = exp_cr(-zg);
+  float den = fadd(1.0f, e);
+  float silu = (float)((double)zg / (double)den);
+  float uc = u > L ? L : (u < -L ? -L : u);
+  return fmul(silu, uc);
+}
+
+// f32 -> bf16 round to nearest even on the bits [moe_v41.rs, fn bf16_bytes].
+__host__ __device__ inline uint16_t bf16_rne(float f) {
+  uint32_t b = __builtin_bit_cast(uint32_t, f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__host__ __device__ inline float bf16_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// q8_1 of one value given the block's f32 scale d (amax/127): roundf(x/d),
+// half away from zero; 0 when amax == 0.
+__host__ __device__ inline int q8_code(float x, float d) {
+  if (d == 0.0f) return 0;
+  float v = (float)((double)x / (double)d);
+  float t = truncf(v);
+  if (fabsf(v - t) >= 0.5f) t += copysignf(1.0f, v);
+  return (int)t;
+}
+
+}  // namespace moe

@@ -74,16 +74,56 @@ def stream_start(seed: int, tag: int) -> int:
     return _mix_scalar(((seed ^ tag) + GOLDEN) & M64)
 
 
+_CHUNK = 1 << 18
+_scratch = {}
+
+
+def _buf(name: str, n: int, dtype) -> np.ndarray:
+    """Reused scratch arrays (fresh allocations are slow where page faults are costly)."""
+    b = _scratch.get(name)
+    if b is None or b.size < n or b.dtype != dtype:
+        b = np.empty(max(n, _CHUNK), dtype)
+        _scratch[name] = b
+    return b[:n]
+
+
+_count = np.arange(1, 2 * _CHUNK + 1, dtype=np.uint64)
+
+
+def _counting(n: int) -> np.ndarray:
+    """1, 2, ..., n (uint64), from a cached array."""
+    global _count
+    if _count.size < n:
+        _count = np.arange(1, n + 1, dtype=np.uint64)
+    return _count[:n]
+
+
+def _draws_into(z: np.ndarray, s0: np.uint64, i0: int) -> None:
+    """z[k] = mix(s0 + (i0+k+1)*G) for the length of z (in place)."""
+    n = z.size
+    ar = _counting(n)
+    t = _buf("tmp", n, np.uint64)
+    with np.errstate(over="ignore"):
+        np.add(ar, np.uint64(i0), out=z)
+        np.multiply(z, np.uint64(GOLDEN), out=z)
+        np.add(z, s0, out=z)
+        np.right_shift(z, np.uint64(30), out=t)
+        np.bitwise_xor(z, t, out=z)
+        np.multiply(z, np.uint64(MIX1), out=z)
+        np.right_shift(z, np.uint64(27), out=t)
+        np.bitwise_xor(z, t, out=z)
+        np.multiply(z, np.uint64(MIX2), out=z)
+        np.right_shift(z, np.uint64(31), out=t)
+        np.bitwise_xor(z, t, out=z)
+
+
 def draws(seed: int, tag: int, i0: int, n: int) -> np.ndarray:
     """Draws i0 .. i0+n-1 of stream (seed, tag) as uint64."""
     s0 = np.uint64(stream_start(seed, tag))
-    with np.errstate(over="ignore"):
-        idx = np.arange(i0 + 1, i0 + n + 1, dtype=np.uint64)
-        z = s0 + idx * np.uint64(GOLDEN)
-        z = (z ^ (z >> np.uint64(30))) * np.uint64(MIX1)
-        z = (z ^ (z >> np.uint64(27))) * np.uint64(MIX2)
-        z = z ^ (z >> np.uint64(31))
-    return z
+    out = np.empty(n, np.uint64)
+    for c0 in range(0, n, _CHUNK):
+        _draws_into(out[c0:c0 + _CHUNK], s0, i0 + c0)
+    return out
 
 
 def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
@@ -97,19 +137,41 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _normal_chunk(s0: np.uint64, i0: int, n: int, out: np.ndarray) -> None:
+    r = _buf("nraw", 6 * n, np.uint64)
+    _draws_into(r, s0, 6 * i0)
+    r = r.reshape(n, 6)
+    lo = _buf("nlo", 6 * n, np.uint64).reshape(n, 6)
+    np.bitwise_and(r, np.uint64(0xFFFFFFFF), out=lo)
+    np.right_shift(r, np.uint64(32), out=r)
+    np.add(r, lo, out=r)                     # each < 2^33, six of them < 2^36: no wrap
+    s = r.sum(axis=1, dtype=np.uint64).astype(np.int64) - np.int64(6 << 32)
+    np.multiply(s.astype(np.float64), 2.0 ** -32, out=out)
+
+
 def normal_f64(seed: int, tag: int, i0: int, n: int) -> np.ndarray:
     """Irwin-Hall N(0,1) values i0..i0+n-1 as exact float64."""
-    r = draws(seed, tag, 6 * i0, 6 * n).reshape(n, 6)
-    lo = (r & np.uint64(0xFFFFFFFF)).astype(np.int64)
-    hi = (r >> np.uint64(32)).astype(np.int64)
-    s = lo.sum(axis=1) + hi.sum(axis=1) - np.int64(6 << 32)
-    return s.astype(np.float64) * (2.0 ** -32)
+    s0 = np.uint64(stream_start(seed, tag))
+    out = np.empty(n, np.float64)
+    ch = _CHUNK // 4
+    for c0 in range(0, n, ch):
+        c1 = min(n, c0 + ch)
+        _normal_chunk(s0, i0 + c0, c1 - c0, out[c0:c1])
+    return out
 
 
 def normal_bf16(seed: int, tag: int, i0: int, n: int, sigma: float) -> np.ndarray:
-    z = normal_f64(seed, tag, i0, n)
-    v = (z * np.float64(sigma)).astype(np.float32)
-    return f32_to_bf16_bits(v)
+    s0 = np.uint64(stream_start(seed, tag))
+    out = np.empty(n, np.uint16)
+    ch = _CHUNK // 4
+    z = _buf("nz", ch, np.float64)
+    for c0 in range(0, n, ch):
+        c1 = min(n, c0 + ch)
+        zz = z[:c1 - c0]
+        _normal_chunk(s0, i0 + c0, c1 - c0, zz)
+        np.multiply(zz, np.float64(sigma), out=zz)
+        out[c0:c1] = f32_to_bf16_bits(zz.astype(np.float32))
+    return out
 
 
 def uniform_f32(seed: int, tag: int, i0: int, n: int, lo: float, span: float) -> np.ndarray:

@@ -1,0 +1,110 @@
+"""CPU checks of libmoe.so: it loads, exports every symbol include/moe.h
+declares, rejects bad arguments before touching a GPU, and its own
+arithmetic (the device score/SwiGLU code compiled for the host) matches the
+oracle bit for bit."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import routing_quant_expert_amd as R
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    L = R.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_workspace_queries():
+    c = R.cfg_from_shape(synth.SHAPE_DS41)
+    n1, n8 = R.workspace_bytes(c, 1), R.workspace_bytes(c, 8)
+    assert 0 < n1 < n8
+    L = R.workspace_layout(c, 8)
+    offs = [L[k] for k in ("xq", "xd", "xs", "logits", "scores", "plan", "g", "u", "h", "hq", "hd", "hs", "y",
+                           "sg", "su", "sh", "sd", "yr", "status")]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs) and L["total"] == n8
+    assert L["max_pairs"] == 48
+    assert R.header_words(c) == 19
+
+
+@pytest.mark.parametrize("field,value", [("dim", 300), ("dim", 256 * 3), ("inter", 0), ("topk", 9),
+                                         ("n_routed", 2000)])
+def test_unsupported_shapes_are_rejected(field, value):
+    c = R.cfg_from_shape(synth.SHAPE_TINY)
+    setattr(c, field, value)
+    assert R.workspace_bytes(c, 1) == 0
+    with pytest.raises(R.MoeError) as ei:
+        R.workspace_layout(c, 1)
+    assert ei.value.code in (-1, -2)
+
+
+class _FakePtr:
+    """Stands in for a device tensor in calls that must fail validation."""
+
+    def __init__(self, addr, n=1, shape=(1,)):
+        self.addr, self.n, self.shape = addr, n, shape
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def test_argument_errors_before_any_launch():
+    c = R.cfg_from_shape(synth.SHAPE_TINY)
+    need = R.workspace_bytes(c, 1)
+    x = _FakePtr(4096, shape=(1, 512))
+    small = _FakePtr(1 << 20, n=need - 256)
+    with pytest.raises(R.MoeError) as ei:   # workspace too small
+        R.route_select(c, x, _FakePtr(8192), _FakePtr(16384), _FakePtr(32768), small, stream=0)
+    assert ei.value.code == -3
+    with pytest.raises(R.MoeError) as ei:   # misaligned workspace
+        R.route_select(c, x, _FakePtr(8192), _FakePtr(16384), _FakePtr(32768), _FakePtr((1 << 20) + 4, n=need),
+                       stream=0)
+    assert ei.value.code == -1
+    with pytest.raises(R.MoeError) as ei:   # decode m > 8
+        R.experts_decode(c, _FakePtr(4096, shape=(9, 512)), _FakePtr(8192), R.Experts(1 << 20, 0, 0, 0, 0),
+                         _FakePtr(16384), _FakePtr(1 << 24, n=1 << 30), stream=0)
+    assert ei.value.code == -1
+    with pytest.raises(R.MoeError) as ei:   # misaligned expert arena
+        R.experts_decode(c, x, _FakePtr(8192), R.Experts((1 << 20) + 8, 0, 0, 0, 0), _FakePtr(16384),
+                         _FakePtr(1 << 24, n=1 << 30), stream=0)
+    assert ei.value.code == -1
+
+
+def test_library_score_chain_matches_oracle_on_host():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.normal(0, 1.28, 400_000), rng.uniform(-110, 25, 300_000), rng.normal(0, 8, 100_000),
+                        np.ldexp(rng.uniform(-1, 1, 100_000), rng.integers(-140, 5, 100_000))]).astype(np.float32)
+    want = oracle.scores(x, 1.0)
+    for flags in (0, 1):           # 1: every exp/log1p through the double-double path
+        got = R.scores_host(x, 1.0, flags)
+        bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+        assert bad.size == 0, (flags, x[bad[:5]], got[bad[:5]], want[bad[:5]])
+    got = R.scores_host(x[:100_000], 0.7)
+    assert np.array_equal(got.view(np.uint32), oracle.scores(x[:100_000], 0.7).view(np.uint32))
+
+
+def test_library_swiglu_matches_oracle_on_host():
+    rng = np.random.default_rng(6)
+    g = np.concatenate([rng.normal(0, 2, 200_000), rng.uniform(-120, 20, 50_000)]).astype(np.float32)
+    u = rng.normal(0, 4, g.size).astype(np.float32)
+    assert np.array_equal(R.swiglu_host(g, u, 7.0).view(np.uint32), oracle.swiglu(g, u, 7.0).view(np.uint32))
