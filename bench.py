@@ -91,6 +91,7 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's expert kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
@@ -125,19 +126,23 @@ def main():
 
     ev = HipEvents()
     K = args.steps
-    gu = ev.create(2 * K)
-    dn = ev.create(2 * K)
+    every = max(1, args.time_every)
+    nt = (K + every - 1) // every
+    gu = ev.create(2 * nt)
+    dn = ev.create(2 * nt)
     L = R.lib()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        L.moe_time_next_launch(R.MOE_K_GATEUP, gu[2 * i], gu[2 * i + 1])
-        L.moe_time_next_launch(R.MOE_K_DOWN, dn[2 * i], dn[2 * i + 1])
+        if i % every == 0:          # a sample of the steps brackets its expert kernels with events
+            j = i // every
+            L.moe_time_next_launch(R.MOE_K_GATEUP, gu[2 * j], gu[2 * j + 1])
+            L.moe_time_next_launch(R.MOE_K_DOWN, dn[2 * j], dn[2 * j + 1])
         step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gu_ms = np.array([ev.elapsed_ms(gu[2 * i], gu[2 * i + 1]) for i in range(K)])
-    dn_ms = np.array([ev.elapsed_ms(dn[2 * i], dn[2 * i + 1]) for i in range(K)])
+    gu_ms = np.array([ev.elapsed_ms(gu[2 * j], gu[2 * j + 1]) for j in range(nt)])
+    dn_ms = np.array([ev.elapsed_ms(dn[2 * j], dn[2 * j + 1]) for j in range(nt)])
     ev.destroy(gu + dn)
 
     wall = t1 - t0
@@ -166,7 +171,7 @@ def main():
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_gateup",
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg * 1e6},
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg * 1e6, "timed_launches": int(nt)},
         "routed_gemvs": {"gateup_us": gu_avg * 1e6, "down_us": dn_avg * 1e6, "bytes": gu_bytes + dn_bytes,
                          "achieved_gbs": routed_gbs, "frac": routed_gbs / HBM_PEAK_GBS,
                          "gateup_p10_p90_us": [float(np.percentile(gu_ms, 10) * 1e3),

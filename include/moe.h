@@ -71,8 +71,8 @@ typedef struct moe_cfg {
  * Inside: gate (w1) and up (w3) at gate_off / up_off, Q2_K [inter rows]
  * [dim/256 super-blocks of 84 B], row-major; down (w2) at down_off, Q3_K
  * [dim rows][inter/256 super-blocks of 110 B]. The raw GGUF blocks are read
- * as they are (no repacking). base must be 16-byte aligned; stride and the
- * offsets multiples of 4 [moe_v41.rs, module doc; device_route.rs, fn arena_of]. */
+ * as they are (no repacking). base, stride and the offsets must be multiples
+ * of 16 bytes [moe_v41.rs, module doc; device_route.rs, fn arena_of]. */
 typedef struct moe_experts {
   const void* base;
   uint64_t stride;

@@ -60,8 +60,8 @@ int hip_fail(hipError_t e, const char* where) {
 
 int check_experts(const moe_experts* ex) {
   if (!ex || !ex->base) return fail(MOE_EINVAL, "experts / experts->base is NULL%s%lld");
-  if (!a16(ex->base) || (ex->stride & 3) || (ex->gate_off & 3) || (ex->up_off & 3) || (ex->down_off & 3))
-    return fail(MOE_EINVAL, "expert arena: base must be 16-byte aligned, stride and offsets multiples of 4%s%lld");
+  if (!a16(ex->base) || (ex->stride & 15) || (ex->gate_off & 15) || (ex->up_off & 15) || (ex->down_off & 15))
+    return fail(MOE_EINVAL, "expert arena: base, stride and offsets must be multiples of 16 bytes%s%lld");
   return MOE_OK;
 }
 
@@ -164,9 +164,9 @@ int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uin
   Ws w = ws_view(ws, L, *cfg, m);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_quant_x(x, m, cfg->dim, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
-  if ((e = launch_router(x, m, gate_w, *cfg, w, logits, s)) != hipSuccess) return hip_fail(e, "router");
-  if ((e = launch_select(bias, m, *cfg, w, header, s)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = launch_front(x, m, gate_w, nullptr, nullptr, *cfg, w, logits, s)) != hipSuccess)
+    return hip_fail(e, "front");
+  if ((e = launch_select(bias, m, *cfg, w, header, false, s)) != hipSuccess) return hip_fail(e, "select");
   return MOE_OK;
 }
 
@@ -182,10 +182,10 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   Ws w = ws_view(ws, L, *cfg, m);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_quant_x(x, m, cfg->dim, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
   if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
   if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
-  if ((e = launch_down(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_down(*experts, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
   if ((e = launch_combine(m, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess) return hip_fail(e, "combine");
   return MOE_OK;
 }
@@ -205,15 +205,11 @@ int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t
   int32_t* hdr = header ? header : w.status + 4;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_quant_x(x, m, cfg->dim, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
-  if ((e = launch_router(x, m, layer->gate_w, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router");
-  if ((e = launch_select(layer->bias, m, *cfg, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
-  if ((e = launch_plan(hdr, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
-  if ((e = launch_shared_gu(x, m, layer->sh_w1, layer->sh_w3, *cfg, w, s)) != hipSuccess)
-    return hip_fail(e, "shared_gu");
+  if ((e = launch_front(x, m, layer->gate_w, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
+    return hip_fail(e, "front");
+  if ((e = launch_select(layer->bias, m, *cfg, w, hdr, true, s)) != hipSuccess) return hip_fail(e, "select");
   if ((e = launch_gateup(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
-  if ((e = launch_down(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down");
-  if ((e = launch_shared_down(m, layer->sh_w2, *cfg, w, s)) != hipSuccess) return hip_fail(e, "shared_down");
+  if ((e = launch_down(layer->experts, m, *cfg, w, layer->sh_w2, s)) != hipSuccess) return hip_fail(e, "down");
   if ((e = launch_combine(m, *cfg, w, w.sd, out_f32, out_bf16, s)) != hipSuccess) return hip_fail(e, "combine");
   return MOE_OK;
 }

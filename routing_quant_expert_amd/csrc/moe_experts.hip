@@ -23,18 +23,34 @@ __device__ inline double fp16_f64(uint32_t bits16) {
 }
 __device__ inline uint16_t f32_to_fp16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-// Copies the byte range [g, g+nbytes) into LDS with 16-byte loads of the
-// aligned chunks that cover it (never touching a page the range does not
-// touch). Returns the offset in LDS of byte g.
-__device__ inline int stage_rows(uint8_t* lds, const uint8_t* g, int nbytes) {
-  uintptr_t a = (uintptr_t)g;
-  uintptr_t a0 = a & ~(uintptr_t)15;
-  int pad = (int)(a - a0);
-  int nchunks = (int)(((a + nbytes + 15) & ~(uintptr_t)15) - a0) >> 4;
-  const uint4* src = reinterpret_cast<const uint4*>(a0);
-  uint4* dst = reinterpret_cast<uint4*>(lds);
-  for (int i = threadIdx.x; i < nchunks; i += blockDim.x) dst[i] = load_nt16(src + i);
-  return pad;
+// ---- direct-to-LDS staging --------------------------------------------------
+// A tile of rows is copied HBM -> LDS with global_load_lds_dwordx4 (no VGPRs,
+// no wait at issue). Workgroups are 256 threads; wave w copies 16-byte chunks
+// w*64 + 256*k + lane (k < KC), so every wave issues exactly KC instructions
+// per tile (lanes past the tile's end re-read its last chunk into the slot's
+// padding) and a tile's arrival is a compile-time vmcnt.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int KC>
+__device__ __forceinline__ void dma_tile(const uint8_t* g, uint8_t* slot, int nchunks) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int i = w * 64 + 256 * k + lane;
+    const int src = i < nchunks ? i : nchunks - 1;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * src),
+                                     (__attribute__((address_space(3))) void*)(slot + 16 * (w * 64 + 256 * k)), 16,
+                                     0, 0);
+  }
 }
 
 // The activation of one token for the super-block `sb`: 64 words of int8
@@ -160,44 +176,81 @@ __device__ inline double dot_q3k(const uint8_t* p, const Act& A) {
 
 // ---------------------------------------------------------------------------
 // Gate/up on Q2_K + clamped SwiGLU + q8_1 of h. Workgroup = (distinct expert
-// u, 32-row group): its 32 gate rows and 32 up rows for every token that
-// picked u. Rows are staged in LDS `rc` at a time; a row's super-blocks go to
-// `nsb` consecutive lanes and are summed by a float64 butterfly.
+// u, 32-row group of the hidden units): its 32 gate rows and 32 up rows for
+// every token that picked u, as four 16-row tiles (gate 0-15, up 0-15, gate
+// 16-31, up 16-31) through a ring of SLOTS LDS slots, the next tiles in flight
+// while one is computed. A row's NSB super-blocks go to NSB consecutive lanes
+// and are summed by a float64 butterfly.
 // ---------------------------------------------------------------------------
+template <int NSB>
+struct GateUpGeom {
+  static constexpr int kRowBytes = NSB * kQ2KBytes;
+  static constexpr int kTileChunks = 16 * kRowBytes / 16;        // 16 rows per tile
+  static constexpr int kKC = (kTileChunks + 255) / 256;
+  static constexpr int kSlotBytes = kKC * 4096;
+  static constexpr int kItems = 16 * NSB;                         // (row, super-block) per tile
+  static constexpr int kIters = (kItems + 255) / 256;
+};
+
+template <int NSB, int SLOTS>
 __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, const int8_t* __restrict__ xq,
                                                 const uint16_t* __restrict__ xd, const int32_t* __restrict__ xs,
-                                                int dim, int inter, int nsb, int rc, float* __restrict__ g_out,
+                                                int dim, int inter, float* __restrict__ g_out,
                                                 float* __restrict__ u_out, float* __restrict__ h_out,
                                                 int8_t* __restrict__ hq, uint16_t* __restrict__ hd,
                                                 int32_t* __restrict__ hs, float L) {
+  using G = GateUpGeom<NSB>;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float gu[2][kMaxDecodeTokens][32];
   const int ngr = inter / 32;
   const int u = blockIdx.x / ngr, grp = blockIdx.x % ngr;
   if (u >= *plan.n_u()) return;
   const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];
-  const int RB = nsb * kQ2KBytes;
-  const int sb = threadIdx.x % nsb;
+  const int sb = threadIdx.x % NSB;
+  const uint8_t* ebase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride;
+  auto tile_src = [&](int c) -> const uint8_t* {
+    const uint64_t off = (c & 1) ? ex.up_off : ex.gate_off;
+    return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
+  };
   Act A;
-  for (int mat = 0; mat < 2; ++mat) {
-    const uint8_t* mbase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride + (mat ? ex.up_off : ex.gate_off);
-    for (int r0 = 0; r0 < 32; r0 += rc) {
-      __syncthreads();
-      int pad = stage_rows(lds, mbase + (uint64_t)(32 * grp + r0) * RB, rc * RB);
-      __syncthreads();
-      const int items = rc * nsb;
-      for (int j = 0; j < np; ++j) {
+  if (np == 1) {
+    const int tok = plan.pair_tok()[first];
+    load_act(A, xq + (int64_t)tok * dim, xd + (int64_t)tok * (dim / 32), xs + (int64_t)tok * (dim / 16), sb);
+  }
+#pragma unroll
+  for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // tiles issued after tile c and still allowed in flight
+    const int issued = (c + SLOTS < 4 ? c + SLOTS : 4);
+    const int after = issued - c - 1;
+    if (after == 3) wait_vmcnt<3 * G::kKC>();
+    else if (after == 2) wait_vmcnt<2 * G::kKC>();
+    else if (after == 1) wait_vmcnt<1 * G::kKC>();
+    else wait_vmcnt<0>();
+    block_sync_lds();
+    const uint8_t* slot = lds + (c % SLOTS) * G::kSlotBytes;
+    const int mat = c & 1, r0 = 16 * (c >> 1);
+    for (int j = 0; j < np; ++j) {
+      if (np > 1) {
         const int tok = plan.pair_tok()[first + j];
         load_act(A, xq + (int64_t)tok * dim, xd + (int64_t)tok * (dim / 32), xs + (int64_t)tok * (dim / 16), sb);
-        for (int base = 0; base < items; base += 256) {
-          const int i = base + threadIdx.x;
-          const bool act = i < items;
-          const int row = i / nsb;
-          double part = act ? dot_q2k(lds + pad + row * RB + kQ2KBytes * sb, A) : 0.0;
-          for (int s = 1; s < nsb; s <<= 1) part += __shfl_xor(part, s);
-          if (act && sb == 0) gu[mat][j][r0 + row] = (float)part;
-        }
       }
+#pragma unroll
+      for (int it = 0; it < G::kIters; ++it) {
+        const int i = it * 256 + threadIdx.x;
+        const bool act = i < G::kItems;
+        const int row = i / NSB;
+        double part = act ? dot_q2k(slot + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
+#pragma unroll
+        for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+        if (act && sb == 0) gu[mat][j][r0 + row] = (float)part;
+      }
+    }
+    if (c + SLOTS < 4) {
+      wait_lgkm0();
+      block_sync_lds();
+      dma_tile<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kSlotBytes, G::kTileChunks);
     }
   }
   __syncthreads();
@@ -225,37 +278,100 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
 }
 
 // ---------------------------------------------------------------------------
-// Down on Q3_K: workgroup = (distinct expert u, 32 output rows), every token
-// that picked u. y[pair][row] = RN32(the row's float64 sum).
+// Down on Q3_K: workgroup = (distinct expert u, 32 output rows) for every token
+// that picked u (both 16-row tiles in flight at once); y[pair][row] =
+// RN32(the row's float64 sum). Workgroups past the routed ones compute the
+// shared expert's down rows: sd = W2s . sh, one wave per row, f32.
 // ---------------------------------------------------------------------------
+template <int NSB>
+struct DownGeom {
+  static constexpr int kRowBytes = NSB * kQ3KBytes;
+  static constexpr int kTileChunks = 16 * kRowBytes / 16;
+  static constexpr int kKC = (kTileChunks + 255) / 256;
+  static constexpr int kSlotBytes = kKC * 4096;
+  static constexpr int kItems = 32 * NSB;
+  static constexpr int kIters = (kItems + 255) / 256;
+};
+
+__device__ inline void bf16x8(uint4 v, float (&f)[8]) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+}
+
+__device__ void shared_down_rows(int blk, int m, int dim, int inter, const uint16_t* __restrict__ w2,
+                                 const uint16_t* __restrict__ sh, float* __restrict__ sd) {
+  const int r = blk * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= dim) return;
+  float p[kMaxDecodeTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxDecodeTokens; ++t) p[t] = 0.0f;
+  const uint16_t* row = w2 + (int64_t)r * inter;
+  for (int k = 8 * lane; k < inter; k += 512) {
+    float a[8];
+    bf16x8(load_nt16(row + k), a);
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t) {
+      if (t < m) {
+        float hv[8];
+        bf16x8(*reinterpret_cast<const uint4*>(sh + (int64_t)t * inter + k), hv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[t] = __builtin_fmaf(a[j], hv[j], p[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxDecodeTokens; ++t)
+    for (int s = 32; s >= 1; s >>= 1) p[t] += __shfl_xor(p[t], s);
+  if (lane < m) {
+    float v = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t)
+      if (t == lane) v = p[t];
+    sd[(int64_t)lane * dim + r] = v;
+  }
+}
+
+template <int NSB>
 __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, const int8_t* __restrict__ hq,
                                               const uint16_t* __restrict__ hd, const int32_t* __restrict__ hs,
-                                              int dim, int inter, int nsb, int rc, float* __restrict__ y) {
+                                              int dim, int inter, float* __restrict__ y, int routed_blocks, int m,
+                                              const uint16_t* __restrict__ w2, const uint16_t* __restrict__ sh,
+                                              float* __restrict__ sd) {
+  using G = DownGeom<NSB>;
   extern __shared__ __align__(16) uint8_t lds[];
+  if ((int)blockIdx.x >= routed_blocks) {
+    shared_down_rows(blockIdx.x - routed_blocks, m, dim, inter, w2, sh, sd);
+    return;
+  }
   const int ngr = dim / 32;
   const int u = blockIdx.x / ngr, grp = blockIdx.x % ngr;
   if (u >= *plan.n_u()) return;
   const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];
-  const int RB = nsb * kQ3KBytes;
-  const int sb = threadIdx.x % nsb;
+  const int sb = threadIdx.x % NSB;
   const uint8_t* mbase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off;
   Act A;
-  for (int r0 = 0; r0 < 32; r0 += rc) {
-    __syncthreads();
-    int pad = stage_rows(lds, mbase + (uint64_t)(32 * grp + r0) * RB, rc * RB);
-    __syncthreads();
-    const int items = rc * nsb;
-    for (int j = 0; j < np; ++j) {
-      const int pair = first + j;
+  if (np == 1) load_act(A, hq + (int64_t)first * inter, hd + (int64_t)first * (inter / 32),
+                        hs + (int64_t)first * (inter / 16), sb);
+  dma_tile<G::kKC>(mbase + (uint64_t)(32 * grp) * G::kRowBytes, lds, G::kTileChunks);
+  dma_tile<G::kKC>(mbase + (uint64_t)(32 * grp + 16) * G::kRowBytes, lds + G::kSlotBytes, G::kTileChunks);
+  wait_vmcnt<0>();
+  block_sync_lds();
+  for (int j = 0; j < np; ++j) {
+    const int pair = first + j;
+    if (np > 1)
       load_act(A, hq + (int64_t)pair * inter, hd + (int64_t)pair * (inter / 32), hs + (int64_t)pair * (inter / 16), sb);
-      for (int base = 0; base < items; base += 256) {
-        const int i = base + threadIdx.x;
-        const bool act = i < items;
-        const int row = i / nsb;
-        double part = act ? dot_q3k(lds + pad + row * RB + kQ3KBytes * sb, A) : 0.0;
-        for (int s = 1; s < nsb; s <<= 1) part += __shfl_xor(part, s);
-        if (act && sb == 0) y[(int64_t)pair * dim + 32 * grp + r0 + row] = (float)part;
-      }
+#pragma unroll
+    for (int it = 0; it < G::kIters; ++it) {
+      const int i = it * 256 + threadIdx.x;
+      const bool act = i < G::kItems;
+      const int row = i / NSB;                       // 0..31
+      const uint8_t* p = lds + (row >> 4) * G::kSlotBytes + (row & 15) * G::kRowBytes + kQ3KBytes * sb;
+      double part = act ? dot_q3k(p, A) : 0.0;
+#pragma unroll
+      for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+      if (act && sb == 0) y[(int64_t)pair * dim + 32 * grp + row] = (float)part;
     }
   }
 }
@@ -281,36 +397,76 @@ __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __r
   if (out_bf16) out_bf16[(int64_t)t * dim + r] = bf16_rne(acc);
 }
 
-int rows_per_stage(int row_bytes) {
-  int rc = 32;
-  while (rc > 1 && rc * row_bytes + 16 > 48 * 1024) rc >>= 1;
-  return rc;
+constexpr int kGateUpSlots = 3;
+
+template <int NSB>
+hipError_t launch_gateup_t(const moe_experts& ex, int max_u, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  using G = GateUpGeom<NSB>;
+  auto kern = k_gateup<NSB, kGateUpSlots>;
+  size_t shm = (size_t)kGateUpSlots * G::kSlotBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(max_u * (c.inter / 32)), dim3(256), shm, s, ex, w.plan, w.xq, w.xd, w.xs, c.dim,
+                     c.inter, w.g, w.u, w.h, w.hq, w.hd, w.hs, c.swiglu_limit);
+  return hipGetLastError();
+}
+
+template <int NSB>
+hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg& c, const Ws& w, const uint16_t* w2,
+                         hipStream_t s) {
+  using G = DownGeom<NSB>;
+  auto kern = k_down<NSB>;
+  size_t shm = (size_t)2 * G::kSlotBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int routed_blocks = max_u * (c.dim / 32);
+  const int shared_blocks = w2 ? (c.dim + 3) / 4 : 0;
+  hipLaunchKernelGGL(kern, dim3(routed_blocks + shared_blocks), dim3(256), shm, s, ex, w.plan, w.hq, w.hd, w.hs,
+                     c.dim, c.inter, w.y, routed_blocks, m, w2, w.sh, w.sd);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  int max_u = min(c.n_routed, m * c.topk);
-  int nsb = c.dim / 256;
-  int rc = rows_per_stage(nsb * kQ2KBytes);
-  size_t shm = (size_t)rc * nsb * kQ2KBytes + 32;
+  const int max_u = min(c.n_routed, m * c.topk);
   timed_begin(MOE_K_GATEUP, s);
-  hipLaunchKernelGGL(k_gateup, dim3(max_u * (c.inter / 32)), dim3(256), shm, s, ex, w.plan, w.xq, w.xd, w.xs, c.dim,
-                     c.inter, nsb, rc, w.g, w.u, w.h, w.hq, w.hd, w.hs, c.swiglu_limit);
-  hipError_t err = hipGetLastError();
+  hipError_t err;
+  switch (c.dim / 256) {
+    case 1: err = launch_gateup_t<1>(ex, max_u, c, w, s); break;
+    case 2: err = launch_gateup_t<2>(ex, max_u, c, w, s); break;
+    case 4: err = launch_gateup_t<4>(ex, max_u, c, w, s); break;
+    case 8: err = launch_gateup_t<8>(ex, max_u, c, w, s); break;
+    case 16: err = launch_gateup_t<16>(ex, max_u, c, w, s); break;
+    case 32: err = launch_gateup_t<32>(ex, max_u, c, w, s); break;
+    default: err = hipErrorInvalidValue; break;
+  }
   timed_end(MOE_K_GATEUP, s);
   return err;
 }
 
-hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  int max_u = min(c.n_routed, m * c.topk);
-  int nsb = c.inter / 256;
-  int rc = rows_per_stage(nsb * kQ3KBytes);
-  size_t shm = (size_t)rc * nsb * kQ3KBytes + 32;
+hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
+                       hipStream_t s) {
+  const int max_u = min(c.n_routed, m * c.topk);
   timed_begin(MOE_K_DOWN, s);
-  hipLaunchKernelGGL(k_down, dim3(max_u * (c.dim / 32)), dim3(256), shm, s, ex, w.plan, w.hq, w.hd, w.hs, c.dim,
-                     c.inter, nsb, rc, w.y);
-  hipError_t err = hipGetLastError();
+  hipError_t err;
+  switch (c.inter / 256) {
+    case 1: err = launch_down_t<1>(ex, m, max_u, c, w, w2, s); break;
+    case 2: err = launch_down_t<2>(ex, m, max_u, c, w, w2, s); break;
+    case 4: err = launch_down_t<4>(ex, m, max_u, c, w, w2, s); break;
+    case 8: err = launch_down_t<8>(ex, m, max_u, c, w, w2, s); break;
+    case 16: err = launch_down_t<16>(ex, m, max_u, c, w, w2, s); break;
+    case 32: err = launch_down_t<32>(ex, m, max_u, c, w, w2, s); break;
+    default: err = hipErrorInvalidValue; break;
+  }
   timed_end(MOE_K_DOWN, s);
   return err;
 }

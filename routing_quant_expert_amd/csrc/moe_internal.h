@@ -63,18 +63,20 @@ bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L);
 Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m);
 
 // ---- launchers (each returns hipError_t of the launch) ----
-hipError_t launch_quant_x(const uint16_t* x, int m, int dim, const Ws& w, hipStream_t s);
-hipError_t launch_router(const uint16_t* x, int m, const uint16_t* gate_w, const moe_cfg& c, const Ws& w,
-                         float* logits_out, hipStream_t s);
-hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s);
+// front: status reset, q8_1 of x, and (when the pointers are given) the
+// router with its scores and the shared expert's gate/up + SwiGLU.
+hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const uint16_t* w1, const uint16_t* w3,
+                        const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s);
+hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, bool with_plan,
+                         hipStream_t s);
 hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
 hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+// down: routed Q3_K rows, plus the shared expert's down rows when w2 is given.
+hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
+                       hipStream_t s);
 hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
-hipError_t launch_shared_gu(const uint16_t* x, int m, const uint16_t* w1, const uint16_t* w3, const moe_cfg& c,
-                            const Ws& w, hipStream_t s);
-hipError_t launch_shared_down(int m, const uint16_t* w2, const moe_cfg& c, const Ws& w, hipStream_t s);
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
 
 // Timing hook (moe_time_next_launch): brackets the next launch of `which`.

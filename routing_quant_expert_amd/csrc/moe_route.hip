@@ -1,5 +1,10 @@
-// Routing kernels: q8_1 of the input, the router GEMV with the scores, the
-// top-k selection with its header, and the plan tables (A1-A3).
+// Routing kernels (A1-A3) and the front of the layer:
+//  * k_front: q8_1 of the input, the router GEMV with the scores, and (for
+//    the whole layer) the shared expert's gate/up GEMVs with its SwiGLU, in
+//    one launch (the workgroup index picks the part);
+//  * k_select / k_select_plan: the top-k selection and its header, and for
+//    decode (m <= 8) the plan tables in the same launch;
+//  * k_plan_small: the plan tables from caller-given headers.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -8,8 +13,13 @@
 namespace moe {
 namespace {
 
-__device__ inline float fp16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ inline uint16_t f32_to_fp16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+__device__ inline void bf16x8(uint4 v, float (&f)[8]) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+}
 
 // ---------------------------------------------------------------------------
 // q8_1 of bf16 rows: one thread per value, a q8_1 block = 32 consecutive
@@ -17,11 +27,9 @@ __device__ inline uint16_t f32_to_fp16_bits(float f) { return __builtin_bit_cast
 // fp16(d), plus the sums of 16 consecutive codes (the q8_1 sum field is not
 // used; the GEMV epilogues need per-16 sums of the codes).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_quant_x(const uint16_t* __restrict__ x, int64_t n, int8_t* __restrict__ xq,
-                                                 uint16_t* __restrict__ xd, int32_t* __restrict__ xs,
-                                                 int32_t* __restrict__ status) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // n is a multiple of 256
-  if (blockIdx.x == 0 && threadIdx.x < 4) status[threadIdx.x] = 0;   // first kernel of every entry point
+__device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* __restrict__ xq,
+                              uint16_t* __restrict__ xd, int32_t* __restrict__ xs) {
+  const int64_t i = (int64_t)blk * 256 + threadIdx.x;   // m*dim is a multiple of 256
   float v = bf16_f32(x[i]);
   float a = fabsf(v);
   for (int s = 16; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
@@ -30,7 +38,7 @@ __global__ __launch_bounds__(256) void k_quant_x(const uint16_t* __restrict__ x,
   xq[i] = (int8_t)q;
   int sum = q;
   for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
-  int lane32 = threadIdx.x & 31;
+  const int lane32 = threadIdx.x & 31;
   if (lane32 == 0) xd[i >> 5] = f32_to_fp16_bits(d);
   if ((lane32 & 15) == 0) xs[i >> 4] = sum;
 }
@@ -45,21 +53,20 @@ __global__ __launch_bounds__(256) void k_quant_x(const uint16_t* __restrict__ x,
 // ---------------------------------------------------------------------------
 constexpr int kRouterTok = 8;
 
-__global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x, int m, int dim,
-                                                const uint16_t* __restrict__ gate_w, int n_routed, float temp,
-                                                float* __restrict__ logits, float* __restrict__ scores,
-                                                float* __restrict__ logits_out) {
-  int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
+__device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int dim,
+                            const uint16_t* __restrict__ gate_w, int n_routed, float temp, float* __restrict__ logits,
+                            float* __restrict__ scores, float* __restrict__ logits_out) {
+  const int e = blk * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (e >= n_routed) return;
   const uint16_t* wr = gate_w + (int64_t)e * dim;
   for (int t0 = 0; t0 < m; t0 += kRouterTok) {
-    int nt = min(kRouterTok, m - t0);
+    const int nt = min(kRouterTok, m - t0);
     float p[kRouterTok];
 #pragma unroll
     for (int t = 0; t < kRouterTok; ++t) p[t] = 0.0f;
     for (int base = 0; base < dim; base += 512) {
-      int k = base + 8 * lane;
+      const int k = base + 8 * lane;
       if (k < dim) {
         uint4 wv = *reinterpret_cast<const uint4*>(wr + k);
         uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -87,12 +94,11 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x, 
       p[t] = v;
     }
     if (lane < nt) {
-      // lane t handles token t0 + t (all lanes hold every token's logit)
       float lg = 0.0f;
 #pragma unroll
       for (int t = 0; t < kRouterTok; ++t)
         if (t == lane) lg = p[t];
-      int64_t o = (int64_t)(t0 + lane) * n_routed + e;
+      const int64_t o = (int64_t)(t0 + lane) * n_routed + e;
       logits[o] = lg;
       if (logits_out) logits_out[o] = lg;
       scores[o] = score_of(lg, temp);
@@ -100,214 +106,336 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ x, 
   }
 }
 
+// Shared expert gate/up (m <= 8): one wave per hidden unit i: sg = W1s[i].x,
+// su = W3s[i].x (f32, any order), sh = bf16(swiglu(sg, su)) [moe_v41.rs,
+// module doc: the shared expert is resident bf16 on the dense GEMM/GEMV].
+__device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, int dim, int inter,
+                               const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
+                               float* __restrict__ sg, float* __restrict__ su, uint16_t* __restrict__ sh, float L) {
+  const int i = blk * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= inter) return;
+  float pg[kMaxDecodeTokens], pu[kMaxDecodeTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxDecodeTokens; ++t) pg[t] = pu[t] = 0.0f;
+  const uint16_t* r1 = w1 + (int64_t)i * dim;
+  const uint16_t* r3 = w3 + (int64_t)i * dim;
+  for (int k = 8 * lane; k < dim; k += 512) {
+    float a[8], b[8];
+    bf16x8(load_nt16(r1 + k), a);
+    bf16x8(load_nt16(r3 + k), b);
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t) {
+      if (t < m) {
+        float xv[8];
+        bf16x8(*reinterpret_cast<const uint4*>(x + (int64_t)t * dim + k), xv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pg[t] = __builtin_fmaf(a[j], xv[j], pg[t]);
+          pu[t] = __builtin_fmaf(b[j], xv[j], pu[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxDecodeTokens; ++t) {
+    for (int s = 32; s >= 1; s >>= 1) {
+      pg[t] += __shfl_xor(pg[t], s);
+      pu[t] += __shfl_xor(pu[t], s);
+    }
+  }
+  if (lane < m) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t)
+      if (t == lane) {
+        g = pg[t];
+        u = pu[t];
+      }
+    const int64_t o = (int64_t)lane * inter + i;
+    sg[o] = g;
+    su[o] = u;
+    sh[o] = bf16_rne(swiglu(g, u, L));
+  }
+}
+
+struct FrontArgs {
+  const uint16_t* x;
+  int m, dim, inter, n_routed;
+  float temp, L;
+  const uint16_t* gate_w;
+  const uint16_t* w1;
+  const uint16_t* w3;
+  float* logits_out;
+  int router_blocks, shared_blocks;
+};
+
+__global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
+  int blk = blockIdx.x;
+  if (blk == 0 && threadIdx.x < 4) w.status[threadIdx.x] = 0;   // every entry point starts here
+  if (blk < a.router_blocks) {
+    router_rows(blk, a.x, a.m, a.dim, a.gate_w, a.n_routed, a.temp, w.logits, w.scores, a.logits_out);
+    return;
+  }
+  blk -= a.router_blocks;
+  if (blk < a.shared_blocks) {
+    shared_gu_rows(blk, a.x, a.m, a.dim, a.inter, a.w1, a.w3, w.sg, w.su, w.sh, a.L);
+    return;
+  }
+  blk -= a.shared_blocks;
+  quant_x_block(blk, a.x, w.xq, w.xd, w.xs);
+}
+
 // ---------------------------------------------------------------------------
-// Selection: one wave per token. key = score + bias; the top-k by key,
-// larger first, equal keys by ascending id (the pages' stable sort), NaN keys
-// last; weights from the unbiased scores of the picks [moe_v41.rs,
-// fn route_from_logits]; the header [device_route.rs, fn parse_header].
+// Selection, one wave per token [moe_v41.rs, fn route_from_logits]: key =
+// score + bias; the top-k by key, larger first, equal keys by ascending id
+// (the pages' sort is stable), NaN keys last; weights = the unbiased scores
+// of the picks, renormalised (sum in pick order, plus 1e-20) and scaled by
+// route_scale, each step one f32 rounding. Lane r holds pick r. Writes the
+// header [device_route.rs, fn parse_header] and the picks/weights to LDS.
 // ---------------------------------------------------------------------------
 __device__ inline bool ranks_before(float ka, int a, float kb, int b) {
-  bool na = isnan(ka), nb = isnan(kb);
+  const bool na = isnan(ka), nb = isnan(kb);
   if (na != nb) return !na;
   if (!na && ka != kb) return ka > kb;
   return a < b;
 }
 
-__global__ __launch_bounds__(64) void k_select(const float* __restrict__ scores, const float* __restrict__ bias,
-                                               int n_routed, int topk, int norm, float route_scale,
-                                               int32_t* __restrict__ header, int32_t* __restrict__ status) {
-  int t = blockIdx.x;
-  int lane = threadIdx.x;
-  const float* sc = scores + (int64_t)t * n_routed;
-  constexpr int kPer = kMaxRouted / 64;
-  float key[kPer];
-  uint32_t taken = 0;
+template <int KPER>
+__device__ void select_token(const float* __restrict__ sc, const float* __restrict__ bias, int n_routed, int topk,
+                             int norm, float route_scale, int32_t* __restrict__ hd, int* picks_out, float* w_out,
+                             int32_t* __restrict__ status) {
+  const int lane = threadIdx.x & 63;
+  float key[KPER];
   bool any_nan = false;
 #pragma unroll
-  for (int c = 0; c < kPer; ++c) {
-    int e = lane + 64 * c;
+  for (int c = 0; c < KPER; ++c) {
+    const int e = lane + 64 * c;
     key[c] = e < n_routed ? fadd(sc[e], bias[e]) : 0.0f;
     if (e < n_routed && isnan(key[c])) any_nan = true;
   }
-  int picks[kMaxTopk];
+  uint32_t taken = 0;
+  int mypick = 0;
   for (int r = 0; r < topk; ++r) {
     float bk = 0.0f;
     int bid = 0x7fffffff;
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      int e = lane + 64 * c;
+    for (int c = 0; c < KPER; ++c) {
+      const int e = lane + 64 * c;
       if (e < n_routed && !((taken >> c) & 1u) && (bid == 0x7fffffff || ranks_before(key[c], e, bk, bid))) {
         bk = key[c];
         bid = e;
       }
     }
+#pragma unroll
     for (int s = 32; s >= 1; s >>= 1) {
-      float ok = __shfl_xor(bk, s);
-      int oid = __shfl_xor(bid, s);
+      const float ok = __shfl_xor(bk, s);
+      const int oid = __shfl_xor(bid, s);
       if (oid != 0x7fffffff && (bid == 0x7fffffff || ranks_before(ok, oid, bk, bid))) {
         bk = ok;
         bid = oid;
       }
     }
-    picks[r] = bid;
+    if (lane == r) mypick = bid;
     if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
   }
-  bool nan_any = __any(any_nan);
+  float wv = lane < topk ? sc[mypick] : 0.0f;
+  if (norm && topk > 1) {
+    float sum = 0.0f;
+    for (int i = 0; i < topk; ++i) sum = fadd(sum, __shfl(wv, i));
+    sum = fadd(sum, 1e-20f);
+    wv = (float)((double)wv / (double)sum);
+  }
+  wv = fmul(wv, route_scale);
+  int rank = 0;
+  for (int i = 0; i < topk; ++i) rank += (__shfl(mypick, i) < mypick) ? 1 : 0;
+  const bool nan_any = __any(any_nan);
+  if (lane < topk) {
+    hd[1 + lane] = mypick;
+    hd[1 + topk + lane] = (int32_t)__builtin_bit_cast(uint32_t, wv);
+    hd[1 + 2 * topk + rank] = mypick;
+    if (picks_out) {
+      picks_out[lane] = mypick;
+      w_out[lane] = wv;
+    }
+  }
   if (lane == 0) {
-    float wt[kMaxTopk];
-    for (int i = 0; i < topk; ++i) wt[i] = sc[picks[i]];
-    if (norm && topk > 1) {
-      float sum = 0.0f;
-      for (int i = 0; i < topk; ++i) sum = fadd(sum, wt[i]);
-      sum = fadd(sum, 1e-20f);
-      for (int i = 0; i < topk; ++i) wt[i] = (float)((double)wt[i] / (double)sum);
-    }
-    for (int i = 0; i < topk; ++i) wt[i] = fmul(wt[i], route_scale);
-    int32_t* hd = header + (int64_t)t * (1 + 3 * topk);
     hd[0] = nan_any ? MOE_STATUS_NAN_KEY : 0;
-    int plan[kMaxTopk];
-    for (int i = 0; i < topk; ++i) {
-      hd[1 + i] = picks[i];
-      hd[1 + topk + i] = (int32_t)__builtin_bit_cast(uint32_t, wt[i]);
-      plan[i] = picks[i];
-    }
-    for (int a = 1; a < topk; ++a)
-      for (int b = a; b > 0 && plan[b] < plan[b - 1]; --b) {
-        int tmp = plan[b];
-        plan[b] = plan[b - 1];
-        plan[b - 1] = tmp;
-      }
-    for (int i = 0; i < topk; ++i) hd[1 + 2 * topk + i] = plan[i];
     if (nan_any) atomicOr(status, MOE_STATUS_NAN_KEY);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Plan tables from the headers: the (expert, token) pairs in ascending
-// expert id then token, the distinct experts, and per token its pairs in
-// plan order [device_route.rs, fn device_route_check: weights and pointers
-// in plan order]. One workgroup; invalid picks disable their token.
+// Plan tables for m <= 8 tokens, one wave (pairs q = t*topk + r <= 64): the
+// valid (expert, token) pairs sorted by expert id then token, the distinct
+// experts, and per token its pairs in plan order (ascending id)
+// [device_route.rs, fn device_route_check: weights and pointers in plan order].
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ header, int m, int topk, int n_routed,
-                                              PlanView plan, int32_t* __restrict__ status) {
-  __shared__ int cnt[kMaxRouted];
-  __shared__ int off[kMaxRouted];
-  __shared__ int uid[kMaxRouted];
-  __shared__ int n_u_s, bad_s;
-  const int hw = 1 + 3 * topk;
-  int tid = threadIdx.x;
-  for (int e = tid; e < n_routed; e += 256) cnt[e] = 0;
-  if (tid == 0) bad_s = 0;
-  __syncthreads();
-  // token validity: picks in range and distinct
-  for (int t = tid; t < m; t += 256) {
-    const int32_t* hd = header + (int64_t)t * hw;
-    bool ok = true;
-    for (int i = 0; i < topk; ++i) {
-      int e = hd[1 + i];
-      if (e < 0 || e >= n_routed) ok = false;
-      for (int j = 0; j < i; ++j)
-        if (hd[1 + j] == e) ok = false;
-    }
-    if (!ok) {
-      atomicOr(&bad_s, 1);
-      for (int i = 0; i < topk; ++i) plan.tok_pairs()[t * topk + i] = -1;
-    } else {
-      for (int i = 0; i < topk; ++i) atomicAdd(&cnt[hd[1 + i]], 1);
-    }
+__device__ void build_plan(const int* picks, const float* wts, const int* tok_ok, int m, int topk, PlanView plan,
+                           int* first_flag) {
+  const int lane = threadIdx.x & 63;
+  const int P = m * topk;
+  const bool mine = lane < P;
+  const int t = mine ? lane / topk : 0;
+  const bool valid = mine && tok_ok[t];
+  const int e = mine ? picks[lane] : 0;
+  int pos = 0, cnt = 0;
+  bool first = valid;
+  for (int q = 0; q < P; ++q) {
+    const int t2 = q / topk;
+    if (!tok_ok[t2]) continue;
+    const int e2 = picks[q];
+    if (e2 < e || (e2 == e && t2 < t)) ++pos;
+    if (e2 == e) ++cnt;
+    if (e2 == e && t2 < t) first = false;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0, nu = 0;
-    for (int e = 0; e < n_routed; ++e) {
-      off[e] = o;
-      uid[e] = cnt[e] ? nu : -1;
-      if (cnt[e]) {
-        plan.u_expert()[nu] = e;
-        plan.u_first()[nu] = o;
-        plan.u_npairs()[nu] = cnt[e];
-        ++nu;
-      }
-      o += cnt[e];
-    }
-    n_u_s = nu;
-    *plan.n_u() = nu;
-    *plan.n_pairs() = o;
-    if (bad_s) atomicOr(status, MOE_STATUS_BAD_PICK);
-  }
-  __syncthreads();
-  int P = m * topk;
-  for (int q = tid; q < P; q += 256) {
-    int t = q / topk, i = q % topk;
-    const int32_t* hd = header + (int64_t)t * hw;
-    int e = hd[1 + i];
-    bool ok = true;
-    for (int a = 0; a < topk; ++a) {
-      int ea = hd[1 + a];
-      if (ea < 0 || ea >= n_routed) ok = false;
-      for (int b = 0; b < a; ++b)
-        if (hd[1 + b] == ea) ok = false;
-    }
-    if (!ok) continue;
-    // rank among the valid tokens before t that picked e
-    int before = 0;
-    for (int t2 = 0; t2 < t; ++t2) {
-      const int32_t* h2 = header + (int64_t)t2 * hw;
-      bool ok2 = true, has = false;
-      for (int a = 0; a < topk; ++a) {
-        int ea = h2[1 + a];
-        if (ea < 0 || ea >= n_routed) ok2 = false;
-        for (int b = 0; b < a; ++b)
-          if (h2[1 + b] == ea) ok2 = false;
-        if (ea == e) has = true;
-      }
-      if (ok2 && has) ++before;
-    }
-    int pos = off[e] + before;
+  if (mine) first_flag[lane] = first ? 1 : 0;
+  __builtin_amdgcn_wave_barrier();
+  int uid = 0;
+  for (int q = 0; q < P; ++q)
+    if (first_flag[q] && picks[q] < e) ++uid;
+  if (valid) {
     plan.pair_tok()[pos] = t;
     plan.pair_expert()[pos] = e;
-    plan.pair_w()[pos] = __builtin_bit_cast(float, hd[1 + topk + i]);
-    // this pick's place in the token's plan order (ascending id)
-    int rank = 0;
-    for (int a = 0; a < topk; ++a)
-      if (hd[1 + a] < e) ++rank;
-    plan.tok_pairs()[t * topk + rank] = pos;
+    plan.pair_w()[pos] = wts[lane];
+    if (first) {
+      plan.u_expert()[uid] = e;
+      plan.u_first()[uid] = pos;
+      plan.u_npairs()[uid] = cnt;
+    }
+    int rk = 0;
+    for (int r2 = 0; r2 < topk; ++r2) rk += picks[t * topk + r2] < e ? 1 : 0;
+    plan.tok_pairs()[t * topk + rk] = pos;
+  } else if (mine) {
+    plan.tok_pairs()[lane] = -1;
   }
+  const unsigned long long vb = __ballot(valid);
+  const unsigned long long fb = __ballot(mine && first);
+  if (lane == 0) {
+    *plan.n_pairs() = __popcll(vb);
+    *plan.n_u() = __popcll(fb);
+  }
+}
+
+template <int KPER>
+__global__ __launch_bounds__(512) void k_select_plan(const float* __restrict__ scores,
+                                                     const float* __restrict__ bias, int m, int n_routed, int topk,
+                                                     int norm, float route_scale, int32_t* __restrict__ header,
+                                                     PlanView plan, int32_t* __restrict__ status) {
+  __shared__ int picks[64];
+  __shared__ float wts[64];
+  __shared__ int tok_ok[kMaxDecodeTokens];
+  __shared__ int first_flag[64];
+  const int wave = threadIdx.x >> 6;
+  if (wave < m) {
+    select_token<KPER>(scores + (int64_t)wave * n_routed, bias, n_routed, topk, norm, route_scale,
+                       header + (int64_t)wave * (1 + 3 * topk), picks + wave * topk, wts + wave * topk, status);
+    if ((threadIdx.x & 63) == 0) tok_ok[wave] = 1;
+  }
+  __syncthreads();
+  if (wave == 0) build_plan(picks, wts, tok_ok, m, topk, plan, first_flag);
+}
+
+template <int KPER>
+__global__ __launch_bounds__(64) void k_select(const float* __restrict__ scores, const float* __restrict__ bias,
+                                               int n_routed, int topk, int norm, float route_scale,
+                                               int32_t* __restrict__ header, int32_t* __restrict__ status) {
+  const int t = blockIdx.x;
+  select_token<KPER>(scores + (int64_t)t * n_routed, bias, n_routed, topk, norm, route_scale,
+                     header + (int64_t)t * (1 + 3 * topk), nullptr, nullptr, status);
+}
+
+// Plan tables from headers given by the caller (m <= 8): picks outside
+// [0, n_routed) or repeated within a token disable that token.
+__global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ header, int m, int topk, int n_routed,
+                                                   PlanView plan, int32_t* __restrict__ status) {
+  __shared__ int picks[64];
+  __shared__ float wts[64];
+  __shared__ int tok_ok[kMaxDecodeTokens];
+  __shared__ int first_flag[64];
+  const int lane = threadIdx.x;
+  const int hw = 1 + 3 * topk;
+  if (lane < m * topk) {
+    const int t = lane / topk, r = lane % topk;
+    picks[lane] = header[t * hw + 1 + r];
+    wts[lane] = __builtin_bit_cast(float, header[t * hw + 1 + topk + r]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < m) {
+    bool ok = true;
+    for (int r = 0; r < topk; ++r) {
+      const int e = picks[lane * topk + r];
+      if (e < 0 || e >= n_routed) ok = false;
+      for (int r2 = 0; r2 < r; ++r2)
+        if (picks[lane * topk + r2] == e) ok = false;
+    }
+    tok_ok[lane] = ok ? 1 : 0;
+    if (!ok) atomicOr(status, MOE_STATUS_BAD_PICK);
+  }
+  __builtin_amdgcn_wave_barrier();
+  build_plan(picks, wts, tok_ok, m, topk, plan, first_flag);
 }
 
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, int64_t n, float temp,
                                                 float* __restrict__ out, int force_slow) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = score_of(lg[i], temp, force_slow != 0);
 }
 
 }  // namespace
 
-hipError_t launch_quant_x(const uint16_t* x, int m, int dim, const Ws& w, hipStream_t s) {
-  int64_t n = (int64_t)m * dim;
-  hipLaunchKernelGGL(k_quant_x, dim3((unsigned)(n / 256)), dim3(256), 0, s, x, n, w.xq, w.xd, w.xs, w.status);
-  return hipGetLastError();
-}
-
-hipError_t launch_router(const uint16_t* x, int m, const uint16_t* gate_w, const moe_cfg& c, const Ws& w,
-                         float* logits_out, hipStream_t s) {
+hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const uint16_t* w1, const uint16_t* w3,
+                        const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s) {
+  FrontArgs a;
+  a.x = x;
+  a.m = m;
+  a.dim = c.dim;
+  a.inter = c.inter;
+  a.n_routed = c.n_routed;
+  a.temp = c.gate_temp;
+  a.L = c.swiglu_limit;
+  a.gate_w = gate_w;
+  a.w1 = w1;
+  a.w3 = w3;
+  a.logits_out = logits_out;
+  a.router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
+  a.shared_blocks = w1 ? (c.inter + 3) / 4 : 0;
+  const int quant_blocks = (int)((int64_t)m * c.dim / 256);
   timed_begin(MOE_K_ROUTER, s);
-  hipLaunchKernelGGL(k_router, dim3((c.n_routed + 3) / 4), dim3(256), 0, s, x, m, c.dim, gate_w, c.n_routed,
-                     c.gate_temp, w.logits, w.scores, logits_out);
+  hipLaunchKernelGGL(k_front, dim3(a.router_blocks + a.shared_blocks + quant_blocks), dim3(256), 0, s, a, w);
   hipError_t err = hipGetLastError();
   timed_end(MOE_K_ROUTER, s);
   return err;
 }
 
-hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s) {
-  hipLaunchKernelGGL(k_select, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk, c.norm_topk_prob,
-                     c.route_scale, header, w.status);
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, bool with_plan,
+                         hipStream_t s) {
+  const int kper = (c.n_routed + 63) / 64;
+  if (with_plan) {
+    if (kper == 6)
+      hipLaunchKernelGGL(k_select_plan<6>, dim3(1), dim3(512), 0, s, w.scores, bias, m, c.n_routed, c.topk,
+                         c.norm_topk_prob, c.route_scale, header, w.plan, w.status);
+    else
+      hipLaunchKernelGGL(k_select_plan<16>, dim3(1), dim3(512), 0, s, w.scores, bias, m, c.n_routed, c.topk,
+                         c.norm_topk_prob, c.route_scale, header, w.plan, w.status);
+  } else {
+    if (kper == 6)
+      hipLaunchKernelGGL(k_select<6>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk,
+                         c.norm_topk_prob, c.route_scale, header, w.status);
+    else
+      hipLaunchKernelGGL(k_select<16>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk,
+                         c.norm_topk_prob, c.route_scale, header, w.status);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
+  hipLaunchKernelGGL(k_plan_small, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  return launch_front(x, m, nullptr, nullptr, nullptr, c, w, nullptr, s);
 }
 
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s) {
