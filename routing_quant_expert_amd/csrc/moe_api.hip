@@ -183,6 +183,13 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if (m == 1) {
+    if ((e = launch_gateup_m1(1, *experts, nullptr, header, nullptr, *cfg, w, s)) != hipSuccess)
+      return hip_fail(e, "gateup_m1");
+    if ((e = launch_down_m1(*experts, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "down_m1");
+    return MOE_OK;
+  }
   if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
   if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(*experts, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
@@ -207,6 +214,13 @@ int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t
   hipError_t e;
   if ((e = launch_front(x, m, layer->gate_w, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
     return hip_fail(e, "front");
+  if (m == 1) {
+    if ((e = launch_gateup_m1(0, layer->experts, layer->bias, nullptr, hdr, *cfg, w, s)) != hipSuccess)
+      return hip_fail(e, "gateup_m1");
+    if ((e = launch_down_m1(layer->experts, *cfg, w, layer->sh_w2, out_f32, out_bf16, s)) != hipSuccess)
+      return hip_fail(e, "down_m1");
+    return MOE_OK;
+  }
   if ((e = launch_select(layer->bias, m, *cfg, w, hdr, true, s)) != hipSuccess) return hip_fail(e, "select");
   if ((e = launch_gateup(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(layer->experts, m, *cfg, w, layer->sh_w2, s)) != hipSuccess) return hip_fail(e, "down");

@@ -1,0 +1,425 @@
+// Single-token decode (m = 1) in three launches after the front kernel:
+//  * k_gateup_m1: every workgroup first derives the token's plan itself (the
+//    top-k selection from the scores, or the caller's header), then runs
+//    one 32-row group of one picked expert's Q2_K gate/up rows + SwiGLU +
+//    q8_1 of h. Workgroup 0 also writes the header and the plan tables.
+//  * k_down_m1: one workgroup per 16 output rows: one wave per picked expert
+//    streams that expert's Q3_K down rows into LDS and dots them with its
+//    q8_1(h); two more waves compute the shared expert's down rows; then the
+//    combine in plan order adds them up [moe_v41.rs, Kernels: accumulate,
+//    finish; fn shared_side].
+// The arithmetic is that of the general kernels (same dot-product and
+// combine order), so the results are bit-identical to them.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+#include "moe_kquant.h"
+#include "moe_math.h"
+
+namespace moe {
+namespace {
+
+__device__ inline bool ranks_before(float ka, int a, float kb, int b) {
+  const bool na = isnan(ka), nb = isnan(kb);
+  if (na != nb) return !na;
+  if (!na && ka != kb) return ka > kb;
+  return a < b;
+}
+
+// One wave: the top-k of one token [moe_v41.rs, fn route_from_logits].
+// Lane r < topk returns pick r (rank order) and its weight; *nan_any is set
+// when any key is NaN.
+template <int KPER>
+__device__ void select_wave(const float* __restrict__ sc, const float* __restrict__ bias, int n_routed, int topk,
+                            int norm, float route_scale, int& pick, float& weight, bool& nan_any) {
+  const int lane = threadIdx.x & 63;
+  float key[KPER];
+  bool has_nan = false;
+#pragma unroll
+  for (int c = 0; c < KPER; ++c) {
+    const int e = lane + 64 * c;
+    key[c] = e < n_routed ? fadd(sc[e], bias[e]) : 0.0f;
+    if (e < n_routed && isnan(key[c])) has_nan = true;
+  }
+  uint32_t taken = 0;
+  int mypick = 0;
+  for (int r = 0; r < topk; ++r) {
+    float bk = 0.0f;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < KPER; ++c) {
+      const int e = lane + 64 * c;
+      if (e < n_routed && !((taken >> c) & 1u) && (bid == 0x7fffffff || ranks_before(key[c], e, bk, bid))) {
+        bk = key[c];
+        bid = e;
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+      const float ok = __shfl_xor(bk, s);
+      const int oid = __shfl_xor(bid, s);
+      if (oid != 0x7fffffff && (bid == 0x7fffffff || ranks_before(ok, oid, bk, bid))) {
+        bk = ok;
+        bid = oid;
+      }
+    }
+    if (lane == r) mypick = bid;
+    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+  }
+  float wv = lane < topk ? sc[mypick] : 0.0f;
+  if (norm && topk > 1) {
+    float sum = 0.0f;
+    for (int i = 0; i < topk; ++i) sum = fadd(sum, __shfl(wv, i));
+    sum = fadd(sum, 1e-20f);
+    wv = (float)((double)wv / (double)sum);
+  }
+  pick = mypick;
+  weight = fmul(wv, route_scale);
+  nan_any = __any(has_nan);
+}
+
+struct M1Plan {
+  int e[kMaxTopk];     // plan order (ascending id); -1 = dropped
+  float w[kMaxTopk];
+  int n_u;
+};
+
+// Wave 0 fills the block's plan (LDS) from the scores (mode 0) or from the
+// caller's header (mode 1); workgroup 0 writes the header (mode 0), the plan
+// tables and the status.
+template <int KPER>
+__device__ void plan_m1(int mode, const float* __restrict__ scores, const float* __restrict__ bias,
+                        const int32_t* __restrict__ header_in, int n_routed, int topk, int norm, float route_scale,
+                        int32_t* __restrict__ header_out, PlanView plan, int32_t* __restrict__ status, M1Plan& P) {
+  const int lane = threadIdx.x & 63;
+  int pick = 0;
+  float wv = 0.0f;
+  bool nan_any = false, ok = true;
+  if (mode == 0) {
+    select_wave<KPER>(scores, bias, n_routed, topk, norm, route_scale, pick, wv, nan_any);
+  } else {
+    if (lane < topk) {
+      pick = header_in[1 + lane];
+      wv = __builtin_bit_cast(float, header_in[1 + topk + lane]);
+    }
+    bool bad = lane < topk && (pick < 0 || pick >= n_routed);
+    for (int i = 0; i < topk; ++i) {
+      const int o = __shfl(pick, i);
+      if (lane < topk && i < lane && o == pick) bad = true;
+    }
+    ok = !__any(bad);
+  }
+  int rank = 0;
+  for (int i = 0; i < topk; ++i) rank += (__shfl(pick, i) < pick) ? 1 : 0;
+  if (lane < kMaxTopk) P.e[lane] = -1;        // a rejected header leaves every slot empty
+  if (lane < topk && ok) {
+    P.e[rank] = pick;
+    P.w[rank] = wv;
+  }
+  if (lane == 0) P.n_u = ok ? topk : 0;
+  if (blockIdx.x == 0) {
+    if (mode == 0 && lane < topk) {
+      header_out[1 + lane] = pick;
+      header_out[1 + topk + lane] = (int32_t)__builtin_bit_cast(uint32_t, wv);
+      header_out[1 + 2 * topk + rank] = pick;
+    }
+    if (lane < topk) {
+      if (ok) {
+        plan.u_expert()[rank] = pick;
+        plan.u_first()[rank] = rank;
+        plan.u_npairs()[rank] = 1;
+        plan.pair_tok()[rank] = 0;
+        plan.pair_expert()[rank] = pick;
+        plan.pair_w()[rank] = wv;
+        plan.tok_pairs()[rank] = rank;
+      } else {
+        plan.tok_pairs()[lane] = -1;
+      }
+    }
+    if (lane == 0) {
+      *plan.n_u() = ok ? topk : 0;
+      *plan.n_pairs() = ok ? topk : 0;
+      if (mode == 0) header_out[0] = nan_any ? MOE_STATUS_NAN_KEY : 0;
+      const int st = (nan_any ? MOE_STATUS_NAN_KEY : 0) | (ok ? 0 : MOE_STATUS_BAD_PICK);
+      if (st) atomicOr(status, st);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int NSB, int SLOTS, int KPER>
+__global__ __launch_bounds__(256) void k_gateup_m1(int mode, moe_experts ex, const float* __restrict__ scores,
+                                                   const float* __restrict__ bias, const int32_t* __restrict__ hdr_in,
+                                                   int n_routed, int topk, int norm, float route_scale,
+                                                   int32_t* __restrict__ hdr_out, Ws w, int dim, int inter,
+                                                   float L) {
+  using G = GateUpGeom<NSB>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float gu[2][32];
+  __shared__ M1Plan P;
+  const int ngr = inter / 32;
+  const int slot = blockIdx.x / ngr, grp = blockIdx.x % ngr;
+  if (threadIdx.x < 64)
+    plan_m1<KPER>(mode, scores, bias, hdr_in, n_routed, topk, norm, route_scale, hdr_out, w.plan, w.status, P);
+  __syncthreads();
+  const int e = P.e[slot];
+  if (e < 0) return;
+  const int sb = threadIdx.x % NSB;
+  const uint8_t* ebase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride;
+  auto tile_src = [&](int c) -> const uint8_t* {
+    const uint64_t off = (c & 1) ? ex.up_off : ex.gate_off;
+    return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
+  };
+  Act A;
+  load_act(A, w.xq, w.xd, w.xs, sb);
+#pragma unroll
+  for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int issued = (c + SLOTS < 4 ? c + SLOTS : 4);
+    const int after = issued - c - 1;
+    if (after == 3) wait_vmcnt<3 * G::kKC>();
+    else if (after == 2) wait_vmcnt<2 * G::kKC>();
+    else if (after == 1) wait_vmcnt<1 * G::kKC>();
+    else wait_vmcnt<0>();
+    block_sync_lds();
+    const uint8_t* sl = lds + (c % SLOTS) * G::kSlotBytes;
+    const int mat = c & 1, r0 = 16 * (c >> 1);
+#pragma unroll
+    for (int it = 0; it < G::kIters; ++it) {
+      const int i = it * 256 + threadIdx.x;
+      const bool act = i < G::kItems;
+      const int row = i / NSB;
+      double part = act ? dot_q2k(sl + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
+#pragma unroll
+      for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+      if (act && sb == 0) gu[mat][r0 + row] = (float)part;
+    }
+    if (c + SLOTS < 4) {
+      wait_lgkm0();
+      block_sync_lds();
+      dma_tile<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kSlotBytes, G::kTileChunks);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, r = lane & 31;
+    const float gv = gu[0][r], uv = gu[1][r];
+    const float hv = swiglu(gv, uv, L);
+    float a = fabsf(hv);
+    for (int s = 16; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
+    const float d = (float)((double)a / 127.0);
+    const int q = a == 0.0f ? 0 : q8_code(hv, d);
+    int sum = q;
+    for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+    if (lane < 32) {
+      const int64_t row = (int64_t)slot * inter + 32 * grp + r;
+      w.g[row] = gv;
+      w.u[row] = uv;
+      w.h[row] = hv;
+      w.hq[row] = (int8_t)q;
+      if (r == 0) w.hd[(int64_t)slot * (inter / 32) + grp] = __builtin_bit_cast(uint16_t, (_Float16)d);
+      if ((r & 15) == 0) w.hs[(int64_t)slot * (inter / 16) + 2 * grp + (r >> 4)] = sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave DMA of `nchunks` 16-byte chunks (lanes past the end re-read the
+// last chunk into the padding after it).
+template <int NCH>
+__device__ __forceinline__ void dma_wave(const uint8_t* g, uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < (NCH + 63) / 64; ++k) {
+    const int i = 64 * k + lane;
+    const int src = i < NCH ? i : NCH - 1;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * src),
+                                     (__attribute__((address_space(3))) void*)(dst + 16 * 64 * k), 16, 0, 0);
+  }
+}
+
+template <int NSB, int ROWS>
+struct DownM1Geom {
+  static constexpr int kRowBytes = NSB * kQ3KBytes;
+  static constexpr int kChunks = ROWS * kRowBytes / 16;
+  static constexpr int kWaveBytes = ((kChunks + 63) / 64) * 1024;
+  static constexpr int kItems = ROWS * NSB;            // per wave
+  static constexpr int kIters = (kItems + 63) / 64;
+};
+
+constexpr int kDownRows = 16;
+
+template <int NSB, bool SHARED>
+__global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
+                                                 const uint16_t* __restrict__ w2, float* __restrict__ out_f32,
+                                                 uint16_t* __restrict__ out_bf16) {
+  using G = DownM1Geom<NSB, kDownRows>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float ys[kMaxTopk][kDownRows];
+  __shared__ float sds[kDownRows];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = blockIdx.x * kDownRows;
+  const int n_u = *w.plan.n_u();
+  if (wave < topk) {
+    const int e = wave < n_u ? w.plan.u_expert()[wave] : -1;
+    if (e >= 0) {
+      const int sb = lane % NSB;
+      Act A;
+      load_act(A, w.hq + (int64_t)wave * inter, w.hd + (int64_t)wave * (inter / 32), w.hs + (int64_t)wave * (inter / 16),
+               sb);
+      uint8_t* mine = lds + wave * G::kWaveBytes;
+      dma_wave<G::kChunks>((const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off +
+                               (uint64_t)row0 * G::kRowBytes, mine);
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < G::kIters; ++it) {
+        const int i = it * 64 + lane;
+        const bool act = i < G::kItems;
+        const int row = i / NSB;
+        double part = act ? dot_q3k(mine + row * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
+#pragma unroll
+        for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+        if (act && sb == 0) {
+          ys[wave][row] = (float)part;
+          w.y[(int64_t)wave * dim + row0 + row] = (float)part;
+        }
+      }
+    } else if (lane < kDownRows) {
+      ys[wave][lane] = 0.0f;
+    }
+  } else if (SHARED && wave < topk + 2) {
+    // shared expert down rows: half of the block's rows per wave, f32
+    constexpr int kR = kDownRows / 2;
+    constexpr int kCh = NSB >= 2 ? NSB / 2 : 1;   // 16-byte chunks of a row per lane (inter = 256*NSB)
+    const int rbase = row0 + kR * (wave - topk);
+    float p[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) p[r] = 0.0f;
+    uint4 wv[kR][kCh];
+    uint4 hvv[kCh];
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {        // every load issued before any is used
+      const int k = 8 * lane + 512 * c;
+      const bool in = k < inter;
+      hvv[c] = in ? *reinterpret_cast<const uint4*>(w.sh + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < kR; ++r) wv[r][c] = in ? load_nt16(w2 + (int64_t)(rbase + r) * inter + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      float hv[8];
+      const uint32_t hh[4] = {hvv[c].x, hvv[c].y, hvv[c].z, hvv[c].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = bf16_f32((uint16_t)(hh[j >> 1] >> (16 * (j & 1))));
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const uint32_t ww[4] = {wv[r][c].x, wv[r][c].y, wv[r][c].z, wv[r][c].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          p[r] = __builtin_fmaf(bf16_f32((uint16_t)(ww[j >> 1] >> (16 * (j & 1)))), hv[j], p[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+      for (int s = 32; s >= 1; s >>= 1) p[r] += __shfl_xor(p[r], s);
+    if (lane < kR) {
+      float v = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+        if (r == lane) v = p[r];
+      sds[kR * (wave - topk) + lane] = v;
+      w.sd[rbase + lane] = v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kDownRows) {
+    const int r = threadIdx.x;
+    float acc = 0.0f;
+    for (int i = 0; i < topk; ++i)
+      if (i < n_u) acc = fadd(acc, fmul(w.plan.pair_w()[i], ys[i][r]));
+    if (SHARED) acc = fadd(acc, sds[r]);
+    if (out_f32) out_f32[row0 + r] = acc;
+    if (out_bf16) out_bf16[row0 + r] = bf16_rne(acc);
+  }
+}
+
+template <int NSB>
+hipError_t launch_gateup_m1_t(int mode, const moe_experts& ex, const float* bias, const int32_t* hdr_in,
+                              int32_t* hdr_out, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  using G = GateUpGeom<NSB>;
+  constexpr int kSlots = 3;
+  const int kper = (c.n_routed + 63) / 64;
+  size_t shm = (size_t)kSlots * G::kSlotBytes;
+  auto kern6 = k_gateup_m1<NSB, kSlots, 6>;
+  auto kern16 = k_gateup_m1<NSB, kSlots, 16>;
+  auto kern = kper == 6 ? kern6 : kern16;
+  static bool attr_set[2] = {false, false};
+  const int ai = kper == 6 ? 0 : 1;
+  if (!attr_set[ai]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set[ai] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(c.topk * (c.inter / 32)), dim3(256), shm, s, mode, ex, w.scores, bias, hdr_in,
+                     c.n_routed, c.topk, c.norm_topk_prob, c.route_scale, hdr_out, w, c.dim, c.inter, c.swiglu_limit);
+  return hipGetLastError();
+}
+
+template <int NSB>
+hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
+                            uint16_t* out_bf16, hipStream_t s) {
+  using G = DownM1Geom<NSB, kDownRows>;
+  size_t shm = (size_t)c.topk * G::kWaveBytes;
+  const int threads = 64 * (c.topk + (w2 ? 2 : 0));
+  auto kern = w2 ? k_down_m1<NSB, true> : k_down_m1<NSB, false>;
+  static bool attr_set[2] = {false, false};
+  const int ai = w2 ? 1 : 0;
+  if (!attr_set[ai]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kMaxTopk * G::kWaveBytes));
+    if (e != hipSuccess) return e;
+    attr_set[ai] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, c.topk, w2,
+                     out_f32, out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gateup_m1(int mode, const moe_experts& ex, const float* bias, const int32_t* hdr_in,
+                            int32_t* hdr_out, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  timed_begin(MOE_K_GATEUP, s);
+  hipError_t err;
+  switch (c.dim / 256) {
+    case 1: err = launch_gateup_m1_t<1>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
+    case 2: err = launch_gateup_m1_t<2>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
+    case 4: err = launch_gateup_m1_t<4>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
+    case 8: err = launch_gateup_m1_t<8>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
+    case 16: err = launch_gateup_m1_t<16>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
+    case 32: err = launch_gateup_m1_t<32>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
+    default: err = hipErrorInvalidValue; break;
+  }
+  timed_end(MOE_K_GATEUP, s);
+  return err;
+}
+
+hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s) {
+  timed_begin(MOE_K_DOWN, s);
+  hipError_t err;
+  switch (c.inter / 256) {
+    case 1: err = launch_down_m1_t<1>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 2: err = launch_down_m1_t<2>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 4: err = launch_down_m1_t<4>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 8: err = launch_down_m1_t<8>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 16: err = launch_down_m1_t<16>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    default: err = hipErrorInvalidValue; break;
+  }
+  timed_end(MOE_K_DOWN, s);
+  return err;
+}
+
+}  // namespace moe

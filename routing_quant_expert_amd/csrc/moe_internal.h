@@ -78,6 +78,13 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
 hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
+// single token: gate/up with the plan derived in every workgroup (mode 0: the
+// selection from the workspace scores; mode 1: the caller's header), then the
+// down rows of every pick + the shared expert's down rows + the combine.
+hipError_t launch_gateup_m1(int mode, const moe_experts& ex, const float* bias, const int32_t* hdr_in,
+                            int32_t* hdr_out, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s);
 
 // Timing hook (moe_time_next_launch): brackets the next launch of `which`.
 void timed_begin(int which, hipStream_t s);

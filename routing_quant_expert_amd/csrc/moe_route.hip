@@ -52,6 +52,7 @@ __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* _
 // never depend on the batch it rides in.
 // ---------------------------------------------------------------------------
 constexpr int kRouterTok = 8;
+constexpr int kLoadAhead = 8;   // 16-byte chunks per lane kept in flight by one wave
 
 __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int dim,
                             const uint16_t* __restrict__ gate_w, int n_routed, float temp, float* __restrict__ logits,
@@ -60,30 +61,42 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
   const int lane = threadIdx.x & 63;
   if (e >= n_routed) return;
   const uint16_t* wr = gate_w + (int64_t)e * dim;
+  const int nch = (dim + 511) / 512;
   for (int t0 = 0; t0 < m; t0 += kRouterTok) {
     const int nt = min(kRouterTok, m - t0);
     float p[kRouterTok];
 #pragma unroll
     for (int t = 0; t < kRouterTok; ++t) p[t] = 0.0f;
-    for (int base = 0; base < dim; base += 512) {
-      const int k = base + 8 * lane;
-      if (k < dim) {
-        uint4 wv = *reinterpret_cast<const uint4*>(wr + k);
-        uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    for (int c0 = 0; c0 < nch; c0 += kLoadAhead) {
+      uint4 wv[kLoadAhead];
 #pragma unroll
-        for (int t = 0; t < kRouterTok; ++t) {
-          if (t < nt) {
-            uint4 xv = *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + t) * dim + k);
-            uint32_t xx[4] = {xv.x, xv.y, xv.z, xv.w};
-            float acc = p[t];
+      for (int c = 0; c < kLoadAhead; ++c) {
+        const int k = 512 * (c0 + c) + 8 * lane;
+        wv[c] = (c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < kRouterTok; ++t) {
+        if (t < nt) {
+          uint4 xv[kLoadAhead];
+#pragma unroll
+          for (int c = 0; c < kLoadAhead; ++c) {
+            const int k = 512 * (c0 + c) + 8 * lane;
+            xv[c] = (c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + t) * dim + k)
+                                              : make_uint4(0, 0, 0, 0);
+          }
+          float acc = p[t];
+#pragma unroll
+          for (int c = 0; c < kLoadAhead; ++c) {
+            const uint32_t ww[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+            const uint32_t xx[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              uint16_t xb = (uint16_t)(xx[j >> 1] >> (16 * (j & 1)));
-              uint16_t wb = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
-              acc = fadd(acc, fmul(bf16_f32(xb), bf16_f32(wb)));
+              const uint16_t xb = (uint16_t)(xx[j >> 1] >> (16 * (j & 1)));
+              const uint16_t wb = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+              acc = fadd(acc, fmul(bf16_f32(xb), bf16_f32(wb)));   // zero padding adds +0: exact
             }
-            p[t] = acc;
           }
+          p[t] = acc;
         }
       }
     }
@@ -120,19 +133,33 @@ __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, i
   for (int t = 0; t < kMaxDecodeTokens; ++t) pg[t] = pu[t] = 0.0f;
   const uint16_t* r1 = w1 + (int64_t)i * dim;
   const uint16_t* r3 = w3 + (int64_t)i * dim;
-  for (int k = 8 * lane; k < dim; k += 512) {
-    float a[8], b[8];
-    bf16x8(load_nt16(r1 + k), a);
-    bf16x8(load_nt16(r3 + k), b);
+  const int nch = (dim + 511) / 512;
+  for (int c0 = 0; c0 < nch; c0 += kLoadAhead) {
+    uint4 av[kLoadAhead], bv[kLoadAhead];
+#pragma unroll
+    for (int c = 0; c < kLoadAhead; ++c) {
+      const int k = 512 * (c0 + c) + 8 * lane;
+      const bool in = c0 + c < nch && k < dim;
+      av[c] = in ? load_nt16(r1 + k) : make_uint4(0, 0, 0, 0);
+      bv[c] = in ? load_nt16(r3 + k) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int t = 0; t < kMaxDecodeTokens; ++t) {
       if (t < m) {
-        float xv[8];
-        bf16x8(*reinterpret_cast<const uint4*>(x + (int64_t)t * dim + k), xv);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pg[t] = __builtin_fmaf(a[j], xv[j], pg[t]);
-          pu[t] = __builtin_fmaf(b[j], xv[j], pu[t]);
+        for (int c = 0; c < kLoadAhead; ++c) {
+          const int k = 512 * (c0 + c) + 8 * lane;
+          if (c0 + c < nch && k < dim) {
+            float a[8], b[8], xv[8];
+            bf16x8(av[c], a);
+            bf16x8(bv[c], b);
+            bf16x8(*reinterpret_cast<const uint4*>(x + (int64_t)t * dim + k), xv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              pg[t] = __builtin_fmaf(a[j], xv[j], pg[t]);
+              pu[t] = __builtin_fmaf(b[j], xv[j], pu[t]);
+            }
+          }
         }
       }
     }

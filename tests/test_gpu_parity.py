@@ -203,7 +203,7 @@ def test_layer_forward_matches_oracle(shape, m):
         assert rel_l2(sg[t], ref["shared"][t]["sg"]) < 1e-5
 
 
-@pytest.mark.parametrize("shape,m", [(TINY, 3), (DS41, 2)])
+@pytest.mark.parametrize("shape,m", [(TINY, 1), (TINY, 3), (DS41, 1), (DS41, 2)])
 def test_experts_decode_matches_oracle(shape, m):
     dl = device_layer(shape)
     c = dl.cfg
@@ -216,6 +216,29 @@ def test_experts_decode_matches_oracle(shape, m):
     R.experts_decode(c, x, hdr, dl.experts, y, ws)
     torch.cuda.synchronize()
     _check_layer(dl, x_np, m, y.cpu().numpy(), None, hdr_np, ws, with_shared=False)
+
+
+def test_experts_decode_single_token_rejects_bad_picks():
+    dl = device_layer(TINY)
+    c = dl.cfg
+    x_np = synth.tokens(dl.spec, 0, 1)
+    _, hdr_np, _ = oracle_header(dl.spec, x_np)
+    ws = workspace(c, 1)
+    for bad in ((2, 384), (3, -1), (4, int(hdr_np[0, 1]))):
+        h = hdr_np.copy()
+        h[0, bad[0]] = bad[1]
+        y = torch.full((1, c.dim), 7.0, dtype=torch.float32, device="cuda")
+        R.experts_decode(c, torch.from_numpy(x_np).cuda(), torch.from_numpy(h).cuda(), dl.experts, y, ws)
+        torch.cuda.synchronize()
+        assert np.all(y.cpu().numpy() == 0), bad
+        L = R.workspace_layout(c, 1)
+        assert ws_array(ws, L, "status", np.int32, 1)[0] & R.MOE_STATUS_BAD_PICK
+    # and a good header afterwards still works in the same workspace
+    y = torch.empty((1, c.dim), dtype=torch.float32, device="cuda")
+    R.experts_decode(c, torch.from_numpy(x_np).cuda(), torch.from_numpy(hdr_np).cuda(), dl.experts, y, ws)
+    torch.cuda.synchronize()
+    ref = olayer.layer_forward(dl.spec, x_np, with_shared=False)
+    assert rel_l2(y.cpu().numpy()[0], ref["y_routed"][0]) < 1e-6
 
 
 def test_experts_decode_rejects_bad_picks():
