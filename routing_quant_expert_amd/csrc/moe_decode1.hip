@@ -15,68 +15,10 @@
 #include "moe_internal.h"
 #include "moe_kquant.h"
 #include "moe_math.h"
+#include "moe_select.h"
 
 namespace moe {
 namespace {
-
-__device__ inline bool ranks_before(float ka, int a, float kb, int b) {
-  const bool na = isnan(ka), nb = isnan(kb);
-  if (na != nb) return !na;
-  if (!na && ka != kb) return ka > kb;
-  return a < b;
-}
-
-// One wave: the top-k of one token [moe_v41.rs, fn route_from_logits].
-// Lane r < topk returns pick r (rank order) and its weight; *nan_any is set
-// when any key is NaN.
-template <int KPER>
-__device__ void select_wave(const float* __restrict__ sc, const float* __restrict__ bias, int n_routed, int topk,
-                            int norm, float route_scale, int& pick, float& weight, bool& nan_any) {
-  const int lane = threadIdx.x & 63;
-  float key[KPER];
-  bool has_nan = false;
-#pragma unroll
-  for (int c = 0; c < KPER; ++c) {
-    const int e = lane + 64 * c;
-    key[c] = e < n_routed ? fadd(sc[e], bias[e]) : 0.0f;
-    if (e < n_routed && isnan(key[c])) has_nan = true;
-  }
-  uint32_t taken = 0;
-  int mypick = 0;
-  for (int r = 0; r < topk; ++r) {
-    float bk = 0.0f;
-    int bid = 0x7fffffff;
-#pragma unroll
-    for (int c = 0; c < KPER; ++c) {
-      const int e = lane + 64 * c;
-      if (e < n_routed && !((taken >> c) & 1u) && (bid == 0x7fffffff || ranks_before(key[c], e, bk, bid))) {
-        bk = key[c];
-        bid = e;
-      }
-    }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float ok = __shfl_xor(bk, s);
-      const int oid = __shfl_xor(bid, s);
-      if (oid != 0x7fffffff && (bid == 0x7fffffff || ranks_before(ok, oid, bk, bid))) {
-        bk = ok;
-        bid = oid;
-      }
-    }
-    if (lane == r) mypick = bid;
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
-  }
-  float wv = lane < topk ? sc[mypick] : 0.0f;
-  if (norm && topk > 1) {
-    float sum = 0.0f;
-    for (int i = 0; i < topk; ++i) sum = fadd(sum, __shfl(wv, i));
-    sum = fadd(sum, 1e-20f);
-    wv = (float)((double)wv / (double)sum);
-  }
-  pick = mypick;
-  weight = fmul(wv, route_scale);
-  nan_any = __any(has_nan);
-}
 
 struct M1Plan {
   int e[kMaxTopk];     // plan order (ascending id); -1 = dropped
@@ -96,21 +38,31 @@ __device__ void plan_m1(int mode, const float* __restrict__ scores, const float*
   float wv = 0.0f;
   bool nan_any = false, ok = true;
   if (mode == 0) {
-    select_wave<KPER>(scores, bias, n_routed, topk, norm, route_scale, pick, wv, nan_any);
+    int picks[kMaxTopk];
+    float wts[kMaxTopk];
+    select_topk<KPER>(scores, bias, n_routed, topk, norm, route_scale, picks, wts, nan_any);
+#pragma unroll
+    for (int r = 0; r < kMaxTopk; ++r)
+      if (r == lane) {
+        pick = picks[r];
+        wv = wts[r];
+      }
   } else {
-    if (lane < topk) {
-      pick = header_in[1 + lane];
-      wv = __builtin_bit_cast(float, header_in[1 + topk + lane]);
-    }
+    const int li = min(lane, topk - 1);
+    pick = header_in[1 + li];
+    wv = __builtin_bit_cast(float, header_in[1 + topk + li]);
     bool bad = lane < topk && (pick < 0 || pick >= n_routed);
-    for (int i = 0; i < topk; ++i) {
-      const int o = __shfl(pick, i);
-      if (lane < topk && i < lane && o == pick) bad = true;
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i) {
+      const int o = __builtin_amdgcn_readlane(pick, i);
+      if (i < topk && lane < topk && i < lane && o == pick) bad = true;
     }
     ok = !__any(bad);
   }
   int rank = 0;
-  for (int i = 0; i < topk; ++i) rank += (__shfl(pick, i) < pick) ? 1 : 0;
+#pragma unroll
+  for (int i = 0; i < kMaxTopk; ++i)
+    if (i < topk) rank += (__builtin_amdgcn_readlane(pick, i) < pick) ? 1 : 0;
   if (lane < kMaxTopk) P.e[lane] = -1;        // a rejected header leaves every slot empty
   if (lane < topk && ok) {
     P.e[rank] = pick;
@@ -159,19 +111,19 @@ __global__ __launch_bounds__(256) void k_gateup_m1(int mode, moe_experts ex, con
   __shared__ M1Plan P;
   const int ngr = inter / 32;
   const int slot = blockIdx.x / ngr, grp = blockIdx.x % ngr;
+  const int sb = threadIdx.x % NSB;
+  Act A;
+  load_act(A, w.xq, w.xd, w.xs, sb);   // independent of the plan: in flight during the selection
   if (threadIdx.x < 64)
     plan_m1<KPER>(mode, scores, bias, hdr_in, n_routed, topk, norm, route_scale, hdr_out, w.plan, w.status, P);
-  __syncthreads();
+  __syncthreads();   // also completes every wave's outstanding loads: the tile DMA below is all vmcnt sees
   const int e = P.e[slot];
   if (e < 0) return;
-  const int sb = threadIdx.x % NSB;
   const uint8_t* ebase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride;
   auto tile_src = [&](int c) -> const uint8_t* {
     const uint64_t off = (c & 1) ? ex.up_off : ex.gate_off;
     return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
   };
-  Act A;
-  load_act(A, w.xq, w.xd, w.xs, sb);
 #pragma unroll
   for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
 #pragma unroll

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
     const int tok = plan.pair_tok()[first];
     load_act(A, xq + (int64_t)tok * dim, xd + (int64_t)tok * (dim / 32), xs + (int64_t)tok * (dim / 16), sb);
   }
+  __syncthreads();   // completes the activation loads: the tile DMA below is all vmcnt sees
 #pragma unroll
   for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
 #pragma unroll

@@ -9,6 +9,7 @@
 
 #include "moe_internal.h"
 #include "moe_math.h"
+#include "moe_select.h"
 
 namespace moe {
 namespace {
@@ -214,69 +215,30 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
 }
 
 // ---------------------------------------------------------------------------
-// Selection, one wave per token [moe_v41.rs, fn route_from_logits]: key =
-// score + bias; the top-k by key, larger first, equal keys by ascending id
-// (the pages' sort is stable), NaN keys last; weights = the unbiased scores
-// of the picks, renormalised (sum in pick order, plus 1e-20) and scaled by
-// route_scale, each step one f32 rounding. Lane r holds pick r. Writes the
-// header [device_route.rs, fn parse_header] and the picks/weights to LDS.
+// Selection, one wave per token (moe_select.h): writes the header
+// [device_route.rs, fn parse_header] and, for the plan, the picks/weights.
 // ---------------------------------------------------------------------------
-__device__ inline bool ranks_before(float ka, int a, float kb, int b) {
-  const bool na = isnan(ka), nb = isnan(kb);
-  if (na != nb) return !na;
-  if (!na && ka != kb) return ka > kb;
-  return a < b;
-}
-
 template <int KPER>
 __device__ void select_token(const float* __restrict__ sc, const float* __restrict__ bias, int n_routed, int topk,
                              int norm, float route_scale, int32_t* __restrict__ hd, int* picks_out, float* w_out,
                              int32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63;
-  float key[KPER];
-  bool any_nan = false;
-#pragma unroll
-  for (int c = 0; c < KPER; ++c) {
-    const int e = lane + 64 * c;
-    key[c] = e < n_routed ? fadd(sc[e], bias[e]) : 0.0f;
-    if (e < n_routed && isnan(key[c])) any_nan = true;
-  }
-  uint32_t taken = 0;
+  int picks[kMaxTopk];
+  float wts[kMaxTopk];
+  bool nan_any = false;
+  select_topk<KPER>(sc, bias, n_routed, topk, norm, route_scale, picks, wts, nan_any);
   int mypick = 0;
-  for (int r = 0; r < topk; ++r) {
-    float bk = 0.0f;
-    int bid = 0x7fffffff;
+  float wv = 0.0f;
 #pragma unroll
-    for (int c = 0; c < KPER; ++c) {
-      const int e = lane + 64 * c;
-      if (e < n_routed && !((taken >> c) & 1u) && (bid == 0x7fffffff || ranks_before(key[c], e, bk, bid))) {
-        bk = key[c];
-        bid = e;
-      }
+  for (int r = 0; r < kMaxTopk; ++r)
+    if (r == lane) {
+      mypick = picks[r];
+      wv = wts[r];
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float ok = __shfl_xor(bk, s);
-      const int oid = __shfl_xor(bid, s);
-      if (oid != 0x7fffffff && (bid == 0x7fffffff || ranks_before(ok, oid, bk, bid))) {
-        bk = ok;
-        bid = oid;
-      }
-    }
-    if (lane == r) mypick = bid;
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
-  }
-  float wv = lane < topk ? sc[mypick] : 0.0f;
-  if (norm && topk > 1) {
-    float sum = 0.0f;
-    for (int i = 0; i < topk; ++i) sum = fadd(sum, __shfl(wv, i));
-    sum = fadd(sum, 1e-20f);
-    wv = (float)((double)wv / (double)sum);
-  }
-  wv = fmul(wv, route_scale);
   int rank = 0;
-  for (int i = 0; i < topk; ++i) rank += (__shfl(mypick, i) < mypick) ? 1 : 0;
-  const bool nan_any = __any(any_nan);
+#pragma unroll
+  for (int r = 0; r < kMaxTopk; ++r)
+    if (r < topk) rank += picks[r] < mypick ? 1 : 0;
   if (lane < topk) {
     hd[1 + lane] = mypick;
     hd[1 + topk + lane] = (int32_t)__builtin_bit_cast(uint32_t, wv);
