@@ -143,8 +143,7 @@ __global__ __launch_bounds__(256) void k_gateup_m1(int mode, moe_experts ex, con
       const bool act = i < G::kItems;
       const int row = i / NSB;
       double part = act ? dot_q2k(sl + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
-#pragma unroll
-      for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+      part = seg_sum_f64<NSB>(part);
       if (act && sb == 0) gu[mat][r0 + row] = (float)part;
     }
     if (c + SLOTS < 4) {
@@ -231,8 +230,7 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
         const bool act = i < G::kItems;
         const int row = i / NSB;
         double part = act ? dot_q3k(mine + row * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
-#pragma unroll
-        for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+        part = seg_sum_f64<NSB>(part);
         if (act && sb == 0) {
           ys[wave][row] = (float)part;
           w.y[(int64_t)wave * dim + row0 + row] = (float)part;

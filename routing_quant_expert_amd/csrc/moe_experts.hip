@@ -79,8 +79,7 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
         const bool act = i < G::kItems;
         const int row = i / NSB;
         double part = act ? dot_q2k(slot + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
-#pragma unroll
-        for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+        part = seg_sum_f64<NSB>(part);
         if (act && sb == 0) gu[mat][j][r0 + row] = (float)part;
       }
     }
@@ -206,8 +205,7 @@ __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, con
       const int row = i / NSB;                       // 0..31
       const uint8_t* p = lds + (row >> 4) * G::kSlotBytes + (row & 15) * G::kRowBytes + kQ3KBytes * sb;
       double part = act ? dot_q3k(p, A) : 0.0;
-#pragma unroll
-      for (int s = 1; s < NSB; s <<= 1) part += __shfl_xor(part, s);
+      part = seg_sum_f64<NSB>(part);
       if (act && sb == 0) y[(int64_t)pair * dim + 32 * grp + row] = (float)part;
     }
   }

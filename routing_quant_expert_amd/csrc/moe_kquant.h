@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "moe_math.h"
 
@@ -83,6 +85,34 @@ __device__ inline void load_act(Act& A, const int8_t* q, const uint16_t* d, cons
 // Code word wi (bytes 4wi..4wi+3 of the 64 code bytes) holds, at bit pair j,
 // the codes of weights 128*(wi/8) + 32*j + 4*(wi%8) + 0..3, i.e. sub-block
 // s = 8*(wi/8) + 2*j + (wi%8)/4, activation word 32*(wi/8) + 8*j + wi%8.
+//
+// To save the shifts, bit pairs j = 1 and 2 are masked in place: their bytes
+// hold 4*code and 16*code (still < 128, so the signed dot4 is exact), and the
+// sub-block sums carry that factor 4^j until the float64 step, where the
+// q8_1 block scale is divided by it (an exact power of two). The 24-bit
+// multiplies (full rate) are exact: every operand is below 2^23.
+
+__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
+
+// Sum of v over aligned groups of NSB lanes (every lane of a group gets the
+// group's sum; the same fixed order on every run).
+template <int NSB>
+__device__ __forceinline__ double seg_sum_f64(double v) {
+  auto step = [](double x, auto ctrl_tag) -> double {
+    constexpr int CTRL = decltype(ctrl_tag)::value;
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+    return x + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  };
+  if constexpr (NSB >= 2) v = step(v, std::integral_constant<int, 0xb1>{});    // lane ^ 1
+  if constexpr (NSB >= 4) v = step(v, std::integral_constant<int, 0x4e>{});    // lane ^ 2
+  if constexpr (NSB >= 8) v = step(v, std::integral_constant<int, 0x141>{});   // other quad of the half row
+  if constexpr (NSB >= 16) v = step(v, std::integral_constant<int, 0x140>{});  // other half of the row
+  if constexpr (NSB >= 32) v += __shfl_xor(v, 16);
+  if constexpr (NSB >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
 
 // Q2_K (84 B: scales[16], qs[64], d, dmin) at a 4-byte aligned LDS address.
 __device__ inline double dot_q2k(const uint8_t* p, const Act& A) {
@@ -92,30 +122,38 @@ __device__ inline double dot_q2k(const uint8_t* p, const Act& A) {
   for (int i = 0; i < 4; ++i) sc[i] = p32[i];
 #pragma unroll
   for (int i = 0; i < 16; ++i) qs[i] = p32[4 + i];
-  uint32_t dd = p32[20];
+  const uint32_t dd = p32[20];
   int I[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s) I[s] = 0;
 #pragma unroll
   for (int wi = 0; wi < 16; ++wi) {
     const int h = wi >> 3, t4 = wi & 7, half = t4 >> 2;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t v = (qs[wi] >> (2 * j)) & 0x03030303u;
-      I[8 * h + 2 * j + half] = __builtin_amdgcn_sdot4((int)v, (int)A.a[32 * h + 8 * j + t4], I[8 * h + 2 * j + half], false);
-    }
+    const uint32_t w = qs[wi];
+    const uint32_t v0 = w & 0x03030303u;           // 1 * code
+    const uint32_t v1 = w & 0x0C0C0C0Cu;           // 4 * code
+    const uint32_t v2 = w & 0x30303030u;           // 16 * code
+    const uint32_t v3 = (w >> 6) & 0x03030303u;    // 1 * code
+    int* Ih = I + 8 * h + half;
+    Ih[0] = __builtin_amdgcn_sdot4((int)v0, (int)A.a[32 * h + t4], Ih[0], false);
+    Ih[2] = __builtin_amdgcn_sdot4((int)v1, (int)A.a[32 * h + 8 + t4], Ih[2], false);
+    Ih[4] = __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
+    Ih[6] = __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
   }
   double accS = 0.0, accM = 0.0;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    uint32_t b0 = (sc[t >> 1] >> (16 * (t & 1))) & 0xFFu;
-    uint32_t b1 = (sc[t >> 1] >> (16 * (t & 1) + 8)) & 0xFFu;
-    int S = (int)(b0 & 15u) * I[2 * t] + (int)(b1 & 15u) * I[2 * t + 1];
-    int M = (int)(b0 >> 4) * A.Q[2 * t] + (int)(b1 >> 4) * A.Q[2 * t + 1];
-    accS = __builtin_fma(A.D8[t], (double)S, accS);
+    const uint32_t word = sc[t >> 1] >> (16 * (t & 1));
+    const int sa = (int)(word & 15u), ma = (int)((word >> 4) & 15u);
+    const int sb_ = (int)((word >> 8) & 15u), mb = (int)((word >> 12) & 15u);
+    const int S = mad24(sa, I[2 * t], __mul24(sb_, I[2 * t + 1]));
+    const int M = mad24(ma, A.Q[2 * t], __mul24(mb, A.Q[2 * t + 1]));
+    const int j = t & 3;
+    const double fj = j == 1 ? 0.25 : (j == 2 ? 0.0625 : 1.0);   // undo the in-place 4^j
+    accS = __builtin_fma(A.D8[t] * fj, (double)S, accS);
     accM = __builtin_fma(A.D8[t], (double)M, accM);
   }
-  double d = fp16_f64(dd & 0xFFFFu), dmin = fp16_f64(dd >> 16);
+  const double d = fp16_f64(dd & 0xFFFFu), dmin = fp16_f64(dd >> 16);
   return d * accS - dmin * accM;
 }
 
@@ -124,7 +162,10 @@ __device__ inline uint32_t ld32_a2(const uint8_t* p) {   // 2-byte aligned LDS d
   return (uint32_t)p16[0] | ((uint32_t)p16[1] << 16);
 }
 
-// Q3_K (110 B: hmask[32], qs[64], scales[12], d) at a 2-byte aligned LDS address.
+// Q3_K (110 B: hmask[32], qs[64], scales[12], d) at a 2-byte aligned LDS
+// address. A weight is q2 + 4*hb - 4 (q2 the 2-bit code, hb its hmask bit);
+// the dot4 runs on q2 + 4*hb (0..7, scaled by 4^j in place for j = 1, 2) and
+// the -4 comes back through the per-16 activation sums.
 __device__ inline double dot_q3k(const uint8_t* p, const Act& A) {
   uint32_t hm[8], qs[16], sc[3];
 #pragma unroll
@@ -133,36 +174,43 @@ __device__ inline double dot_q3k(const uint8_t* p, const Act& A) {
   for (int i = 0; i < 16; ++i) qs[i] = ld32_a2(p + 32 + 4 * i);
 #pragma unroll
   for (int i = 0; i < 3; ++i) sc[i] = ld32_a2(p + 96 + 4 * i);
-  uint32_t dbits = reinterpret_cast<const uint16_t*>(p)[54];
+  const uint32_t dbits = reinterpret_cast<const uint16_t*>(p)[54];
   int I[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s) I[s] = 0;
 #pragma unroll
   for (int wi = 0; wi < 16; ++wi) {
     const int h = wi >> 3, t4 = wi & 7, half = t4 >> 2;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t q2 = (qs[wi] >> (2 * j)) & 0x03030303u;
-      uint32_t hb = (hm[t4] >> (4 * h + j)) & 0x01010101u;
-      uint32_t v = q2 | (hb << 2);   // value + 4, in 0..7
-      I[8 * h + 2 * j + half] = __builtin_amdgcn_sdot4((int)v, (int)A.a[32 * h + 8 * j + t4], I[8 * h + 2 * j + half], false);
-    }
+    const uint32_t w = qs[wi], m = hm[t4];
+    // bytes of (q2 + 4*hb) * f_j: hb is bit 4h+j of each hmask byte, moved to bit 2+2j (j<3) or 2 (j=3)
+    const uint32_t v0 = (w & 0x03030303u) | (((m >> (4 * h)) << 2) & 0x04040404u);
+    const uint32_t v1 = (w & 0x0C0C0C0Cu) | ((4 * h + 1 >= 4 ? (m >> (4 * h + 1 - 4)) : (m << (4 - 4 * h - 1))) & 0x10101010u);
+    const uint32_t v2 = (w & 0x30303030u) | ((4 * h + 2 >= 6 ? (m >> (4 * h + 2 - 6)) : (m << (6 - 4 * h - 2))) & 0x40404040u);
+    const uint32_t v3 = ((w >> 6) & 0x03030303u) | ((4 * h + 3 >= 2 ? (m >> (4 * h + 3 - 2)) : (m << (2 - 4 * h - 3))) & 0x04040404u);
+    int* Ih = I + 8 * h + half;
+    Ih[0] = __builtin_amdgcn_sdot4((int)v0, (int)A.a[32 * h + t4], Ih[0], false);
+    Ih[2] = __builtin_amdgcn_sdot4((int)v1, (int)A.a[32 * h + 8 + t4], Ih[2], false);
+    Ih[4] = __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
+    Ih[6] = __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
   }
   double acc = 0.0;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
+    const int j = t & 3;
+    const int fj = j == 1 ? 4 : (j == 2 ? 16 : 1);
     int S = 0;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int s = 2 * t + k;
-      uint32_t lo_b = (sc[(s & 7) >> 2] >> (8 * (s & 3))) & 0xFFu;   // byte s (s<8) or s-8
-      uint32_t lo = s < 8 ? (lo_b & 15u) : (lo_b >> 4);
-      uint32_t hi_b = (sc[2] >> (8 * (s & 3))) & 0xFFu;               // byte 8 + s%4
-      uint32_t hi = (hi_b >> (2 * (s >> 2))) & 3u;
-      int us = (int)(lo | (hi << 4)) - 32;
-      S += us * (I[s] - 4 * A.Q[s]);
+      const uint32_t lo_b = (sc[(s & 7) >> 2] >> (8 * (s & 3))) & 0xFFu;   // byte s (s<8) or s-8
+      const uint32_t lo = s < 8 ? (lo_b & 15u) : (lo_b >> 4);
+      const uint32_t hi_b = (sc[2] >> (8 * (s & 3))) & 0xFFu;               // byte 8 + s%4
+      const uint32_t hi = (hi_b >> (2 * (s >> 2))) & 3u;
+      const int us = (int)(lo | (hi << 4)) - 32;
+      S = mad24(us, I[s] - 4 * fj * A.Q[s], S);
     }
-    acc = __builtin_fma(A.D8[t], (double)S, acc);
+    const double fjd = j == 1 ? 0.25 : (j == 2 ? 0.0625 : 1.0);
+    acc = __builtin_fma(A.D8[t] * fjd, (double)S, acc);
   }
   return fp16_f64(dbits) * acc;
 }
