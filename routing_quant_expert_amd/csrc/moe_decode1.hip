@@ -109,16 +109,20 @@ __global__ __launch_bounds__(256) void k_gateup_m1(int mode, moe_experts ex, con
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float gu[2][32];
   __shared__ M1Plan P;
+  __shared__ __align__(16) uint8_t act_lds[ActLds<NSB>::kBytes];
   const int ngr = inter / 32;
   const int slot = blockIdx.x / ngr, grp = blockIdx.x % ngr;
   const int sb = threadIdx.x % NSB;
-  Act A;
-  load_act(A, w.xq, w.xd, w.xs, sb);   // independent of the plan: in flight during the selection
-  if (threadIdx.x < 64)
+  if (threadIdx.x < 64) {
     plan_m1<KPER>(mode, scores, bias, hdr_in, n_routed, topk, norm, route_scale, hdr_out, w.plan, w.status, P);
+  } else {   // meanwhile the other waves stage the token's q8_1 activation, once for the block
+    for (int i = threadIdx.x - 64; i < ActLds<NSB>::kChunks; i += 192) act_piece_to_lds<NSB>(act_lds, w.xq, w.xs, w.xd, i);
+  }
   __syncthreads();   // also completes every wave's outstanding loads: the tile DMA below is all vmcnt sees
   const int e = P.e[slot];
   if (e < 0) return;
+  Act A;
+  load_act_lds<NSB>(A, act_lds, sb);
   const uint8_t* ebase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride;
   auto tile_src = [&](int c) -> const uint8_t* {
     const uint64_t off = (c & 1) ? ex.up_off : ex.gate_off;
@@ -207,6 +211,7 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
                                                  uint16_t* __restrict__ out_bf16) {
   using G = DownM1Geom<NSB, kDownRows>;
   extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ __align__(16) uint8_t act_lds[kMaxTopk][ActLds<NSB>::kBytes];
   __shared__ float ys[kMaxTopk][kDownRows];
   __shared__ float sds[kDownRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -216,14 +221,18 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
     const int e = wave < n_u ? w.plan.u_expert()[wave] : -1;
     if (e >= 0) {
       const int sb = lane % NSB;
-      Act A;
-      load_act(A, w.hq + (int64_t)wave * inter, w.hd + (int64_t)wave * (inter / 32), w.hs + (int64_t)wave * (inter / 16),
-               sb);
       uint8_t* mine = lds + wave * G::kWaveBytes;
       dma_wave<G::kChunks>((const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off +
                                (uint64_t)row0 * G::kRowBytes, mine);
+      // this expert's q8_1(h), staged once for the wave while its rows stream in
+      uint8_t* al = act_lds[wave];
+      for (int i = lane; i < ActLds<NSB>::kChunks; i += 64)
+        act_piece_to_lds<NSB>(al, w.hq + (int64_t)wave * inter, w.hs + (int64_t)wave * (inter / 16),
+                              w.hd + (int64_t)wave * (inter / 32), i);
       wait_vmcnt<0>();
       asm volatile("" ::: "memory");
+      Act A;
+      load_act_lds<NSB>(A, al, sb);
 #pragma unroll
       for (int it = 0; it < G::kIters; ++it) {
         const int i = it * 64 + lane;

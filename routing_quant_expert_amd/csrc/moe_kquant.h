@@ -81,6 +81,67 @@ __device__ inline void load_act(Act& A, const int8_t* q, const uint16_t* d, cons
   for (int t = 0; t < 8; ++t) A.D8[t] = fp16_f64((dw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
 }
 
+// The same activation staged once per workgroup in LDS (instead of every
+// lane fetching its own copy from L2): per super-block sb the 256 codes,
+// then the 16 code sums, then the 8 scales. The codes and sums of
+// consecutive sb are padded by 16 bytes so that the 16 lanes of a quarter
+// wave (16 different sb) read different LDS banks.
+template <int NSB>
+struct ActLds {
+  static constexpr int kCodeStride = 256 + 16;
+  static constexpr int kQStride = 64 + 16;
+  static constexpr int kQ = NSB * kCodeStride;
+  static constexpr int kD = kQ + NSB * kQStride;
+  static constexpr int kBytes = kD + NSB * 16;
+  static constexpr int kChunks = NSB * 21;   // 16-byte pieces: 16 code, 4 sum, 1 scale per sb
+};
+
+// Copies piece i (< ActLds<NSB>::kChunks) of one token's q8_1 activation.
+template <int NSB>
+__device__ __forceinline__ void act_piece_to_lds(uint8_t* lds, const int8_t* q, const int32_t* s, const uint16_t* d,
+                                                 int i) {
+  using AL = ActLds<NSB>;
+  if (i < NSB * 16) {
+    *reinterpret_cast<uint4*>(lds + (i >> 4) * AL::kCodeStride + 16 * (i & 15)) =
+        *reinterpret_cast<const uint4*>(q + 16 * i);
+  } else if (i < NSB * 20) {
+    const int j = i - NSB * 16;
+    *reinterpret_cast<uint4*>(lds + AL::kQ + (j >> 2) * AL::kQStride + 16 * (j & 3)) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(s) + 16 * j);
+  } else {
+    const int j = i - NSB * 20;
+    *reinterpret_cast<uint4*>(lds + AL::kD + 16 * j) =
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(d) + 16 * j);
+  }
+}
+
+template <int NSB>
+__device__ __forceinline__ void load_act_lds(Act& A, const uint8_t* lds, int sb) {
+  using AL = ActLds<NSB>;
+  const uint4* q4 = reinterpret_cast<const uint4*>(lds + sb * AL::kCodeStride);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint4 v = q4[i];
+    A.a[4 * i] = v.x;
+    A.a[4 * i + 1] = v.y;
+    A.a[4 * i + 2] = v.z;
+    A.a[4 * i + 3] = v.w;
+  }
+  const int4* s4 = reinterpret_cast<const int4*>(lds + AL::kQ + sb * AL::kQStride);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int4 v = s4[i];
+    A.Q[4 * i] = v.x;
+    A.Q[4 * i + 1] = v.y;
+    A.Q[4 * i + 2] = v.z;
+    A.Q[4 * i + 3] = v.w;
+  }
+  const uint4 dv = *reinterpret_cast<const uint4*>(lds + AL::kD + 16 * sb);
+  const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) A.D8[t] = fp16_f64((dw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
+}
+
 // Weight w of a super-block: h = w/128, j = (w%128)/32, l = w%32, s = w/16.
 // Code word wi (bytes 4wi..4wi+3 of the 64 code bytes) holds, at bit pair j,
 // the codes of weights 128*(wi/8) + 32*j + 4*(wi%8) + 0..3, i.e. sub-block

@@ -4,10 +4,8 @@
 //   ascending expert id (the pages' stable sort over ids 0..n-1), NaN keys
 //   after every other key; weights = the unbiased scores of the picks in pick
 //   order, renormalised by their f32 sum (+1e-20) and scaled by route_scale.
-// Each expert gets a 64-bit composite that orders exactly like that rule:
-//   high word: the key's bits mapped to an unsigned order (+0 and -0 equal,
-//   NaN lowest), low word: ~id. A round takes the wave maximum of the
-//   not-yet-taken composites with a DPP reduction (no LDS traffic).
+// Keys are compared through their bits mapped to an unsigned order (+0 and
+// -0 equal, NaN lowest); the wave maximum is a DPP reduction (no LDS).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,76 +20,69 @@ __device__ __forceinline__ uint32_t key_order_bits(float k) {
   return (u >> 31) ? ~u : (u | 0x80000000u);
 }
 
-// DPP move of a 32-bit value (bound_ctrl: lanes without a source read 0).
-template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
-}
-
-template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = dpp_u32<CTRL, ROW_MASK, BANK_MASK>((uint32_t)v);
-  const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BANK_MASK>((uint32_t)(v >> 32));
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  return o > v ? o : v;
-}
-
-// Maximum of v over the 64 lanes, returned uniformly (from lane 63).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_step<0xb1>(v);          // quad_perm [1,0,3,2]
-  v = dpp_max_step<0x4e>(v);          // quad_perm [2,3,0,1]
-  v = dpp_max_step<0x114>(v);         // row_shr:4
-  v = dpp_max_step<0x118>(v);         // row_shr:8
-  v = dpp_max_step<0x142, 0xa>(v);    // row_bcast:15
-  v = dpp_max_step<0x143, 0xc>(v);    // row_bcast:31
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Maximum of v over the 64 lanes, returned uniformly (from lane 63), by a
+// DPP reduction: quad_perm [1,0,3,2], [2,3,0,1], row_shr:4, row_shr:8,
+// row_bcast:15, row_bcast:31.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // The wave selects `topk` experts from scores[0..n_routed) (this token's row)
 // with bias. On return every lane holds the same picks[] (rank order) and
 // weights[]; nan_any tells whether any key was NaN. KPER = ceil(n_routed/64).
+// A round takes the wave maximum of the available keys' order bits, then the
+// smallest id holding that maximum (one ballot per register column, in id
+// order), which is exactly the pages' stable descending sort.
 template <int KPER>
 __device__ __forceinline__ void select_topk(const float* __restrict__ scores, const float* __restrict__ bias,
                                             int n_routed, int topk, int norm, float route_scale,
                                             int (&picks)[kMaxTopk], float (&weights)[kMaxTopk], bool& nan_any) {
   const int lane = threadIdx.x & 63;
-  float sc[KPER];
-  uint64_t comp[KPER];
-  bool has_nan = false;
-  float bs[KPER];
+  float sc[KPER], bs[KPER];
 #pragma unroll
   for (int c = 0; c < KPER; ++c) {   // every load issued before any is used (indices clamped, no branches)
     const int e = min(lane + 64 * c, n_routed - 1);
     sc[c] = scores[e];
     bs[c] = bias[e];
   }
+  uint32_t ko[KPER];
+  uint32_t avail = 0;                // bit c: expert lane + 64c still available
+  bool has_nan = false;
 #pragma unroll
   for (int c = 0; c < KPER; ++c) {
-    const int e = lane + 64 * c;
-    const bool in = e < n_routed;
+    const bool in = lane + 64 * c < n_routed;
     const float k = fadd(sc[c], bs[c]);
     has_nan |= in && isnan(k);
-    comp[c] = in ? (((uint64_t)key_order_bits(k) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+    ko[c] = key_order_bits(k);
+    avail |= in ? (1u << c) : 0u;
   }
   nan_any = __any(has_nan);
 #pragma unroll
   for (int r = 0; r < kMaxTopk; ++r) {
     if (r < topk) {
-      uint64_t best = 0;
+      uint32_t best = 0;
 #pragma unroll
-      for (int c = 0; c < KPER; ++c) best = comp[c] > best ? comp[c] : best;
-      const uint64_t win = wave_max_u64(best);
-      const int id = (int)(0xFFFFFFFFu - (uint32_t)win);
+      for (int c = 0; c < KPER; ++c) best = ((avail >> c) & 1u) ? max(best, ko[c]) : best;
+      const uint32_t top = wave_max_u32(best);
+      int id = -1;
+#pragma unroll
+      for (int c = 0; c < KPER; ++c) {
+        const unsigned long long b = __ballot(((avail >> c) & 1u) && ko[c] == top);
+        if (id < 0 && b) id = 64 * c + __builtin_ctzll(b);
+      }
       const int wc = id >> 6, wl = id & 63;
       float s_here = sc[0];
 #pragma unroll
       for (int c = 1; c < KPER; ++c) s_here = (c == wc) ? sc[c] : s_here;
       weights[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_here), wl));
       picks[r] = id;
-#pragma unroll
-      for (int c = 0; c < KPER; ++c) comp[c] = (c == wc && lane == wl) ? 0ull : comp[c];
+      if (lane == wl) avail &= ~(1u << wc);
     }
   }
   if (norm && topk > 1) {
