@@ -23,6 +23,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("moe_decode1.hip", "moe_kquant.h", "moe_select.h", "moe_math.h", "moe_internal.h")
+
+
+def kernel_source_sha() -> str:
+    """Hash of the sources of the single-token kernels (ties measured counters to a kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routing_quant_expert_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_decode_m1_dim4096.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(\{.*?\})\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel") != kernel or d.get("source_sha") != kernel_source_sha():
+        return None
+    return d.get("traffic_bytes")
 
 
 class HipEvents:
@@ -92,7 +119,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's expert kernels")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 256 MiB device-to-device three times (calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        src = torch.full((256 << 20,), 3, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {src.numel()} bytes x3", flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
               f"of the layer is a design note, not a measured path.", file=sys.stderr)
@@ -170,7 +209,7 @@ def main():
                    "n_routed": s.n_routed, "topk": s.topk, "m": 1, "tokens_cycled": args.tokens,
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_gateup",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("k_gateup_m1"), "kernel": "k_gateup_m1",
                      "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg * 1e6, "timed_launches": int(nt)},
         "routed_gemvs": {"gateup_us": gu_avg * 1e6, "down_us": dn_avg * 1e6, "bytes": gu_bytes + dn_bytes,
                          "achieved_gbs": routed_gbs, "frac": routed_gbs / HBM_PEAK_GBS,

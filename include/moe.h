@@ -191,8 +191,13 @@ int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int3
 int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, float* out);
 
 /* Kernel timing hook: the next launch of kernel `which` (MOE_K_*) on the
- * calling thread is bracketed by hipEventRecord(begin) / (end) on its
- * stream. One-shot; pass NULL events to clear. For measurement only. */
+ * calling thread records the two events (hipEvent_t, created by the caller)
+ * at its dispatch's start and end (hipExtLaunchKernelGGL), on the stream it
+ * is launched on. One-shot; pass NULL events to clear. For measurement only.
+ *   MOE_K_GATEUP  the routed gate/up (Q2_K) kernel
+ *   MOE_K_DOWN    the routed down (Q3_K) kernel (with the shared down rows
+ *                 and the combine in the single-token layer)
+ *   MOE_K_ROUTER  the front kernel (q8_1 of x, router, shared gate/up) */
 #define MOE_K_GATEUP 1
 #define MOE_K_DOWN 2
 #define MOE_K_ROUTER 3

@@ -120,15 +120,12 @@ Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m) {
   return w;
 }
 
-void timed_begin(int which, hipStream_t s) {
-  if (which >= 1 && which <= 3 && g_ev_begin[which]) hipEventRecord(g_ev_begin[which], s);
-}
-
-void timed_end(int which, hipStream_t s) {
-  if (which >= 1 && which <= 3 && g_ev_end[which]) {
-    hipEventRecord(g_ev_end[which], s);
-    g_ev_begin[which] = g_ev_end[which] = nullptr;
-  }
+bool take_timed(int which, hipEvent_t* begin, hipEvent_t* end) {
+  if (which < 1 || which > 3 || !g_ev_begin[which] || !g_ev_end[which]) return false;
+  *begin = g_ev_begin[which];
+  *end = g_ev_end[which];
+  g_ev_begin[which] = g_ev_end[which] = nullptr;
+  return true;
 }
 
 }  // namespace moe

@@ -321,8 +321,8 @@ hipError_t launch_gateup_m1_t(int mode, const moe_experts& ex, const float* bias
     if (e != hipSuccess) return e;
     attr_set[ai] = true;
   }
-  hipLaunchKernelGGL(kern, dim3(c.topk * (c.inter / 32)), dim3(256), shm, s, mode, ex, w.scores, bias, hdr_in,
-                     c.n_routed, c.topk, c.norm_topk_prob, c.route_scale, hdr_out, w, c.dim, c.inter, c.swiglu_limit);
+  MOE_LAUNCH(MOE_K_GATEUP, kern, dim3(c.topk * (c.inter / 32)), dim3(256), shm, s, mode, ex, w.scores, bias, hdr_in,
+             c.n_routed, c.topk, c.norm_topk_prob, c.route_scale, hdr_out, w, c.dim, c.inter, c.swiglu_limit);
   return hipGetLastError();
 }
 
@@ -341,8 +341,8 @@ hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w
     if (e != hipSuccess) return e;
     attr_set[ai] = true;
   }
-  hipLaunchKernelGGL(kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, c.topk, w2,
-                     out_f32, out_bf16);
+  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, c.topk, w2,
+             out_f32, out_bf16);
   return hipGetLastError();
 }
 
@@ -350,7 +350,6 @@ hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w
 
 hipError_t launch_gateup_m1(int mode, const moe_experts& ex, const float* bias, const int32_t* hdr_in,
                             int32_t* hdr_out, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  timed_begin(MOE_K_GATEUP, s);
   hipError_t err;
   switch (c.dim / 256) {
     case 1: err = launch_gateup_m1_t<1>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
@@ -361,13 +360,11 @@ hipError_t launch_gateup_m1(int mode, const moe_experts& ex, const float* bias, 
     case 32: err = launch_gateup_m1_t<32>(mode, ex, bias, hdr_in, hdr_out, c, w, s); break;
     default: err = hipErrorInvalidValue; break;
   }
-  timed_end(MOE_K_GATEUP, s);
   return err;
 }
 
 hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
                           uint16_t* out_bf16, hipStream_t s) {
-  timed_begin(MOE_K_DOWN, s);
   hipError_t err;
   switch (c.inter / 256) {
     case 1: err = launch_down_m1_t<1>(ex, c, w, w2, out_f32, out_bf16, s); break;
@@ -377,7 +374,6 @@ hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, 
     case 16: err = launch_down_m1_t<16>(ex, c, w, w2, out_f32, out_bf16, s); break;
     default: err = hipErrorInvalidValue; break;
   }
-  timed_end(MOE_K_DOWN, s);
   return err;
 }
 

@@ -245,8 +245,8 @@ hipError_t launch_gateup_t(const moe_experts& ex, int max_u, const moe_cfg& c, c
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(max_u * (c.inter / 32)), dim3(256), shm, s, ex, w.plan, w.xq, w.xd, w.xs, c.dim,
-                     c.inter, w.g, w.u, w.h, w.hq, w.hd, w.hs, c.swiglu_limit);
+  MOE_LAUNCH(MOE_K_GATEUP, kern, dim3(max_u * (c.inter / 32)), dim3(256), shm, s, ex, w.plan, w.xq, w.xd, w.xs, c.dim,
+             c.inter, w.g, w.u, w.h, w.hq, w.hd, w.hs, c.swiglu_limit);
   return hipGetLastError();
 }
 
@@ -264,8 +264,8 @@ hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg&
   }
   const int routed_blocks = max_u * (c.dim / 32);
   const int shared_blocks = w2 ? (c.dim + 3) / 4 : 0;
-  hipLaunchKernelGGL(kern, dim3(routed_blocks + shared_blocks), dim3(256), shm, s, ex, w.plan, w.hq, w.hd, w.hs,
-                     c.dim, c.inter, w.y, routed_blocks, m, w2, w.sh, w.sd);
+  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(routed_blocks + shared_blocks), dim3(256), shm, s, ex, w.plan, w.hq, w.hd, w.hs,
+             c.dim, c.inter, w.y, routed_blocks, m, w2, w.sh, w.sd);
   return hipGetLastError();
 }
 
@@ -273,7 +273,6 @@ hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg&
 
 hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
   const int max_u = min(c.n_routed, m * c.topk);
-  timed_begin(MOE_K_GATEUP, s);
   hipError_t err;
   switch (c.dim / 256) {
     case 1: err = launch_gateup_t<1>(ex, max_u, c, w, s); break;
@@ -284,14 +283,12 @@ hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const W
     case 32: err = launch_gateup_t<32>(ex, max_u, c, w, s); break;
     default: err = hipErrorInvalidValue; break;
   }
-  timed_end(MOE_K_GATEUP, s);
   return err;
 }
 
 hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
                        hipStream_t s) {
   const int max_u = min(c.n_routed, m * c.topk);
-  timed_begin(MOE_K_DOWN, s);
   hipError_t err;
   switch (c.inter / 256) {
     case 1: err = launch_down_t<1>(ex, m, max_u, c, w, w2, s); break;
@@ -302,7 +299,6 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
     case 32: err = launch_down_t<32>(ex, m, max_u, c, w, w2, s); break;
     default: err = hipErrorInvalidValue; break;
   }
-  timed_end(MOE_K_DOWN, s);
   return err;
 }
 

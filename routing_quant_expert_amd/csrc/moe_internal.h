@@ -2,6 +2,7 @@
 // workspace layout, plan tables and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -86,8 +87,19 @@ hipError_t launch_gateup_m1(int mode, const moe_experts& ex, const float* bias, 
 hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
                           uint16_t* out_bf16, hipStream_t s);
 
-// Timing hook (moe_time_next_launch): brackets the next launch of `which`.
-void timed_begin(int which, hipStream_t s);
-void timed_end(int which, hipStream_t s);
+// Timing hook (moe_time_next_launch): the event pair set for kernel `which`,
+// taken (and cleared) by its next launch, which then goes through
+// hipExtLaunchKernelGGL so that the events hold the dispatch's own start and
+// end times.
+bool take_timed(int which, hipEvent_t* begin, hipEvent_t* end);
+
+#define MOE_LAUNCH(which, kern, grid, block, shm, stream, ...)                                          \
+  do {                                                                                                \
+    hipEvent_t moe_eb_, moe_ee_;                                                                      \
+    if (take_timed(which, &moe_eb_, &moe_ee_))                                                        \
+      hipExtLaunchKernelGGL(kern, grid, block, shm, stream, moe_eb_, moe_ee_, 0, __VA_ARGS__);        \
+    else                                                                                              \
+      hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                                \
+  } while (0)
 
 }  // namespace moe

@@ -390,11 +390,8 @@ hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const 
   a.router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
   a.shared_blocks = w1 ? (c.inter + 3) / 4 : 0;
   const int quant_blocks = (int)((int64_t)m * c.dim / 256);
-  timed_begin(MOE_K_ROUTER, s);
-  hipLaunchKernelGGL(k_front, dim3(a.router_blocks + a.shared_blocks + quant_blocks), dim3(256), 0, s, a, w);
-  hipError_t err = hipGetLastError();
-  timed_end(MOE_K_ROUTER, s);
-  return err;
+  MOE_LAUNCH(MOE_K_ROUTER, k_front, dim3(a.router_blocks + a.shared_blocks + quant_blocks), dim3(256), 0, s, a, w);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, bool with_plan,
