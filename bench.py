@@ -1,6 +1,6 @@
 #!/usr/bin/env python3
 """Benchmark: MoE-layer decode tokens/s at m=1 on one MI355X, and the HBM
-roofline fraction of the routed-expert GEMV on expert-weight bytes.
+roofline fraction of the layer kernel on its weight bytes.
 
 Workload: one DeepSeek-V4.1-Flash-style MoE layer, dim 4096, inter 2048,
 384 routed experts (Q2_K gate/up, Q3_K down, all resident: 3.5 GB), top-6,
@@ -9,8 +9,12 @@ whole layer forward (route, select, routed experts, shared expert, combine)
 for one token; steps cycle through `--tokens` distinct input rows so that
 consecutive tokens pick mostly different experts (the 256 MB last-level
 cache cannot hold a token's 54.7 MB of expert blocks from one step to the
-next). The routed gate/up kernel (the dominant one) is timed per launch with
-HIP events on its own stream inside the timed region.
+next). At m = 1 the whole layer is one kernel (k_layer1); a sample of its
+launches is timed with HIP events recorded by the dispatch itself, inside
+the timed region.
+
+--m 2..8 runs the multi-token path instead (correlated token rows, the
+union of their picks read once); its gate/up kernel is the one timed.
 """
 import argparse
 import ctypes
@@ -23,11 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("moe_decode1.hip", "moe_kquant.h", "moe_select.h", "moe_math.h", "moe_internal.h")
+KERNEL_SOURCES = ("moe_layer1.hip", "moe_front.h", "moe_kquant.h", "moe_select.h", "moe_math.h", "moe_internal.h")
 
 
 def kernel_source_sha() -> str:
-    """Hash of the sources of the single-token kernels (ties measured counters to a kernel version)."""
+    """Hash of the sources of the single-token kernel (ties measured counters to a kernel version)."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -118,7 +122,9 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's expert kernels")
+    ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's timed kernel")
+    ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernel; 2..8: the "
+                                                     "multi-token path on correlated rows)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -136,6 +142,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
               f"of the layer is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
+    if not 1 <= args.m <= 8:
+        print("bench.py: --m must be 1..8", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -147,54 +156,80 @@ def main():
     torch.cuda.set_device(0)
     spec = synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed)
     s = spec.shape
+    m = args.m
     print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts) on the device",
           file=sys.stderr, flush=True)
     dl = DeviceLayer(spec)
-    xs = torch.from_numpy(synth.tokens(spec, 0, args.tokens)).cuda()
-    ws = torch.empty(R.workspace_bytes(dl.cfg, 1), dtype=torch.uint8, device="cuda")
-    out = torch.empty((1, s.dim), dtype=torch.uint16, device="cuda")
+    if m == 1:
+        xs = torch.from_numpy(synth.tokens(spec, 0, args.tokens)).cuda()
+    else:
+        groups = [synth.correlated_tokens(spec, m, group=g) for g in range(args.tokens)]
+        xs = torch.from_numpy(np.concatenate(groups)).cuda()
+    ws = torch.empty(R.workspace_bytes(dl.cfg, m), dtype=torch.uint8, device="cuda")
+    R.workspace_init(dl.cfg, m, ws)
+    out = torch.empty((m, s.dim), dtype=torch.uint16, device="cuda")
+    hw = R.header_words(dl.cfg)
+    hdrs = torch.empty((args.steps, m, hw), dtype=torch.int32, device="cuda")
+    hdr_w = torch.empty((m, hw), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
-    def step(i):
-        t = i % args.tokens
-        R.layer_forward(dl.cfg, dl.layer, xs[t:t + 1], out, ws)
+    def step(i, hdr):
+        t = (i % args.tokens) * m
+        R.layer_forward(dl.cfg, dl.layer, xs[t:t + m], out, ws, header=hdr)
 
     for i in range(args.warmup):
-        step(i)
+        step(i, hdr_w)
     torch.cuda.synchronize()
 
     ev = HipEvents()
     K = args.steps
     every = max(1, args.time_every)
     nt = (K + every - 1) // every
-    gu = ev.create(2 * nt)
-    dn = ev.create(2 * nt)
+    evs = ev.create(2 * nt)
+    which = R.MOE_K_LAYER if m == 1 else R.MOE_K_GATEUP
     L = R.lib()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if i % every == 0:          # a sample of the steps brackets its expert kernels with events
+        if i % every == 0:          # a sample of the steps brackets the timed kernel with events
             j = i // every
-            L.moe_time_next_launch(R.MOE_K_GATEUP, gu[2 * j], gu[2 * j + 1])
-            L.moe_time_next_launch(R.MOE_K_DOWN, dn[2 * j], dn[2 * j + 1])
-        step(args.warmup + i)
+            L.moe_time_next_launch(which, evs[2 * j], evs[2 * j + 1])
+        step(args.warmup + i, hdrs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gu_ms = np.array([ev.elapsed_ms(gu[2 * j], gu[2 * j + 1]) for j in range(nt)])
-    dn_ms = np.array([ev.elapsed_ms(dn[2 * j], dn[2 * j + 1]) for j in range(nt)])
-    ev.destroy(gu + dn)
+    k_ms = np.array([ev.elapsed_ms(evs[2 * j], evs[2 * j + 1]) for j in range(nt)])
+    ev.destroy(evs)
+    status = R.workspace_layout(dl.cfg, m)
+    st = int(ws[status["status"]:status["status"] + 4].view(torch.int32).item())
+    if st & R.MOE_STATUS_TIMEOUT:
+        print("bench: the device reported a timed-out wait; results invalid", file=sys.stderr)
+        sys.exit(3)
 
     wall = t1 - t0
     ms_per_step = wall * 1e3 / K
-    gu_bytes = s.topk * 2 * s.gate_bytes          # 6 experts x (gate + up) Q2_K blocks
-    dn_bytes = s.topk * s.down_bytes              # 6 experts x down Q3_K blocks
-    gu_avg = float(gu_ms.mean()) * 1e-3
-    dn_avg = float(dn_ms.mean()) * 1e-3
-    achieved = gu_bytes / gu_avg / 1e9
-    routed_gbs = (gu_bytes + dn_bytes) / (gu_avg + dn_avg) / 1e9
+    k_avg = float(k_ms.mean()) * 1e-3
+    router_bytes = s.n_routed * s.dim * 2
+    shared_bytes = 3 * s.inter * s.dim * 2
+    expert_bytes = 2 * s.gate_bytes + s.down_bytes
+    if m == 1:
+        kernel = "k_layer1"
+        launch_bytes = router_bytes + shared_bytes + s.topk * expert_bytes
+        extra = {"layer_bytes": {"router": router_bytes, "shared": shared_bytes, "routed": s.topk * expert_bytes}}
+        workload = "moe_layer_decode_m1_dim4096_inter2048_e384_top6"
+    else:
+        picks = hdrs[:, :, 1:1 + s.topk].cpu().numpy()
+        n_u = np.array([len(np.unique(p)) for p in picks[::every]])   # the timed steps' unions
+        kernel = "k_gateup"
+        launch_bytes = float(n_u.mean()) * 2 * s.gate_bytes
+        step_bytes = [len(np.unique(p)) * expert_bytes + router_bytes + shared_bytes for p in picks]
+        extra = {"union_experts_mean": float(n_u.mean()),
+                 "step_weight_bytes_mean": float(np.mean(step_bytes)),
+                 "step_achieved_gbs": float(np.mean(step_bytes)) / (wall / K) / 1e9}
+        workload = f"moe_layer_decode_m{m}_correlated_dim4096_inter2048_e384_top6"
+    achieved = launch_bytes / k_avg / 1e9
     res = {
         "metric": "MoE-layer decode tokens/s at m=1 and % of HBM peak on expert-weight bytes",
-        "value": K / wall,
+        "value": K * m / wall,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -205,18 +240,18 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": "moe_layer_decode_m1_dim4096_inter2048_e384_top6", "dim": s.dim, "inter": s.inter,
-                   "n_routed": s.n_routed, "topk": s.topk, "m": 1, "tokens_cycled": args.tokens,
+        "config": {"workload": workload, "dim": s.dim, "inter": s.inter,
+                   "n_routed": s.n_routed, "topk": s.topk, "m": m, "tokens_cycled": args.tokens,
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("k_gateup_m1"), "kernel": "k_gateup_m1",
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": gu_avg * 1e6, "timed_launches": int(nt)},
-        "routed_gemvs": {"gateup_us": gu_avg * 1e6, "down_us": dn_avg * 1e6, "bytes": gu_bytes + dn_bytes,
-                         "achieved_gbs": routed_gbs, "frac": routed_gbs / HBM_PEAK_GBS,
-                         "gateup_p10_p90_us": [float(np.percentile(gu_ms, 10) * 1e3),
-                                               float(np.percentile(gu_ms, 90) * 1e3)]},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(kernel) if m == 1 else None, "kernel": kernel,
+                     "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
+                     "launch_p10_p90_us": [float(np.percentile(k_ms, 10) * 1e3),
+                                           float(np.percentile(k_ms, 90) * 1e3)]},
+        "detail": extra,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and m == 1:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
     print(json.dumps(res), flush=True)

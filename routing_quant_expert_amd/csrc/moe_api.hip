@@ -13,8 +13,16 @@ namespace moe {
 namespace {
 
 thread_local std::string g_err;
-thread_local hipEvent_t g_ev_begin[4] = {nullptr, nullptr, nullptr, nullptr};
-thread_local hipEvent_t g_ev_end[4] = {nullptr, nullptr, nullptr, nullptr};
+constexpr int kTimedKernels = 5;   // MOE_K_* ids 1..4
+thread_local hipEvent_t g_ev_begin[kTimedKernels] = {};
+thread_local hipEvent_t g_ev_end[kTimedKernels] = {};
+constexpr uint32_t kDefaultSpin = 1u << 20;
+uint32_t g_spin_limit = kDefaultSpin;
+
+__global__ void k_zero16(uint4* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0, 0, 0, 0);
+}
 
 int fail(int code, const char* fmt, const char* a = "", long long b = 0) {
   char buf[512];
@@ -90,6 +98,7 @@ bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
   L->sd = take(t, m * c.dim * 4);
   L->yr = take(t, m * c.dim * 4);
   L->status = take(t, 16 + m * (1 + 3 * c.topk) * 4);   // status words, then a header scratch
+  L->ctl = take(t, 256);
   L->total = t;
   L->max_pairs = (int32_t)P;
   return true;
@@ -117,11 +126,21 @@ Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m) {
   w.sd = reinterpret_cast<float*>(b + L.sd);
   w.yr = reinterpret_cast<float*>(b + L.yr);
   w.status = reinterpret_cast<int32_t*>(b + L.status);
+  w.ctl = reinterpret_cast<Ctl*>(b + L.ctl);
   return w;
 }
 
+uint32_t spin_limit() { return g_spin_limit; }
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, static_cast<uint4*>(p), n);
+  return hipGetLastError();
+}
+
 bool take_timed(int which, hipEvent_t* begin, hipEvent_t* end) {
-  if (which < 1 || which > 3 || !g_ev_begin[which] || !g_ev_end[which]) return false;
+  if (which < 1 || which >= kTimedKernels || !g_ev_begin[which] || !g_ev_end[which]) return false;
   *begin = g_ev_begin[which];
   *end = g_ev_end[which];
   g_ev_begin[which] = g_ev_end[which] = nullptr;
@@ -141,6 +160,15 @@ size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m) {
   moe_ws_layout L;
   layout_of(*cfg, max_m, &L);
   return L.total;
+}
+
+int moe_workspace_init(const moe_cfg* cfg, int32_t max_m, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (max_m < 1) return fail(MOE_EINVAL, "max_m must be >= 1%s (max_m %lld)", "", max_m);
+  moe_ws_layout L;
+  if (int r = check_ws(*cfg, max_m, ws, ws_bytes, &L)) return r;
+  hipError_t e = launch_zero(static_cast<uint8_t*>(ws) + L.ctl, 256, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "workspace_init");
 }
 
 int moe_workspace_layout(const moe_cfg* cfg, int32_t max_m, moe_ws_layout* out) {
@@ -179,14 +207,13 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   Ws w = ws_view(ws, L, *cfg, m);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
-  if (m == 1) {
-    if ((e = launch_gateup_m1(1, *experts, nullptr, header, nullptr, *cfg, w, s)) != hipSuccess)
-      return hip_fail(e, "gateup_m1");
-    if ((e = launch_down_m1(*experts, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess)
-      return hip_fail(e, "down_m1");
+  if (m == 1 && layer1_supported(*cfg)) {
+    if ((e = launch_layer1(1, *cfg, x, nullptr, *experts, header, nullptr, y_routed, nullptr, nullptr, w, s)) !=
+        hipSuccess)
+      return hip_fail(e, "layer1");
     return MOE_OK;
   }
+  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
   if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
   if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(*experts, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
@@ -209,15 +236,14 @@ int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t
   int32_t* hdr = header ? header : w.status + 4;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_front(x, m, layer->gate_w, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
-    return hip_fail(e, "front");
-  if (m == 1) {
-    if ((e = launch_gateup_m1(0, layer->experts, layer->bias, nullptr, hdr, *cfg, w, s)) != hipSuccess)
-      return hip_fail(e, "gateup_m1");
-    if ((e = launch_down_m1(layer->experts, *cfg, w, layer->sh_w2, out_f32, out_bf16, s)) != hipSuccess)
-      return hip_fail(e, "down_m1");
+  if (m == 1 && layer1_supported(*cfg)) {
+    if ((e = launch_layer1(0, *cfg, x, layer, layer->experts, nullptr, hdr, out_f32, out_bf16, nullptr, w, s)) !=
+        hipSuccess)
+      return hip_fail(e, "layer1");
     return MOE_OK;
   }
+  if ((e = launch_front(x, m, layer->gate_w, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
+    return hip_fail(e, "front");
   if ((e = launch_select(layer->bias, m, *cfg, w, hdr, true, s)) != hipSuccess) return hip_fail(e, "select");
   if ((e = launch_gateup(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(layer->experts, m, *cfg, w, layer->sh_w2, s)) != hipSuccess) return hip_fail(e, "down");
@@ -243,8 +269,13 @@ int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, floa
   return MOE_OK;
 }
 
+int moe_set_wait_limit(uint32_t polls) {
+  g_spin_limit = polls ? polls : kDefaultSpin;
+  return MOE_OK;
+}
+
 int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end) {
-  if (which < 1 || which > 3) return fail(MOE_EINVAL, "unknown kernel id%s %lld", "", which);
+  if (which < 1 || which >= kTimedKernels) return fail(MOE_EINVAL, "unknown kernel id%s %lld", "", which);
   g_ev_begin[which] = (hipEvent_t)ev_begin;
   g_ev_end[which] = (hipEvent_t)ev_end;
   return MOE_OK;

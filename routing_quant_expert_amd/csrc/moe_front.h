@@ -1,0 +1,188 @@
+// Device parts of the layer's front, shared by the multi-token launches and
+// the single-token persistent kernel: q8_1 of the input rows, the router
+// GEMV rows with their scores, and the shared expert's gate/up rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+#include "moe_math.h"
+
+namespace moe {
+namespace front {
+
+__device__ inline uint16_t fp16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+__device__ inline void bf16x8(uint4 v, float (&f)[8]) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+}
+
+// ---------------------------------------------------------------------------
+// q8_1 of bf16 rows: one thread per value, a q8_1 block = 32 consecutive
+// lanes. d = amax/127, code = roundf(x/d) (half away from zero), stored scale
+// fp16(d), plus the sums of 16 consecutive codes (the q8_1 sum field is not
+// used; the GEMV epilogues need per-16 sums of the codes).
+// ---------------------------------------------------------------------------
+__device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* __restrict__ xq,
+                              uint16_t* __restrict__ xd, int32_t* __restrict__ xs) {
+  const int64_t i = (int64_t)blk * 256 + threadIdx.x;   // m*dim is a multiple of 256
+  float v = bf16_f32(x[i]);
+  float a = fabsf(v);
+  for (int s = 16; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
+  float d = (float)((double)a / 127.0);
+  int q = a == 0.0f ? 0 : q8_code(v, d);
+  xq[i] = (int8_t)q;
+  int sum = q;
+  for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+  const int lane32 = threadIdx.x & 31;
+  if (lane32 == 0) xd[i >> 5] = fp16_bits(d);
+  if ((lane32 & 15) == 0) xs[i >> 4] = sum;
+}
+
+// ---------------------------------------------------------------------------
+// Router GEMV + scores. One wave64 per expert row, all tokens of the call.
+// Lane l accumulates positions 512*i + 8*l + j (i ascending, j = 0..7) in
+// f32 (product, then add: every bf16 x bf16 product is exact), then the 64
+// partials combine as p += shfl_xor(p, s) for s = 32..1 and lane 0 holds the
+// logit. This per-row order is the same for every m, so a token's logits
+// never depend on the batch it rides in.
+// ---------------------------------------------------------------------------
+constexpr int kRouterTok = 8;
+constexpr int kLoadAhead = 8;   // 16-byte chunks per lane kept in flight by one wave
+
+__device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int dim,
+                            const uint16_t* __restrict__ gate_w, int n_routed, float temp, float* __restrict__ logits,
+                            float* __restrict__ scores, float* __restrict__ logits_out) {
+  const int e = blk * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= n_routed) return;
+  const uint16_t* wr = gate_w + (int64_t)e * dim;
+  const int nch = (dim + 511) / 512;
+  for (int t0 = 0; t0 < m; t0 += kRouterTok) {
+    const int nt = min(kRouterTok, m - t0);
+    float p[kRouterTok];
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) p[t] = 0.0f;
+    for (int c0 = 0; c0 < nch; c0 += kLoadAhead) {
+      uint4 wv[kLoadAhead];
+#pragma unroll
+      for (int c = 0; c < kLoadAhead; ++c) {
+        const int k = 512 * (c0 + c) + 8 * lane;
+        wv[c] = (c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < kRouterTok; ++t) {
+        if (t < nt) {
+          uint4 xv[kLoadAhead];
+#pragma unroll
+          for (int c = 0; c < kLoadAhead; ++c) {
+            const int k = 512 * (c0 + c) + 8 * lane;
+            xv[c] = (c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + t) * dim + k)
+                                              : make_uint4(0, 0, 0, 0);
+          }
+          float acc = p[t];
+#pragma unroll
+          for (int c = 0; c < kLoadAhead; ++c) {
+            const uint32_t ww[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+            const uint32_t xx[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const uint16_t xb = (uint16_t)(xx[j >> 1] >> (16 * (j & 1)));
+              const uint16_t wb = (uint16_t)(ww[j >> 1] >> (16 * (j & 1)));
+              acc = fadd(acc, fmul(bf16_f32(xb), bf16_f32(wb)));   // zero padding adds +0: exact
+            }
+          }
+          p[t] = acc;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kRouterTok; ++t) {
+      float v = p[t];
+      for (int s = 32; s >= 1; s >>= 1) v = fadd(v, __shfl_xor(v, s));
+      p[t] = v;
+    }
+    if (lane < nt) {
+      float lg = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kRouterTok; ++t)
+        if (t == lane) lg = p[t];
+      const int64_t o = (int64_t)(t0 + lane) * n_routed + e;
+      logits[o] = lg;
+      if (logits_out) logits_out[o] = lg;
+      scores[o] = score_of(lg, temp);
+    }
+  }
+}
+
+// Shared expert gate/up (m <= 8): one wave per hidden unit i: sg = W1s[i].x,
+// su = W3s[i].x (f32, any order), sh = bf16(swiglu(sg, su)) [moe_v41.rs,
+// module doc: the shared expert is resident bf16 on the dense GEMM/GEMV].
+__device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, int dim, int inter,
+                               const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
+                               float* __restrict__ sg, float* __restrict__ su, uint16_t* __restrict__ sh, float L) {
+  const int i = blk * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= inter) return;
+  float pg[kMaxDecodeTokens], pu[kMaxDecodeTokens];
+#pragma unroll
+  for (int t = 0; t < kMaxDecodeTokens; ++t) pg[t] = pu[t] = 0.0f;
+  const uint16_t* r1 = w1 + (int64_t)i * dim;
+  const uint16_t* r3 = w3 + (int64_t)i * dim;
+  const int nch = (dim + 511) / 512;
+  for (int c0 = 0; c0 < nch; c0 += kLoadAhead) {
+    uint4 av[kLoadAhead], bv[kLoadAhead];
+#pragma unroll
+    for (int c = 0; c < kLoadAhead; ++c) {
+      const int k = 512 * (c0 + c) + 8 * lane;
+      const bool in = c0 + c < nch && k < dim;
+      av[c] = in ? load_nt16(r1 + k) : make_uint4(0, 0, 0, 0);
+      bv[c] = in ? load_nt16(r3 + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t) {
+      if (t < m) {
+#pragma unroll
+        for (int c = 0; c < kLoadAhead; ++c) {
+          const int k = 512 * (c0 + c) + 8 * lane;
+          if (c0 + c < nch && k < dim) {
+            float a[8], b[8], xv[8];
+            bf16x8(av[c], a);
+            bf16x8(bv[c], b);
+            bf16x8(*reinterpret_cast<const uint4*>(x + (int64_t)t * dim + k), xv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              pg[t] = __builtin_fmaf(a[j], xv[j], pg[t]);
+              pu[t] = __builtin_fmaf(b[j], xv[j], pu[t]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMaxDecodeTokens; ++t) {
+    for (int s = 32; s >= 1; s >>= 1) {
+      pg[t] += __shfl_xor(pg[t], s);
+      pu[t] += __shfl_xor(pu[t], s);
+    }
+  }
+  if (lane < m) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t)
+      if (t == lane) {
+        g = pg[t];
+        u = pu[t];
+      }
+    const int64_t o = (int64_t)lane * inter + i;
+    sg[o] = g;
+    su[o] = u;
+    sh[o] = bf16_rne(swiglu(g, u, L));
+  }
+}
+
+}  // namespace front
+}  // namespace moe

@@ -37,6 +37,19 @@ struct PlanView {
   static int words(int max_pairs, int max_m, int topk) { return 2 + 6 * max_pairs + max_m * topk; }
 };
 
+// Control words of the single-token persistent kernel (workspace region
+// `ctl`): zero between calls.
+struct Ctl {
+  uint32_t ticket;       // next work item
+  uint32_t exited;       // workgroups that ran out of work
+  uint32_t r_done;       // router items finished
+  uint32_t s_done;       // shared gate/up items finished
+  uint32_t g_done;       // routed gate/up items finished
+  uint32_t plan_ready;   // 1 once the plan, header and status are written
+  uint32_t fault;        // a bounded wait ran out
+  uint32_t pad;
+};
+
 // Device-side view of the workspace for one call.
 struct Ws {
   int8_t* xq;
@@ -58,6 +71,7 @@ struct Ws {
   float* sd;
   float* yr;
   int32_t* status;
+  Ctl* ctl;
 };
 
 bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L);
@@ -79,13 +93,16 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
 hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
-// single token: gate/up with the plan derived in every workgroup (mode 0: the
-// selection from the workspace scores; mode 1: the caller's header), then the
-// down rows of every pick + the shared expert's down rows + the combine.
-hipError_t launch_gateup_m1(int mode, const moe_experts& ex, const float* bias, const int32_t* hdr_in,
-                            int32_t* hdr_out, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s);
+// Single token, the whole layer (mode 0: routing here, `layer` given) or the
+// routed experts for a caller's header (mode 1) in one persistent launch.
+bool layer1_supported(const moe_cfg& c);
+hipError_t launch_layer1(int mode, const moe_cfg& c, const uint16_t* x, const moe_layer* layer,
+                         const moe_experts& ex, const int32_t* hdr_in, int32_t* hdr_out, float* out_f32,
+                         uint16_t* out_bf16, uint16_t* x_next, const Ws& w, hipStream_t s);
+// Polls a bounded wait makes before it gives up (moe_set_wait_limit).
+uint32_t spin_limit();
+// Zero-fill of `bytes` bytes (a multiple of 16) with a kernel (no memset node).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // Timing hook (moe_time_next_launch): the event pair set for kernel `which`,
 // taken (and cleared) by its next launch, which then goes through

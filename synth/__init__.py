@@ -341,15 +341,16 @@ def tokens(spec: LayerSpec, t0: int, m: int) -> np.ndarray:
     return out
 
 
-def correlated_tokens(spec: LayerSpec, m: int, weight: float = 0.5) -> np.ndarray:
-    """x_t = bf16(w*c + sqrt(1-w^2)*z_t): rows sharing one N(0,1) component c."""
+def correlated_tokens(spec: LayerSpec, m: int, weight: float = 0.5, group: int = 0) -> np.ndarray:
+    """x_t = bf16(w*c + sqrt(1-w^2)*z_t): rows sharing one N(0,1) component c.
+    Group g uses its own c and the z of rows g*m .. g*m+m-1."""
     d = spec.shape.dim
-    c = normal_f64(spec.seed, make_tag(K_X_COMMON, spec.layer, 0), 0, d)
+    c = normal_f64(spec.seed, make_tag(K_X_COMMON, spec.layer, group), 0, d)
     a = np.float64(weight)
     b = np.sqrt(np.float64(1.0) - a * a)
     out = np.empty((m, d), dtype=np.uint16)
     for i in range(m):
-        z = normal_f64(spec.seed, make_tag(K_X, spec.layer, i), 0, d)
+        z = normal_f64(spec.seed, make_tag(K_X, spec.layer, group * m + i), 0, d)
         v = (a * c + b * z).astype(np.float32)
         out[i] = f32_to_bf16_bits(v)
     return out

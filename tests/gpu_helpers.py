@@ -22,7 +22,9 @@ def workspace(cfg, m):
     assert n > 0
     ws = torch.empty(n + 256, dtype=torch.uint8, device="cuda")
     off = (-ws.data_ptr()) % 256
-    return ws[off:off + n]
+    ws = ws[off:off + n]
+    R.workspace_init(cfg, m, ws)
+    return ws
 
 
 def ws_array(ws, layout: dict, name: str, dtype, count: int) -> np.ndarray:
