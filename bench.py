@@ -9,9 +9,10 @@ whole layer forward (route, select, routed experts, shared expert, combine)
 for one token; steps cycle through `--tokens` distinct input rows so that
 consecutive tokens pick mostly different experts (the 256 MB last-level
 cache cannot hold a token's 54.7 MB of expert blocks from one step to the
-next). At m = 1 the whole layer is one kernel (k_layer1); a sample of its
-launches is timed with HIP events recorded by the dispatch itself, inside
-the timed region.
+next). A sample of the steps has its three kernels (front, routed gate/up,
+routed + shared down with the combine) timed with HIP events recorded by the
+dispatches themselves, inside the timed region; the roofline line is the
+routed gate/up kernel's.
 
 --m 2..8 runs the multi-token path instead (correlated token rows, the
 union of their picks read once); its gate/up kernel is the one timed.
@@ -27,11 +28,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("moe_layer1.hip", "moe_front.h", "moe_kquant.h", "moe_select.h", "moe_math.h", "moe_internal.h")
+KERNEL_SOURCES = ("moe_decode1.hip", "moe_kquant.h", "moe_math.h", "moe_internal.h")
 
 
 def kernel_source_sha() -> str:
-    """Hash of the sources of the single-token kernel (ties measured counters to a kernel version)."""
+    """Hash of the sources of the single-token expert kernels (ties measured counters to a kernel version)."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -185,47 +186,58 @@ def main():
     K = args.steps
     every = max(1, args.time_every)
     nt = (K + every - 1) // every
-    evs = ev.create(2 * nt)
-    which = R.MOE_K_LAYER if m == 1 else R.MOE_K_GATEUP
+    kinds = (("front", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("down", R.MOE_K_DOWN))
+    evs = {k: ev.create(2 * nt) for k, _ in kinds}
     L = R.lib()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if i % every == 0:          # a sample of the steps brackets the timed kernel with events
+        if i % every == 0:          # a sample of the steps brackets its kernels with events
             j = i // every
-            L.moe_time_next_launch(which, evs[2 * j], evs[2 * j + 1])
+            for k, which in kinds:
+                L.moe_time_next_launch(which, evs[k][2 * j], evs[k][2 * j + 1])
         step(args.warmup + i, hdrs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k_ms = np.array([ev.elapsed_ms(evs[2 * j], evs[2 * j + 1]) for j in range(nt)])
-    ev.destroy(evs)
-    status = R.workspace_layout(dl.cfg, m)
-    st = int(ws[status["status"]:status["status"] + 4].view(torch.int32).item())
-    if st & R.MOE_STATUS_TIMEOUT:
-        print("bench: the device reported a timed-out wait; results invalid", file=sys.stderr)
-        sys.exit(3)
+    k_ms = {k: np.array([ev.elapsed_ms(evs[k][2 * j], evs[k][2 * j + 1]) for j in range(nt)]) for k, _ in kinds}
+    for k, _ in kinds:
+        ev.destroy(evs[k])
 
     wall = t1 - t0
     ms_per_step = wall * 1e3 / K
-    k_avg = float(k_ms.mean()) * 1e-3
     router_bytes = s.n_routed * s.dim * 2
-    shared_bytes = 3 * s.inter * s.dim * 2
+    shared_gu_bytes = 2 * s.inter * s.dim * 2
+    shared_down_bytes = s.inter * s.dim * 2
     expert_bytes = 2 * s.gate_bytes + s.down_bytes
+    us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
     if m == 1:
-        kernel = "k_layer1"
-        launch_bytes = router_bytes + shared_bytes + s.topk * expert_bytes
-        extra = {"layer_bytes": {"router": router_bytes, "shared": shared_bytes, "routed": s.topk * expert_bytes}}
+        kernel = "k_gateup_m1"
+        n_u = np.full(1, s.topk)
         workload = "moe_layer_decode_m1_dim4096_inter2048_e384_top6"
     else:
         picks = hdrs[:, :, 1:1 + s.topk].cpu().numpy()
         n_u = np.array([len(np.unique(p)) for p in picks[::every]])   # the timed steps' unions
         kernel = "k_gateup"
-        launch_bytes = float(n_u.mean()) * 2 * s.gate_bytes
-        step_bytes = [len(np.unique(p)) * expert_bytes + router_bytes + shared_bytes for p in picks]
-        extra = {"union_experts_mean": float(n_u.mean()),
-                 "step_weight_bytes_mean": float(np.mean(step_bytes)),
-                 "step_achieved_gbs": float(np.mean(step_bytes)) / (wall / K) / 1e9}
         workload = f"moe_layer_decode_m{m}_correlated_dim4096_inter2048_e384_top6"
+    if m == 1:   # the single-token launches: router | selection, routed + shared gate/up | down + combine
+        kbytes = {"front": router_bytes,
+                  "gateup": s.topk * 2 * s.gate_bytes + shared_gu_bytes,
+                  "down": s.topk * s.down_bytes + shared_down_bytes}
+    else:
+        kbytes = {"front": router_bytes + shared_gu_bytes,
+                  "gateup": float(n_u.mean()) * 2 * s.gate_bytes,
+                  "down": float(n_u.mean()) * s.down_bytes + shared_down_bytes}
+    launch_bytes = kbytes["gateup"]
+    k_avg = us["gateup"] * 1e-6
+    routed_bytes = float(n_u.mean()) * expert_bytes
+    extra = {"kernels": {k: {"avg_us": us[k], "weight_bytes": kbytes[k], "gbs": kbytes[k] / us[k] / 1e3}
+                         for k, _ in kinds},
+             "layer_weight_bytes": sum(kbytes.values()),
+             "layer_kernels_us": sum(us.values()),
+             "layer_kernels_gbs": sum(kbytes.values()) / sum(us.values()) / 1e3,
+             "expert_kernels_gbs": (kbytes["gateup"] + kbytes["down"]) / (us["gateup"] + us["down"]) / 1e3}
+    if m > 1:
+        extra["union_experts_mean"] = float(n_u.mean())
     achieved = launch_bytes / k_avg / 1e9
     res = {
         "metric": "MoE-layer decode tokens/s at m=1 and % of HBM peak on expert-weight bytes",
@@ -247,8 +259,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(kernel) if m == 1 else None, "kernel": kernel,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
-                     "launch_p10_p90_us": [float(np.percentile(k_ms, 10) * 1e3),
-                                           float(np.percentile(k_ms, 90) * 1e3)]},
+                     "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
+                                           float(np.percentile(k_ms["gateup"], 90) * 1e3)]},
         "detail": extra,
     }
     if not args.no_cpu and m == 1:

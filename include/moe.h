@@ -27,9 +27,9 @@
  *   - Return value: MOE_OK (0) or a negative MOE_E* code; moe_last_error()
  *     gives a thread-local message for the last failing call.
  *   - Supported shapes: n_routed <= 1024, 1 <= topk <= 8, dim and inter
- *     multiples of 256 with dim/256 and inter/256 powers of two <= 64 (the
- *     K-quant kernels give each 256-weight super-block of a row to one lane),
- *     dim a multiple of 512 is not required. Anything else: MOE_EUNSUPPORTED.
+ *     multiples of 256 with dim/256 and inter/256 powers of two <= 16 (the
+ *     K-quant kernels give each 256-weight super-block of a row to one lane
+ *     and stage whole row tiles in LDS). Anything else: MOE_EUNSUPPORTED.
  *   - Calls that share one workspace on one stream run in order; calls that
  *     overlap on different streams must use different workspaces.
  */
@@ -53,9 +53,6 @@ extern "C" {
 #define MOE_STATUS_MISS 1        /* an expert was not resident (never set: all experts resident) */
 #define MOE_STATUS_NAN_KEY 2     /* a ranking key score+bias was NaN (the pages' "finite scores") */
 #define MOE_STATUS_BAD_PICK 4    /* moe_experts_decode: a pick outside [0,n_routed) or repeated    */
-#define MOE_STATUS_TIMEOUT 8     /* workspace status only: a bounded wait of the single-token
-                                    kernel gave up (workspace not initialised, or a wait limit
-                                    set too low); the outputs of that call are not valid       */
 
 /* Layer configuration [moe_v41.rs, struct MoeV41Cfg]. max_tokens is not a
  * field: the workspace is sized per call through moe_workspace_bytes. */
@@ -109,9 +106,10 @@ int32_t moe_header_words(const moe_cfg* cfg);
 /* Bytes of workspace the calls below need for up to max_m tokens (>= 1).
  * Returns 0 for an invalid or unsupported cfg. The workspace must be
  * 256-byte aligned device memory. Its control region (the `ctl` offset of
- * moe_workspace_layout, 256 bytes) must be zero before the first call:
- * moe_workspace_init does that, and every call leaves it zero again. The
- * rest needs no initialisation. */
+ * moe_workspace_layout, 256 bytes: the counter through which the last
+ * router workgroup of moe_layer_forward learns that it is last) must be zero
+ * before the first call: moe_workspace_init does that, and every call leaves
+ * it zero again. The rest needs no initialisation. */
 size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m);
 
 /* Zero the workspace's control region (asynchronous, on `stream`, with a
@@ -144,7 +142,7 @@ typedef struct moe_ws_layout {
   uint64_t sd;       /* f32   [max_m][dim]        shared down                      */
   uint64_t yr;       /* f32   [max_m][dim]        routed sum (layer forward)       */
   uint64_t status;   /* int32 [4] device status words (word 0: OR of MOE_STATUS_*) */
-  uint64_t ctl;      /* 256 B control words of the single-token kernel (zero between calls) */
+  uint64_t ctl;      /* 256 B control words (zero between calls)                   */
   int32_t max_pairs; /* max_m * topk                                              */
   int32_t plan_words;
 } moe_ws_layout;
@@ -206,22 +204,17 @@ int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, floa
  * calling thread records the two events (hipEvent_t, created by the caller)
  * at its dispatch's start and end (hipExtLaunchKernelGGL), on the stream it
  * is launched on. One-shot; pass NULL events to clear. For measurement only.
- *   MOE_K_GATEUP  the routed gate/up (Q2_K) kernel of the multi-token path
- *   MOE_K_DOWN    the routed down (Q3_K) kernel of the multi-token path
- *   MOE_K_ROUTER  the front kernel (q8_1 of x, router, shared gate/up)
- *   MOE_K_LAYER   the single-token persistent kernel (the whole layer at m = 1) */
+ *   MOE_K_GATEUP  the routed gate/up (Q2_K) kernel (at m = 1 with the
+ *                 selection and the shared expert's gate/up rows)
+ *   MOE_K_DOWN    the routed down (Q3_K) kernel (with the shared down rows
+ *                 and the combine at m = 1)
+ *   MOE_K_ROUTER  the front kernel (q8_1 of x and the router; for m > 1 also
+ *                 the selection, the plan and the shared gate/up) */
 #define MOE_K_GATEUP 1
 #define MOE_K_DOWN 2
 #define MOE_K_ROUTER 3
-#define MOE_K_LAYER 4
 int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end);
 
-/* Polls a bounded device-side wait of the single-token kernel makes before
- * it gives up and sets MOE_STATUS_TIMEOUT (default 1 << 20, about a second).
- * A wait that gives up lets its kernel run to the end with invalid results
- * instead of hanging. 0 restores the default. Process-wide; for testing the
- * time-out path. */
-int moe_set_wait_limit(uint32_t polls);
 
 const char* moe_last_error(void);
 

@@ -15,8 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_STATUS_MISS = 1
 MOE_STATUS_NAN_KEY = 2
 MOE_STATUS_BAD_PICK = 4
-MOE_STATUS_TIMEOUT = 8
-MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER, MOE_K_LAYER = 1, 2, 3, 4
+MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER = 1, 2, 3
 
 
 class MoeError(RuntimeError):
@@ -64,7 +63,6 @@ def lib():
         L.moe_workspace_bytes.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32]
         L.moe_workspace_layout.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32, ctypes.POINTER(WsLayout)]
         L.moe_workspace_init.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
-        L.moe_set_wait_limit.argtypes = [ctypes.c_uint32]
         L.moe_route_select.argtypes = [ctypes.POINTER(Cfg), _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
                                        ctypes.c_size_t, _VP]
         L.moe_experts_decode.argtypes = [ctypes.POINTER(Cfg), _VP, ctypes.c_int32, _VP, ctypes.POINTER(Experts),
@@ -118,10 +116,6 @@ def workspace_layout(cfg: Cfg, max_m: int) -> dict:
 def workspace_init(cfg: Cfg, max_m: int, ws, stream=None):
     _check(lib().moe_workspace_init(ctypes.byref(cfg), max_m, _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)))
-
-
-def set_wait_limit(polls: int):
-    _check(lib().moe_set_wait_limit(int(polls)))
 
 
 def route_select(cfg: Cfg, x, gate_w, bias, header, ws, logits=None, stream=None):

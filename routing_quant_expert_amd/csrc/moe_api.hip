@@ -13,11 +13,9 @@ namespace moe {
 namespace {
 
 thread_local std::string g_err;
-constexpr int kTimedKernels = 5;   // MOE_K_* ids 1..4
+constexpr int kTimedKernels = 4;   // MOE_K_* ids 1..3
 thread_local hipEvent_t g_ev_begin[kTimedKernels] = {};
 thread_local hipEvent_t g_ev_end[kTimedKernels] = {};
-constexpr uint32_t kDefaultSpin = 1u << 20;
-uint32_t g_spin_limit = kDefaultSpin;
 
 __global__ void k_zero16(uint4* p, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -31,15 +29,15 @@ int fail(int code, const char* fmt, const char* a = "", long long b = 0) {
   return code;
 }
 
-bool pow2_upto64(int v) { return v >= 1 && v <= 64 && (v & (v - 1)) == 0; }
+bool pow2_upto16(int v) { return v >= 1 && v <= 16 && (v & (v - 1)) == 0; }
 
 int check_cfg(const moe_cfg* c) {
   if (!c) return fail(MOE_EINVAL, "cfg is NULL%s%lld");
   if (!(c->gate_temp > 0.0f) || !std::isfinite(c->gate_temp) || !std::isfinite(c->route_scale) ||
       !(c->swiglu_limit > 0.0f) || (c->norm_topk_prob != 0 && c->norm_topk_prob != 1))
     return fail(MOE_EINVAL, "cfg value out of range (gate_temp > 0, finite route_scale, swiglu_limit > 0, norm 0/1)%s%lld");
-  if (c->dim % 256 || c->inter % 256 || !pow2_upto64(c->dim / 256) || !pow2_upto64(c->inter / 256))
-    return fail(MOE_EUNSUPPORTED, "dim and inter must be 256 * a power of two <= 64 %s(dim %lld)", "", c->dim);
+  if (c->dim % 256 || c->inter % 256 || !pow2_upto16(c->dim / 256) || !pow2_upto16(c->inter / 256))
+    return fail(MOE_EUNSUPPORTED, "dim and inter must be 256 * a power of two <= 16 %s(dim %lld)", "", c->dim);
   if (c->topk < 1 || c->topk > kMaxTopk || c->n_routed < c->topk || c->n_routed > kMaxRouted)
     return fail(MOE_EUNSUPPORTED, "need 1 <= topk <= 8 and topk <= n_routed <= 1024%s (n_routed %lld)", "", c->n_routed);
   return MOE_OK;
@@ -130,8 +128,6 @@ Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m) {
   return w;
 }
 
-uint32_t spin_limit() { return g_spin_limit; }
-
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;
@@ -189,9 +185,9 @@ int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uin
   Ws w = ws_view(ws, L, *cfg, m);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_front(x, m, gate_w, nullptr, nullptr, *cfg, w, logits, s)) != hipSuccess)
+  if ((e = launch_front(x, m, gate_w, nullptr, nullptr, nullptr, *cfg, w, logits, s)) != hipSuccess)
     return hip_fail(e, "front");
-  if ((e = launch_select(bias, m, *cfg, w, header, false, s)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = launch_select(bias, m, *cfg, w, header, s)) != hipSuccess) return hip_fail(e, "select");
   return MOE_OK;
 }
 
@@ -207,13 +203,14 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   Ws w = ws_view(ws, L, *cfg, m);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (m == 1 && layer1_supported(*cfg)) {
-    if ((e = launch_layer1(1, *cfg, x, nullptr, *experts, header, nullptr, y_routed, nullptr, nullptr, w, s)) !=
-        hipSuccess)
-      return hip_fail(e, "layer1");
+  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if (m == 1) {
+    if ((e = launch_gateup_m1(*experts, nullptr, header, x, nullptr, *cfg, w, s)) != hipSuccess)
+      return hip_fail(e, "gateup_m1");
+    if ((e = launch_down_m1(*experts, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "down_m1");
     return MOE_OK;
   }
-  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
   if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
   if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(*experts, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
@@ -236,15 +233,18 @@ int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t
   int32_t* hdr = header ? header : w.status + 4;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (m == 1 && layer1_supported(*cfg)) {
-    if ((e = launch_layer1(0, *cfg, x, layer, layer->experts, nullptr, hdr, out_f32, out_bf16, nullptr, w, s)) !=
-        hipSuccess)
-      return hip_fail(e, "layer1");
+  FrontSelect sel{layer->bias, hdr};
+  if (m == 1) {   // router + q8_1 of x; then the selection, the routed and the shared gate/up in one launch
+    if ((e = launch_front(x, 1, layer->gate_w, nullptr, nullptr, nullptr, *cfg, w, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "front");
+    if ((e = launch_gateup_m1(layer->experts, &sel, nullptr, x, layer, *cfg, w, s)) != hipSuccess)
+      return hip_fail(e, "gateup_m1");
+    if ((e = launch_down_m1(layer->experts, *cfg, w, layer->sh_w2, out_f32, out_bf16, s)) != hipSuccess)
+      return hip_fail(e, "down_m1");
     return MOE_OK;
   }
-  if ((e = launch_front(x, m, layer->gate_w, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
+  if ((e = launch_front(x, m, layer->gate_w, &sel, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
     return hip_fail(e, "front");
-  if ((e = launch_select(layer->bias, m, *cfg, w, hdr, true, s)) != hipSuccess) return hip_fail(e, "select");
   if ((e = launch_gateup(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(layer->experts, m, *cfg, w, layer->sh_w2, s)) != hipSuccess) return hip_fail(e, "down");
   if ((e = launch_combine(m, *cfg, w, w.sd, out_f32, out_bf16, s)) != hipSuccess) return hip_fail(e, "combine");
@@ -266,11 +266,6 @@ int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int3
 int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, float* out) {
   if (n < 0 || (n > 0 && (!g || !u || !out))) return fail(MOE_EINVAL, "bad swiglu arguments%s%lld");
   for (int64_t i = 0; i < n; ++i) out[i] = swiglu(g[i], u[i], limit);
-  return MOE_OK;
-}
-
-int moe_set_wait_limit(uint32_t polls) {
-  g_spin_limit = polls ? polls : kDefaultSpin;
   return MOE_OK;
 }
 

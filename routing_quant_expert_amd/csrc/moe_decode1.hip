@@ -1,0 +1,430 @@
+// Single-token decode (m = 1), after the front launch (router + q8_1 of x):
+//  * k_gateup_m1: the first workgroups compute the shared expert's gate/up
+//    rows (16 hidden units each, bf16 rows streamed through registers); they
+//    need no plan, so the HBM pipe is busy from the start. Every other
+//    workgroup first derives the token's plan itself (the top-k selection
+//    from the scores, or the caller's header) while its other waves stage the
+//    q8_1 activation in LDS, then runs one 32-row group of one picked
+//    expert's Q2_K gate/up rows + SwiGLU + q8_1 of h. The first of them also
+//    writes the header and the plan tables.
+//  * k_down_m1: one workgroup per 16 output rows: one wave per picked expert
+//    streams that expert's Q3_K down rows into LDS and dots them with its
+//    q8_1(h); two more waves compute the shared expert's down rows; then the
+//    combine in plan order adds them up [moe_v41.rs, Kernels: accumulate,
+//    finish; fn shared_side].
+// The arithmetic is that of the general kernels (same dot-product and
+// combine order), so the results are bit-identical to them.
+#include <hip/hip_runtime.h>
+
+#include "moe_front.h"
+#include "moe_internal.h"
+#include "moe_kquant.h"
+#include "moe_math.h"
+#include "moe_select.h"
+
+namespace moe {
+namespace {
+
+struct M1Plan {
+  int e[kMaxTopk];     // plan order (ascending id); -1 = dropped
+  float w[kMaxTopk];
+  int n_u;
+};
+
+// Wave 0 fills the block's plan (LDS) from the scores (mode 0) or from the
+// caller's header (mode 1, checked: ids in range, no repeats); the `writer`
+// workgroup also writes the header (mode 0), the plan tables and the status.
+template <int KPER>
+__device__ void plan_m1(int mode, bool writer, const float* __restrict__ scores, const float* __restrict__ bias,
+                        const int32_t* __restrict__ header_in, int n_routed, int topk, int norm, float route_scale,
+                        int32_t* __restrict__ header_out, PlanView plan, int32_t* __restrict__ status, M1Plan& P) {
+  const int lane = threadIdx.x & 63;
+  int pick = 0;
+  float wv = 0.0f;
+  bool nan_any = false, ok = true;
+  if (mode == 0) {
+    int picks[kMaxTopk];
+    float wts[kMaxTopk];
+    select_topk<KPER>(scores, bias, n_routed, topk, norm, route_scale, picks, wts, nan_any);
+#pragma unroll
+    for (int r = 0; r < kMaxTopk; ++r)
+      if (r == lane) {
+        pick = picks[r];
+        wv = wts[r];
+      }
+  } else {
+    const int li = min(lane, topk - 1);
+    pick = header_in[1 + li];
+    wv = __builtin_bit_cast(float, header_in[1 + topk + li]);
+    bool bad = lane < topk && (pick < 0 || pick >= n_routed);
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i) {
+      const int o = __builtin_amdgcn_readlane(pick, i);
+      if (i < topk && lane < topk && i < lane && o == pick) bad = true;
+    }
+    ok = !__any(bad);
+  }
+  int rank = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxTopk; ++i)
+    if (i < topk) rank += (__builtin_amdgcn_readlane(pick, i) < pick) ? 1 : 0;
+  if (lane < kMaxTopk) P.e[lane] = -1;        // a rejected header leaves every slot empty
+  if (lane < topk && ok) {
+    P.e[rank] = pick;
+    P.w[rank] = wv;
+  }
+  if (lane == 0) P.n_u = ok ? topk : 0;
+  if (writer) {
+    if (mode == 0 && lane < topk) {
+      header_out[1 + lane] = pick;
+      header_out[1 + topk + lane] = (int32_t)__builtin_bit_cast(uint32_t, wv);
+      header_out[1 + 2 * topk + rank] = pick;
+    }
+    if (lane < topk) {
+      if (ok) {
+        plan.u_expert()[rank] = pick;
+        plan.u_first()[rank] = rank;
+        plan.u_npairs()[rank] = 1;
+        plan.pair_tok()[rank] = 0;
+        plan.pair_expert()[rank] = pick;
+        plan.pair_w()[rank] = wv;
+        plan.tok_pairs()[rank] = rank;
+      } else {
+        plan.tok_pairs()[lane] = -1;
+      }
+    }
+    if (lane == 0) {
+      *plan.n_u() = ok ? topk : 0;
+      *plan.n_pairs() = ok ? topk : 0;
+      if (mode == 0) header_out[0] = nan_any ? MOE_STATUS_NAN_KEY : 0;
+      const int st = (nan_any ? MOE_STATUS_NAN_KEY : 0) | (ok ? 0 : MOE_STATUS_BAD_PICK);
+      if (st) atomicOr(status, st);
+    }
+  }
+}
+
+struct GateUp1Args {
+  int mode;                 // 0: select from the scores; 1: the caller's header
+  int shared_blocks;        // leading workgroups that run the shared expert's gate/up (mode 0)
+  moe_experts ex;
+  const float* bias;
+  const int32_t* hdr_in;
+  int32_t* hdr_out;
+  int n_routed, topk, norm;
+  float route_scale;
+  int dim, inter;
+  float L;
+  const uint16_t* x;
+  const uint16_t* w1;
+  const uint16_t* w3;
+};
+
+// ---------------------------------------------------------------------------
+template <int NSB, int SLOTS, int KPER>
+__global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
+  using G = GateUpGeom<NSB>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float gu[2][32];
+  __shared__ M1Plan P;
+  __shared__ __align__(16) uint8_t act_lds[ActLds<NSB>::kBytes];
+  const bool shared = (int)blockIdx.x < a.shared_blocks;
+  const int u0 = blockIdx.x * front::kSharedUnitsPerBlock;
+  if (shared) {
+    front::shared_gu_units_m1(u0, a.x, a.dim, a.inter, a.w1, a.w3, gu[0], gu[1]);
+    __syncthreads();
+  } else {
+    const int blk = blockIdx.x - a.shared_blocks;
+    const int ngr = a.inter / 32;
+    const int slot = blk / ngr, grp = blk % ngr;
+    const int sb = threadIdx.x % NSB;
+    if (threadIdx.x < 64) {
+      plan_m1<KPER>(a.mode, blk == 0, w.scores, a.bias, a.hdr_in, a.n_routed, a.topk, a.norm, a.route_scale,
+                    a.hdr_out, w.plan, w.status, P);
+    } else {   // meanwhile the other waves stage the token's q8_1 activation, once for the block
+      for (int i = threadIdx.x - 64; i < ActLds<NSB>::kChunks; i += 192)
+        act_piece_to_lds<NSB>(act_lds, w.xq, w.xs, w.xd, i);
+    }
+    __syncthreads();   // also completes every wave's outstanding loads: the tile DMA below is all vmcnt sees
+    const int e = P.e[slot];
+    if (e < 0) return;
+    Act A;
+    load_act_lds<NSB>(A, act_lds, sb);
+    const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
+    auto tile_src = [&](int c) -> const uint8_t* {
+      const uint64_t off = (c & 1) ? a.ex.up_off : a.ex.gate_off;
+      return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
+    };
+  #pragma unroll
+    for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
+  #pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int issued = (c + SLOTS < 4 ? c + SLOTS : 4);
+      const int after = issued - c - 1;
+      if (after == 3) wait_vmcnt<3 * G::kKC>();
+      else if (after == 2) wait_vmcnt<2 * G::kKC>();
+      else if (after == 1) wait_vmcnt<1 * G::kKC>();
+      else wait_vmcnt<0>();
+      block_sync_lds();
+      const uint8_t* sl = lds + (c % SLOTS) * G::kSlotBytes;
+      const int mat = c & 1, r0 = 16 * (c >> 1);
+  #pragma unroll
+      for (int it = 0; it < G::kIters; ++it) {
+        const int i = it * 256 + threadIdx.x;
+        const bool act = i < G::kItems;
+        const int row = i / NSB;
+        double part = act ? dot_q2k(sl + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
+        part = seg_sum_f64<NSB>(part);
+        if (act && sb == 0) gu[mat][r0 + row] = (float)part;
+      }
+      if (c + SLOTS < 4) {
+        wait_lgkm0();
+        block_sync_lds();
+        dma_tile<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kSlotBytes, G::kTileChunks);
+      }
+    }
+    __syncthreads();
+  }
+  // one SwiGLU site for both kinds of workgroup (the function is large)
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, r = lane & 31;
+    const float gv = gu[0][r], uv = gu[1][r];
+    const float hv = swiglu(gv, uv, a.L);
+    if (shared) {
+      if (lane < front::kSharedUnitsPerBlock && u0 + lane < a.inter) {
+        w.sg[u0 + lane] = gv;
+        w.su[u0 + lane] = uv;
+        w.sh[u0 + lane] = bf16_rne(hv);
+      }
+      return;
+    }
+    const int blk = blockIdx.x - a.shared_blocks;
+    const int slot = blk / (a.inter / 32), grp = blk % (a.inter / 32);
+    float am = fabsf(hv);
+    for (int s = 16; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
+    const float d = (float)((double)am / 127.0);
+    const int q = am == 0.0f ? 0 : q8_code(hv, d);
+    int sum = q;
+    for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+    if (lane < 32) {
+      const int64_t row = (int64_t)slot * a.inter + 32 * grp + r;
+      w.g[row] = gv;
+      w.u[row] = uv;
+      w.h[row] = hv;
+      w.hq[row] = (int8_t)q;
+      if (r == 0) w.hd[(int64_t)slot * (a.inter / 32) + grp] = __builtin_bit_cast(uint16_t, (_Float16)d);
+      if ((r & 15) == 0) w.hs[(int64_t)slot * (a.inter / 16) + 2 * grp + (r >> 4)] = sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-wave DMA of `nchunks` 16-byte chunks (lanes past the end re-read the
+// last chunk into the padding after it).
+template <int NCH>
+__device__ __forceinline__ void dma_wave(const uint8_t* g, uint8_t* dst) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < (NCH + 63) / 64; ++k) {
+    const int i = 64 * k + lane;
+    const int src = i < NCH ? i : NCH - 1;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * src),
+                                     (__attribute__((address_space(3))) void*)(dst + 16 * 64 * k), 16, 0, 0);
+  }
+}
+
+template <int NSB, int ROWS>
+struct DownM1Geom {
+  static constexpr int kRowBytes = NSB * kQ3KBytes;
+  static constexpr int kChunks = ROWS * kRowBytes / 16;
+  static constexpr int kWaveBytes = ((kChunks + 63) / 64) * 1024;
+  static constexpr int kItems = ROWS * NSB;            // per wave
+  static constexpr int kIters = (kItems + 63) / 64;
+};
+
+constexpr int kDownRows = 16;
+
+template <int NSB, bool SHARED>
+__global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
+                                                 const uint16_t* __restrict__ w2, float* __restrict__ out_f32,
+                                                 uint16_t* __restrict__ out_bf16) {
+  using G = DownM1Geom<NSB, kDownRows>;
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ __align__(16) uint8_t act_lds[kMaxTopk][ActLds<NSB>::kBytes];
+  __shared__ float ys[kMaxTopk][kDownRows];
+  __shared__ float sds[kDownRows];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = blockIdx.x * kDownRows;
+  const int n_u = *w.plan.n_u();
+  if (wave < topk) {
+    const int e = wave < n_u ? w.plan.u_expert()[wave] : -1;
+    if (e >= 0) {
+      const int sb = lane % NSB;
+      uint8_t* mine = lds + wave * G::kWaveBytes;
+      dma_wave<G::kChunks>((const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off +
+                               (uint64_t)row0 * G::kRowBytes, mine);
+      // this expert's q8_1(h), staged once for the wave while its rows stream in
+      uint8_t* al = act_lds[wave];
+      for (int i = lane; i < ActLds<NSB>::kChunks; i += 64)
+        act_piece_to_lds<NSB>(al, w.hq + (int64_t)wave * inter, w.hs + (int64_t)wave * (inter / 16),
+                              w.hd + (int64_t)wave * (inter / 32), i);
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      Act A;
+      load_act_lds<NSB>(A, al, sb);
+#pragma unroll
+      for (int it = 0; it < G::kIters; ++it) {
+        const int i = it * 64 + lane;
+        const bool act = i < G::kItems;
+        const int row = i / NSB;
+        double part = act ? dot_q3k(mine + row * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
+        part = seg_sum_f64<NSB>(part);
+        if (act && sb == 0) {
+          ys[wave][row] = (float)part;
+          w.y[(int64_t)wave * dim + row0 + row] = (float)part;
+        }
+      }
+    } else if (lane < kDownRows) {
+      ys[wave][lane] = 0.0f;
+    }
+  } else if (SHARED && wave < topk + 2) {
+    // shared expert down rows: half of the block's rows per wave, f32
+    constexpr int kR = kDownRows / 2;
+    constexpr int kCh = NSB >= 2 ? NSB / 2 : 1;   // 16-byte chunks of a row per lane (inter = 256*NSB)
+    const int rbase = row0 + kR * (wave - topk);
+    float p[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) p[r] = 0.0f;
+    uint4 wv[kR][kCh];
+    uint4 hvv[kCh];
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {        // every load issued before any is used
+      const int k = 8 * lane + 512 * c;
+      const bool in = k < inter;
+      hvv[c] = in ? *reinterpret_cast<const uint4*>(w.sh + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < kR; ++r) wv[r][c] = in ? load_nt16(w2 + (int64_t)(rbase + r) * inter + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      float hv[8];
+      const uint32_t hh[4] = {hvv[c].x, hvv[c].y, hvv[c].z, hvv[c].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = bf16_f32((uint16_t)(hh[j >> 1] >> (16 * (j & 1))));
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const uint32_t ww[4] = {wv[r][c].x, wv[r][c].y, wv[r][c].z, wv[r][c].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          p[r] = __builtin_fmaf(bf16_f32((uint16_t)(ww[j >> 1] >> (16 * (j & 1)))), hv[j], p[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+      for (int s = 32; s >= 1; s >>= 1) p[r] += __shfl_xor(p[r], s);
+    if (lane < kR) {
+      float v = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+        if (r == lane) v = p[r];
+      sds[kR * (wave - topk) + lane] = v;
+      w.sd[rbase + lane] = v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kDownRows) {
+    const int r = threadIdx.x;
+    float acc = 0.0f;
+    for (int i = 0; i < topk; ++i)
+      if (i < n_u) acc = fadd(acc, fmul(w.plan.pair_w()[i], ys[i][r]));
+    if (SHARED) acc = fadd(acc, sds[r]);
+    if (out_f32) out_f32[row0 + r] = acc;
+    if (out_bf16) out_bf16[row0 + r] = bf16_rne(acc);
+  }
+}
+
+template <int NSB>
+hipError_t launch_gateup_m1_t(const GateUp1Args& a, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  using G = GateUpGeom<NSB>;
+  constexpr int kSlots = 3;
+  const size_t shm = (size_t)kSlots * G::kSlotBytes;
+  auto kern6 = k_gateup_m1<NSB, kSlots, 6>;
+  auto kern16 = k_gateup_m1<NSB, kSlots, 16>;
+  const bool small = c.n_routed <= 384;
+  auto kern = small ? kern6 : kern16;
+  static bool attr_set[2] = {false, false};
+  const int ai = small ? 0 : 1;
+  if (!attr_set[ai]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set[ai] = true;
+  }
+  MOE_LAUNCH(MOE_K_GATEUP, kern, dim3(a.shared_blocks + c.topk * (c.inter / 32)), dim3(256), shm, s, a, w);
+  return hipGetLastError();
+}
+
+template <int NSB>
+hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
+                            uint16_t* out_bf16, hipStream_t s) {
+  using G = DownM1Geom<NSB, kDownRows>;
+  size_t shm = (size_t)c.topk * G::kWaveBytes;
+  const int threads = 64 * (c.topk + (w2 ? 2 : 0));
+  auto kern = w2 ? k_down_m1<NSB, true> : k_down_m1<NSB, false>;
+  static bool attr_set[2] = {false, false};
+  const int ai = w2 ? 1 : 0;
+  if (!attr_set[ai]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kMaxTopk * G::kWaveBytes));
+    if (e != hipSuccess) return e;
+    attr_set[ai] = true;
+  }
+  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, c.topk, w2,
+             out_f32, out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const int32_t* hdr_in,
+                            const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  GateUp1Args a;
+  a.mode = sel ? 0 : 1;
+  a.shared_blocks = (sel && layer) ? (c.inter + front::kSharedUnitsPerBlock - 1) / front::kSharedUnitsPerBlock : 0;
+  a.ex = ex;
+  a.bias = sel ? sel->bias : nullptr;
+  a.hdr_in = hdr_in;
+  a.hdr_out = sel ? sel->header : nullptr;
+  a.n_routed = c.n_routed;
+  a.topk = c.topk;
+  a.norm = c.norm_topk_prob;
+  a.route_scale = c.route_scale;
+  a.dim = c.dim;
+  a.inter = c.inter;
+  a.L = c.swiglu_limit;
+  a.x = x;
+  a.w1 = layer ? layer->sh_w1 : nullptr;
+  a.w3 = layer ? layer->sh_w3 : nullptr;
+  switch (c.dim / 256) {
+    case 1: return launch_gateup_m1_t<1>(a, c, w, s);
+    case 2: return launch_gateup_m1_t<2>(a, c, w, s);
+    case 4: return launch_gateup_m1_t<4>(a, c, w, s);
+    case 8: return launch_gateup_m1_t<8>(a, c, w, s);
+    case 16: return launch_gateup_m1_t<16>(a, c, w, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s) {
+  hipError_t err;
+  switch (c.inter / 256) {
+    case 1: err = launch_down_m1_t<1>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 2: err = launch_down_m1_t<2>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 4: err = launch_down_m1_t<4>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 8: err = launch_down_m1_t<8>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 16: err = launch_down_m1_t<16>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    default: err = hipErrorInvalidValue; break;
+  }
+  return err;
+}
+
+}  // namespace moe

@@ -37,18 +37,12 @@ struct PlanView {
   static int words(int max_pairs, int max_m, int topk) { return 2 + 6 * max_pairs + max_m * topk; }
 };
 
-// Control words of the single-token persistent kernel (workspace region
-// `ctl`): zero between calls.
+// Control words (workspace region `ctl`, 256 bytes, zero between calls).
 struct Ctl {
-  uint32_t ticket;       // next work item
-  uint32_t exited;       // workgroups that ran out of work
-  uint32_t r_done;       // router items finished
-  uint32_t s_done;       // shared gate/up items finished
-  uint32_t g_done;       // routed gate/up items finished
-  uint32_t plan_ready;   // 1 once the plan, header and status are written
-  uint32_t fault;        // a bounded wait ran out
-  uint32_t pad;
+  uint32_t router_done;   // router workgroups of the running front launch that have finished
+  uint32_t pad[63];
 };
+static_assert(sizeof(Ctl) == 256, "control region size");
 
 // Device-side view of the workspace for one call.
 struct Ws {
@@ -78,13 +72,18 @@ bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L);
 Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m);
 
 // ---- launchers (each returns hipError_t of the launch) ----
-// front: status reset, q8_1 of x, and (when the pointers are given) the
-// router with its scores and the shared expert's gate/up + SwiGLU.
-hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const uint16_t* w1, const uint16_t* w3,
-                        const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s);
+// front: status reset, q8_1 of x (and for m = 1 its LDS image), and when
+// gate_w is given the router with its scores; when `sel` is given, the last
+// router workgroup also selects every token's top-k, writes the headers and
+// builds the plan; when w1/w3 are given, the shared expert's gate/up + SwiGLU.
+struct FrontSelect {
+  const float* bias;
+  int32_t* header;
+};
+hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const FrontSelect* sel, const uint16_t* w1,
+                        const uint16_t* w3, const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s);
 hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, bool with_plan,
-                         hipStream_t s);
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s);
 hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
 hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
 // down: routed Q3_K rows, plus the shared expert's down rows when w2 is given.
@@ -93,14 +92,15 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
 hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
                           hipStream_t s);
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
-// Single token, the whole layer (mode 0: routing here, `layer` given) or the
-// routed experts for a caller's header (mode 1) in one persistent launch.
-bool layer1_supported(const moe_cfg& c);
-hipError_t launch_layer1(int mode, const moe_cfg& c, const uint16_t* x, const moe_layer* layer,
-                         const moe_experts& ex, const int32_t* hdr_in, int32_t* hdr_out, float* out_f32,
-                         uint16_t* out_bf16, uint16_t* x_next, const Ws& w, hipStream_t s);
-// Polls a bounded wait makes before it gives up (moe_set_wait_limit).
-uint32_t spin_limit();
+// single token: the gate/up rows of every pick + SwiGLU + q8_1 of h, with the
+// plan selected here from the front launch's scores (`sel` given; the shared
+// expert's gate/up rows run in the same launch when `layer` is given too) or
+// from the caller's header (checked here); then the down rows of every pick +
+// the shared expert's down rows + the combine.
+hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const int32_t* hdr_in,
+                            const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s);
 // Zero-fill of `bytes` bytes (a multiple of 16) with a kernel (no memset node).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

@@ -1,15 +1,17 @@
 // Routing kernels (A1-A3) and the front of the layer:
 //  * k_front: q8_1 of the input, the router GEMV with the scores, and (for
 //    the whole layer) the shared expert's gate/up GEMVs with its SwiGLU, in
-//    one launch (the workgroup index picks the part);
-//  * k_select / k_select_plan: the top-k selection and its header, and for
-//    decode (m <= 8) the plan tables in the same launch;
+//    one launch (the workgroup index picks the part). For the layer, the last
+//    router workgroup to finish also runs every token's top-k selection,
+//    writes the headers and builds the plan, while the shared rows stream;
+//  * k_select: the top-k selection and its header alone (routing only);
 //  * k_plan_small: the plan tables from caller-given headers.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
 #include "moe_math.h"
 #include "moe_front.h"
+#include "moe_kquant.h"
 #include "moe_select.h"
 
 namespace moe {
@@ -18,33 +20,6 @@ namespace {
 using front::quant_x_block;
 using front::router_rows;
 using front::shared_gu_rows;
-
-struct FrontArgs {
-  const uint16_t* x;
-  int m, dim, inter, n_routed;
-  float temp, L;
-  const uint16_t* gate_w;
-  const uint16_t* w1;
-  const uint16_t* w3;
-  float* logits_out;
-  int router_blocks, shared_blocks;
-};
-
-__global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
-  int blk = blockIdx.x;
-  if (blk == 0 && threadIdx.x < 4) w.status[threadIdx.x] = 0;   // every entry point starts here
-  if (blk < a.router_blocks) {
-    router_rows(blk, a.x, a.m, a.dim, a.gate_w, a.n_routed, a.temp, w.logits, w.scores, a.logits_out);
-    return;
-  }
-  blk -= a.router_blocks;
-  if (blk < a.shared_blocks) {
-    shared_gu_rows(blk, a.x, a.m, a.dim, a.inter, a.w1, a.w3, w.sg, w.su, w.sh, a.L);
-    return;
-  }
-  blk -= a.shared_blocks;
-  quant_x_block(blk, a.x, w.xq, w.xd, w.xs);
-}
 
 // ---------------------------------------------------------------------------
 // Selection, one wave per token (moe_select.h): writes the header
@@ -138,23 +113,70 @@ __device__ void build_plan(const int* picks, const float* wts, const int* tok_ok
   }
 }
 
+struct FrontArgs {
+  const uint16_t* x;
+  int m, dim, inter, n_routed, topk, norm;
+  float temp, L, route_scale;
+  const uint16_t* gate_w;
+  const float* bias;   // non-null: select, write the headers and the plan
+  int32_t* header;
+  const uint16_t* w1;
+  const uint16_t* w3;
+  float* logits_out;
+  int router_blocks, shared_blocks;
+};
+
+// Every token's selection (one wave per token, four waves) and the plan
+// [moe_v41.rs, fn route_from_logits; device_route.rs, fn device_route_check].
 template <int KPER>
-__global__ __launch_bounds__(512) void k_select_plan(const float* __restrict__ scores,
-                                                     const float* __restrict__ bias, int m, int n_routed, int topk,
-                                                     int norm, float route_scale, int32_t* __restrict__ header,
-                                                     PlanView plan, int32_t* __restrict__ status) {
+__device__ void select_all(const FrontArgs& a, const Ws& w) {
   __shared__ int picks[64];
   __shared__ float wts[64];
   __shared__ int tok_ok[kMaxDecodeTokens];
   __shared__ int first_flag[64];
   const int wave = threadIdx.x >> 6;
-  if (wave < m) {
-    select_token<KPER>(scores + (int64_t)wave * n_routed, bias, n_routed, topk, norm, route_scale,
-                       header + (int64_t)wave * (1 + 3 * topk), picks + wave * topk, wts + wave * topk, status);
-    if ((threadIdx.x & 63) == 0) tok_ok[wave] = 1;
+  const int hw = 1 + 3 * a.topk;
+  for (int t = wave; t < a.m; t += 4) {
+    select_token<KPER>(w.scores + (int64_t)t * a.n_routed, a.bias, a.n_routed, a.topk, a.norm, a.route_scale,
+                       a.header + (int64_t)t * hw, picks + t * a.topk, wts + t * a.topk, w.status);
+    if ((threadIdx.x & 63) == 0) tok_ok[t] = 1;
   }
   __syncthreads();
-  if (wave == 0) build_plan(picks, wts, tok_ok, m, topk, plan, first_flag);
+  if (wave == 0) build_plan(picks, wts, tok_ok, a.m, a.topk, w.plan, first_flag);
+}
+
+__global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
+  __shared__ int s_last;
+  int blk = blockIdx.x;
+  if (blk == 0 && threadIdx.x < 4) w.status[threadIdx.x] = 0;   // every entry point starts here
+  if (blk < a.router_blocks) {
+    router_rows(blk, a.x, a.m, a.dim, a.gate_w, a.n_routed, a.temp, w.logits, w.scores, a.logits_out);
+    if (!a.bias) return;
+    // Count this workgroup's rows as done; the last of the router workgroups
+    // selects. Each wave completes its stores, then one release (one L2
+    // write-back) covers the workgroup; the selecting workgroup acquires.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(&w.ctl->router_done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old + 1 == (uint32_t)a.router_blocks;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (a.n_routed <= 384) select_all<6>(a, w);
+    else select_all<16>(a, w);
+    // the counter is back to zero for the next launch (no other workgroup touches it now)
+    if (threadIdx.x == 0) __hip_atomic_store(&w.ctl->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  blk -= a.router_blocks;
+  if (blk < a.shared_blocks) {
+    shared_gu_rows(blk, a.x, a.m, a.dim, a.inter, a.w1, a.w3, w.sg, w.su, w.sh, a.L);
+    return;
+  }
+  blk -= a.shared_blocks;
+  quant_x_block(blk, a.x, w.xq, w.xd, w.xs);
 }
 
 template <int KPER>
@@ -205,17 +227,22 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, in
 
 }  // namespace
 
-hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const uint16_t* w1, const uint16_t* w3,
-                        const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s) {
+hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const FrontSelect* sel, const uint16_t* w1,
+                        const uint16_t* w3, const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s) {
   FrontArgs a;
   a.x = x;
   a.m = m;
   a.dim = c.dim;
   a.inter = c.inter;
   a.n_routed = c.n_routed;
+  a.topk = c.topk;
+  a.norm = c.norm_topk_prob;
   a.temp = c.gate_temp;
   a.L = c.swiglu_limit;
+  a.route_scale = c.route_scale;
   a.gate_w = gate_w;
+  a.bias = (gate_w && sel) ? sel->bias : nullptr;
+  a.header = sel ? sel->header : nullptr;
   a.w1 = w1;
   a.w3 = w3;
   a.logits_out = logits_out;
@@ -226,24 +253,14 @@ hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const 
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, bool with_plan,
-                         hipStream_t s) {
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s) {
   const int kper = (c.n_routed + 63) / 64;
-  if (with_plan) {
-    if (kper == 6)
-      hipLaunchKernelGGL(k_select_plan<6>, dim3(1), dim3(512), 0, s, w.scores, bias, m, c.n_routed, c.topk,
-                         c.norm_topk_prob, c.route_scale, header, w.plan, w.status);
-    else
-      hipLaunchKernelGGL(k_select_plan<16>, dim3(1), dim3(512), 0, s, w.scores, bias, m, c.n_routed, c.topk,
-                         c.norm_topk_prob, c.route_scale, header, w.plan, w.status);
-  } else {
-    if (kper == 6)
-      hipLaunchKernelGGL(k_select<6>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk,
-                         c.norm_topk_prob, c.route_scale, header, w.status);
-    else
-      hipLaunchKernelGGL(k_select<16>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk,
-                         c.norm_topk_prob, c.route_scale, header, w.status);
-  }
+  if (kper == 6)
+    hipLaunchKernelGGL(k_select<6>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk, c.norm_topk_prob,
+                       c.route_scale, header, w.status);
+  else
+    hipLaunchKernelGGL(k_select<16>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk, c.norm_topk_prob,
+                       c.route_scale, header, w.status);
   return hipGetLastError();
 }
 
@@ -253,7 +270,7 @@ hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws&
 }
 
 hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  return launch_front(x, m, nullptr, nullptr, nullptr, c, w, nullptr, s);
+  return launch_front(x, m, nullptr, nullptr, nullptr, nullptr, c, w, nullptr, s);
 }
 
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s) {

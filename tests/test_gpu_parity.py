@@ -262,11 +262,11 @@ def test_experts_decode_rejects_bad_picks():
     assert ws_array(ws, L, "status", np.int32, 1)[0] & R.MOE_STATUS_BAD_PICK
 
 
-# ------------------------------------------------ the single-token kernel
+# ------------------------------------------------ the single-token launches
 @pytest.mark.parametrize("shape,calls", [(TINY, 4), (DS41, 2)])
 def test_single_token_kernel_reuses_its_workspace(shape, calls):
-    """Back-to-back m = 1 layers on one workspace: the kernel's control words
-    are left at zero by every call, so each call is right on its own."""
+    """Back-to-back m = 1 layers on one workspace: the front launch's router
+    counter is left at zero by every call, so each call is right on its own."""
     dl = device_layer(shape)
     c = dl.cfg
     ws = workspace(c, 1)
@@ -292,9 +292,9 @@ def test_single_token_kernel_reuses_its_workspace(shape, calls):
 
 @pytest.mark.parametrize("shape", [TINY, DS41])
 def test_single_token_kernel_equals_multi_token_path(shape):
-    """The same token alone (one launch) and twice in an m = 2 call (the
-    multi-token launches): identical header and routed sum, and layer outputs
-    that differ only by the shared expert's f32 summation order."""
+    """The same token alone (the single-token kernels) and twice in an m = 2
+    call (the multi-token kernels): identical header and routed sum, and layer
+    outputs that differ only by the shared expert's f32 summation order."""
     dl = device_layer(shape)
     c = dl.cfg
     x_np = synth.tokens(dl.spec, 77, 1)
@@ -318,33 +318,3 @@ def test_single_token_kernel_equals_multi_token_path(shape):
     assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
     assert np.array_equal(y2[0].view(np.uint32), y2[1].view(np.uint32))
     assert rel_l2(o1[0], o2[0]) <= 1e-5 and np.abs(o1[0] - o2[0]).max() <= 1e-3
-
-
-def test_single_token_kernel_wait_limit():
-    """A wait limit of one poll makes the kernel's waits give up instead of
-    waiting: the launch still drains, reports MOE_STATUS_TIMEOUT when a wait
-    gave up, and leaves the workspace ready for the next call."""
-    dl = device_layer(TINY)
-    c = dl.cfg
-    ws = workspace(c, 1)
-    x_np = synth.tokens(dl.spec, 5, 1)
-    x = torch.from_numpy(x_np).cuda()
-    out = torch.empty((1, TINY.dim), dtype=torch.uint16, device="cuda")
-    o32 = torch.empty((1, TINY.dim), dtype=torch.float32, device="cuda")
-    L = R.workspace_layout(c, 1)
-    say("single-token kernel with a wait limit of 1 poll")
-    try:
-        R.set_wait_limit(1)
-        R.layer_forward(c, dl.layer, x, out, ws, out_f32=o32)
-        torch.cuda.synchronize()
-    finally:
-        R.set_wait_limit(0)
-    st = int(ws_array(ws, L, "status", np.int32, 1)[0])
-    assert st & ~(R.MOE_STATUS_TIMEOUT | R.MOE_STATUS_NAN_KEY) == 0, st
-    assert not ws_array(ws, L, "ctl", np.uint32, 64).any()
-    say(f"  status after the limited call: {st}")
-    R.layer_forward(c, dl.layer, x, out, ws, out_f32=o32)
-    torch.cuda.synchronize()
-    assert int(ws_array(ws, L, "status", np.int32, 1)[0]) == 0
-    ref = olayer.layer_forward(dl.spec, x_np)
-    assert rel_l2(o32.cpu().numpy()[0], ref["out_f32"][0]) <= 1e-3

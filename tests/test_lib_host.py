@@ -35,14 +35,14 @@ def test_workspace_queries():
     assert 0 < n1 < n8
     L = R.workspace_layout(c, 8)
     offs = [L[k] for k in ("xq", "xd", "xs", "logits", "scores", "plan", "g", "u", "h", "hq", "hd", "hs", "y",
-                           "sg", "su", "sh", "sd", "yr", "status")]
+                           "sg", "su", "sh", "sd", "yr", "status", "ctl")]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs) and L["total"] == n8
     assert L["max_pairs"] == 48
     assert R.header_words(c) == 19
 
 
-@pytest.mark.parametrize("field,value", [("dim", 300), ("dim", 256 * 3), ("inter", 0), ("topk", 9),
-                                         ("n_routed", 2000)])
+@pytest.mark.parametrize("field,value", [("dim", 300), ("dim", 256 * 3), ("dim", 256 * 32), ("inter", 0),
+                                         ("inter", 256 * 32), ("topk", 9), ("n_routed", 2000)])
 def test_unsupported_shapes_are_rejected(field, value):
     c = R.cfg_from_shape(synth.SHAPE_TINY)
     setattr(c, field, value)
