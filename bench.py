@@ -114,6 +114,75 @@ def cpu_baseline(spec, seconds: float):
                       f"input generation excluded"}
 
 
+def stack_bench(args):
+    """One token (or m) per step through a stack of `--layers` dim-4096 layers,
+    all resident; the residual stream between layers runs on the device."""
+    import numpy as np
+    import torch
+
+    import routing_quant_expert_amd as R
+    import synth
+    from synth.device import DeviceLayer
+
+    n, m = args.layers, args.m
+    specs = [synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed, layer=l) for l in range(n)]
+    s = specs[0].shape
+    print(f"bench: generating {n} layers on the device", file=sys.stderr, flush=True)
+    dls = [DeviceLayer(sp) for sp in specs]
+    layers = [d.layer for d in dls]
+    cfg = dls[0].cfg
+    nt_tok = max(1, args.tokens)
+    xs_all = torch.empty((nt_tok, n + 1, m, s.dim), dtype=torch.uint16, device="cuda")
+    for t in range(nt_tok):
+        x0 = synth.tokens(specs[0], t * m, m) if m == 1 else synth.correlated_tokens(specs[0], m, group=t)
+        xs_all[t, 0] = torch.from_numpy(x0).cuda()
+    ws = torch.empty(R.workspace_bytes(cfg, m), dtype=torch.uint8, device="cuda")
+    R.workspace_init(cfg, m, ws)
+    hdrs = torch.empty((n, m, R.header_words(cfg)), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i):
+        R.stack_forward(cfg, layers, xs_all[i % nt_tok], ws, headers=hdrs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    layer_bytes = s.n_routed * s.dim * 2 + 3 * s.inter * s.dim * 2 + s.topk * (2 * s.gate_bytes + s.down_bytes)
+    step_bytes = n * layer_bytes if m == 1 else None
+    res = {
+        "metric": "MoE-layer decode tokens/s at m=1 and % of HBM peak on expert-weight bytes",
+        "value": K * m / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"moe_stack{n}_decode_m{m}_dim4096_inter2048_e384_top6", "layers": n, "m": m,
+                   "dim": s.dim, "inter": s.inter, "n_routed": s.n_routed, "topk": s.topk,
+                   "resident_weight_bytes": n * (s.n_routed * s.expert_stride + 3 * s.inter * s.dim * 2 +
+                                                 s.n_routed * s.dim * 2), "seed": args.seed},
+        "detail": {"us_per_layer": wall * 1e6 / K / n},
+    }
+    if step_bytes:
+        gbs = step_bytes / (wall / K) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "whole step (all launches)",
+                           "bytes_per_launch": step_bytes}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +195,8 @@ def main():
     ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's timed kernel")
     ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernel; 2..8: the "
                                                      "multi-token path on correlated rows)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="decode through a stack of this many layers per step (each its own seeded weights)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -160,6 +231,8 @@ def main():
     m = args.m
     print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts) on the device",
           file=sys.stderr, flush=True)
+    if args.layers > 1:
+        return stack_bench(args)
     dl = DeviceLayer(spec)
     if m == 1:
         xs = torch.from_numpy(synth.tokens(spec, 0, args.tokens)).cuda()

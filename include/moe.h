@@ -185,6 +185,20 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
 int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
                       float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step through a stack of n_layers MoE layers for m <= 8 tokens:
+ * for l = 0 .. n_layers-1, out_l = layer l applied to x_l exactly as
+ * moe_layer_forward computes it, and x_{l+1} = bf16(f32(x_l) + out_l), the
+ * residual stream between layers (the pages' step runs the layers back to
+ * back [step_seg.rs, module doc]; they name no norm between MoE layers and
+ * none is applied here). All launches are enqueued on `stream` in order,
+ * with no host synchronisation; the workspace is reused by every layer.
+ *   layers   HOST array of n_layers moe_layer (device pointers inside)
+ *   xs       bf16 [n_layers+1][m][dim]: xs[0] is the input, xs[l+1] is written
+ *   out_f32  f32  [n_layers][m][dim] per-layer output before the residual add, may be NULL
+ *   headers  int32 [n_layers][m][moe_header_words] per-layer headers, may be NULL */
+int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_layers, uint16_t* xs, int32_t m,
+                      float* out_f32, int32_t* headers, void* ws, size_t ws_bytes, void* stream);
+
 /* The score chain of A3 alone on device data: out[i] = sqrt(softplus(
  * logits[i] / temp)) with correctly rounded exp, log1p, division and sqrt
  * [moe_v41.rs, fn softplus, fn route_from_logits]. flags bit 0 forces the

@@ -8,13 +8,15 @@ prefill are defined exactly as m = 1 repeated):
      Q2_K gate/up GEMV, clamped SwiGLU, q8_1, Q3_K down GEMV
   4. acc = sum over the plan of w*y (f32, in plan order), then + shared expert
      output, out = bf16(acc)                           [moe_v41.rs, fn shared_side]
+A stack of layers (one decode step through them, [step_seg.rs, module doc])
+adds each layer's output to its input in f32 and rounds to bf16.
 """
 from __future__ import annotations
 
 import numpy as np
 
 import synth
-from . import (bf16_to_f32, combine, expert, header_fields, q8_1, router_logits, select, shared)
+from . import (bf16_to_f32, combine, expert, f32_to_bf16, header_fields, q8_1, router_logits, select, shared)
 
 
 class ExpertCache:
@@ -74,3 +76,30 @@ def layer_forward(spec: synth.LayerSpec, x_bf16: np.ndarray, *, with_shared: boo
         out["out_f32"][t], out["out_bf16"][t] = combine(ys, w_plan, sd)
         out["tok"].append({"ids": ids, "w_plan": w_plan, "experts": per if keep_experts else None})
     return out
+
+
+def residual(x_bf16: np.ndarray, out_f32: np.ndarray) -> np.ndarray:
+    """The residual stream between stacked layers (the reading stated in the
+    layer-stack entry point: no norm is named, none is applied):
+    x_next = bf16(f32(x) + out), one f32 addition rounded to nearest."""
+    return f32_to_bf16(bf16_to_f32(x_bf16) + np.asarray(out_f32, np.float32))
+
+
+def stack_forward(specs, x0_bf16: np.ndarray, xs_given=None, layer_kwargs=None) -> dict:
+    """One decode step through the layers of `specs` in order. Each layer is
+    layer_forward on x_l; x_{l+1} = residual(x_l, out_l). With `xs_given`
+    ([n_layers+1, m, dim] bf16), layer l reads xs_given[l] instead of its own
+    x_l (teacher forcing: every layer checked on the same input as the
+    device's). layer_kwargs: per-layer keyword arguments for layer_forward
+    (weights given explicitly instead of generated from the spec)."""
+    x = np.ascontiguousarray(x0_bf16, np.uint16)
+    xs, outs, headers = [x], [], []
+    for l, spec in enumerate(specs):
+        xin = xs_given[l] if xs_given is not None else x
+        kw = dict(layer_kwargs[l]) if layer_kwargs is not None else {}
+        r = layer_forward(spec, xin, keep_experts=False, **kw)
+        outs.append(r["out_f32"])
+        headers.append(r["header"])
+        x = residual(xin, r["out_f32"])
+        xs.append(x)
+    return {"xs": np.stack(xs), "out_f32": np.stack(outs), "headers": np.stack(headers)}

@@ -7,12 +7,12 @@ in include/moe.h); this package only marshals arguments to it.
 from .binding import (MOE_K_DOWN, MOE_K_GATEUP, MOE_K_ROUTER, MOE_STATUS_BAD_PICK, MOE_STATUS_MISS,
                       MOE_STATUS_NAN_KEY, Cfg, Experts, Layer, MoeError, cfg_from_shape,
                       experts_decode, header_words, layer_forward, lib, route_select, scores, scores_host,
-                      swiglu_host, time_next_launch, workspace_bytes, workspace_init,
+                      stack_forward, swiglu_host, time_next_launch, workspace_bytes, workspace_init,
                       workspace_layout)
 
 __all__ = [
     "Cfg", "Experts", "Layer", "MoeError", "cfg_from_shape", "experts_decode", "header_words", "layer_forward",
-    "lib", "route_select", "scores", "scores_host", "swiglu_host", "time_next_launch",
+    "lib", "route_select", "scores", "scores_host", "stack_forward", "swiglu_host", "time_next_launch",
     "workspace_bytes", "workspace_init", "workspace_layout", "MOE_K_GATEUP", "MOE_K_DOWN", "MOE_K_ROUTER",
     "MOE_STATUS_MISS", "MOE_STATUS_NAN_KEY", "MOE_STATUS_BAD_PICK",
 ]

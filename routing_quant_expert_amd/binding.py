@@ -69,6 +69,8 @@ def lib():
                                          _VP, _VP, ctypes.c_size_t, _VP]
         L.moe_layer_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), _VP, ctypes.c_int32, _VP, _VP,
                                         _VP, _VP, ctypes.c_size_t, _VP]
+        L.moe_stack_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), ctypes.c_int32, _VP,
+                                         ctypes.c_int32, _VP, _VP, _VP, ctypes.c_size_t, _VP]
         L.moe_scores.argtypes = [_VP, ctypes.c_int64, ctypes.c_float, _VP, ctypes.c_int32, _VP]
         L.moe_scores_host.argtypes = [_VP, ctypes.c_int64, ctypes.c_float, _VP, ctypes.c_int32]
         L.moe_swiglu_host.argtypes = [_VP, _VP, ctypes.c_int64, ctypes.c_float, _VP]
@@ -135,6 +137,15 @@ def layer_forward(cfg: Cfg, layer: Layer, x, out_bf16, ws, out_f32=None, header=
     _check(lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(layer), _ptr(x), m, _ptr(out_bf16),
                                    _ptr(out_f32), _ptr(header), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
+
+
+def stack_forward(cfg: Cfg, layers, xs, ws, out_f32=None, headers=None, stream=None):
+    """xs: bf16 [n_layers+1, m, dim] (xs[0] the input); layers: a sequence of Layer."""
+    n = len(layers)
+    arr = (Layer * n)(*layers)
+    m = xs.shape[1]
+    _check(lib().moe_stack_forward(ctypes.byref(cfg), arr, n, _ptr(xs), m, _ptr(out_f32), _ptr(headers), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def scores(logits, temp: float, out, flags: int = 0, stream=None):

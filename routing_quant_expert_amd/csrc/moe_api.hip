@@ -143,6 +143,35 @@ bool take_timed(int which, hipEvent_t* begin, hipEvent_t* end) {
   return true;
 }
 
+int check_layer(const moe_layer* layer) {
+  if (!layer || !layer->gate_w || !layer->bias || !layer->sh_w1 || !layer->sh_w2 || !layer->sh_w3)
+    return fail(MOE_EINVAL, "layer weights must be non-NULL%s%lld");
+  if (!a16(layer->gate_w) || !a16(layer->sh_w1) || !a16(layer->sh_w2) || !a16(layer->sh_w3))
+    return fail(MOE_EINVAL, "the bf16 weights must be 16-byte aligned%s%lld");
+  return check_experts(&layer->experts);
+}
+
+// One layer's launches on `s` (A1-A7), the result to `o`.
+int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, int m, const LayerOut& o,
+                   int32_t* hdr, const Ws& w, hipStream_t s) {
+  hipError_t e;
+  FrontSelect sel{layer.bias, hdr};
+  if (m == 1) {   // router + q8_1 of x; then the selection, the routed and the shared gate/up in one launch
+    if ((e = launch_front(x, 1, layer.gate_w, nullptr, nullptr, nullptr, c, w, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "front");
+    if ((e = launch_gateup_m1(layer.experts, &sel, nullptr, x, &layer, c, w, s)) != hipSuccess)
+      return hip_fail(e, "gateup_m1");
+    if ((e = launch_down_m1(layer.experts, c, w, layer.sh_w2, o, s)) != hipSuccess) return hip_fail(e, "down_m1");
+    return MOE_OK;
+  }
+  if ((e = launch_front(x, m, layer.gate_w, &sel, layer.sh_w1, layer.sh_w3, c, w, nullptr, s)) != hipSuccess)
+    return hip_fail(e, "front");
+  if ((e = launch_gateup(layer.experts, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup");
+  if ((e = launch_down(layer.experts, m, c, w, layer.sh_w2, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_combine(m, c, w, w.sd, o, s)) != hipSuccess) return hip_fail(e, "combine");
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -207,47 +236,52 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   if (m == 1) {
     if ((e = launch_gateup_m1(*experts, nullptr, header, x, nullptr, *cfg, w, s)) != hipSuccess)
       return hip_fail(e, "gateup_m1");
-    if ((e = launch_down_m1(*experts, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess)
+    if ((e = launch_down_m1(*experts, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) !=
+        hipSuccess)
       return hip_fail(e, "down_m1");
     return MOE_OK;
   }
   if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
   if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(*experts, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
-  if ((e = launch_combine(m, *cfg, w, nullptr, y_routed, nullptr, s)) != hipSuccess) return hip_fail(e, "combine");
+  if ((e = launch_combine(m, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) != hipSuccess)
+    return hip_fail(e, "combine");
   return MOE_OK;
 }
 
 int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
                       float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
-  if (!layer || !x || !out_bf16 || !layer->gate_w || !layer->bias || !layer->sh_w1 || !layer->sh_w2 || !layer->sh_w3)
-    return fail(MOE_EINVAL, "layer weights, x and out_bf16 must be non-NULL%s%lld");
+  if (!x || !out_bf16) return fail(MOE_EINVAL, "x and out_bf16 must be non-NULL%s%lld");
+  if (int r = check_layer(layer)) return r;
   if (m < 1 || m > kMaxDecodeTokens) return fail(MOE_EINVAL, "decode needs 1 <= m <= 8%s (m %lld)", "", m);
-  if (!a16(x) || !a16(layer->gate_w) || !a16(layer->sh_w1) || !a16(layer->sh_w2) || !a16(layer->sh_w3))
-    return fail(MOE_EINVAL, "x and the bf16 weights must be 16-byte aligned%s%lld");
-  if (int r = check_experts(&layer->experts)) return r;
+  if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
   moe_ws_layout L;
   if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
   Ws w = ws_view(ws, L, *cfg, m);
-  int32_t* hdr = header ? header : w.status + 4;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  FrontSelect sel{layer->bias, hdr};
-  if (m == 1) {   // router + q8_1 of x; then the selection, the routed and the shared gate/up in one launch
-    if ((e = launch_front(x, 1, layer->gate_w, nullptr, nullptr, nullptr, *cfg, w, nullptr, s)) != hipSuccess)
-      return hip_fail(e, "front");
-    if ((e = launch_gateup_m1(layer->experts, &sel, nullptr, x, layer, *cfg, w, s)) != hipSuccess)
-      return hip_fail(e, "gateup_m1");
-    if ((e = launch_down_m1(layer->experts, *cfg, w, layer->sh_w2, out_f32, out_bf16, s)) != hipSuccess)
-      return hip_fail(e, "down_m1");
-    return MOE_OK;
+  LayerOut o{out_f32, out_bf16, nullptr, nullptr};
+  return layer_launches(*cfg, *layer, x, m, o, header ? header : w.status + 4, w, (hipStream_t)stream);
+}
+
+int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_layers, uint16_t* xs, int32_t m,
+                      float* out_f32, int32_t* headers, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!layers || !xs) return fail(MOE_EINVAL, "layers and xs must be non-NULL%s%lld");
+  if (n_layers < 1) return fail(MOE_EINVAL, "n_layers must be >= 1%s (n_layers %lld)", "", n_layers);
+  if (m < 1 || m > kMaxDecodeTokens) return fail(MOE_EINVAL, "decode needs 1 <= m <= 8%s (m %lld)", "", m);
+  if (!a16(xs) || ((int64_t)m * cfg->dim * 2) % 16) return fail(MOE_EINVAL, "xs must be 16-byte aligned%s%lld");
+  for (int l = 0; l < n_layers; ++l)
+    if (int r = check_layer(&layers[l])) return r;
+  moe_ws_layout L;
+  if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
+  Ws w = ws_view(ws, L, *cfg, m);
+  const int64_t row = (int64_t)m * cfg->dim;
+  const int hw = 1 + 3 * cfg->topk;
+  for (int l = 0; l < n_layers; ++l) {
+    LayerOut o{out_f32 ? out_f32 + l * row : nullptr, nullptr, xs + l * row, xs + (l + 1) * row};
+    int32_t* hdr = headers ? headers + (int64_t)l * m * hw : w.status + 4;
+    if (int r = layer_launches(*cfg, layers[l], xs + l * row, m, o, hdr, w, (hipStream_t)stream)) return r;
   }
-  if ((e = launch_front(x, m, layer->gate_w, &sel, layer->sh_w1, layer->sh_w3, *cfg, w, nullptr, s)) != hipSuccess)
-    return hip_fail(e, "front");
-  if ((e = launch_gateup(layer->experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
-  if ((e = launch_down(layer->experts, m, *cfg, w, layer->sh_w2, s)) != hipSuccess) return hip_fail(e, "down");
-  if ((e = launch_combine(m, *cfg, w, w.sd, out_f32, out_bf16, s)) != hipSuccess) return hip_fail(e, "combine");
   return MOE_OK;
 }
 

@@ -244,9 +244,8 @@ struct DownM1Geom {
 constexpr int kDownRows = 16;
 
 template <int NSB, bool SHARED>
-__global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
-                                                 const uint16_t* __restrict__ w2, float* __restrict__ out_f32,
-                                                 uint16_t* __restrict__ out_bf16) {
+__global__ __launch_bounds__(64 * (kMaxTopk + 2)) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
+                                                 const uint16_t* __restrict__ w2, LayerOut o) {
   using G = DownM1Geom<NSB, kDownRows>;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ __align__(16) uint8_t act_lds[kMaxTopk][ActLds<NSB>::kBytes];
@@ -337,8 +336,9 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
     for (int i = 0; i < topk; ++i)
       if (i < n_u) acc = fadd(acc, fmul(w.plan.pair_w()[i], ys[i][r]));
     if (SHARED) acc = fadd(acc, sds[r]);
-    if (out_f32) out_f32[row0 + r] = acc;
-    if (out_bf16) out_bf16[row0 + r] = bf16_rne(acc);
+    if (o.f32) o.f32[row0 + r] = acc;
+    if (o.bf16) o.bf16[row0 + r] = bf16_rne(acc);
+    if (o.next) o.next[row0 + r] = bf16_rne(fadd(bf16_f32(o.resid[row0 + r]), acc));
   }
 }
 
@@ -363,8 +363,8 @@ hipError_t launch_gateup_m1_t(const GateUp1Args& a, const moe_cfg& c, const Ws& 
 }
 
 template <int NSB>
-hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
-                            uint16_t* out_bf16, hipStream_t s) {
+hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
+                            hipStream_t s) {
   using G = DownM1Geom<NSB, kDownRows>;
   size_t shm = (size_t)c.topk * G::kWaveBytes;
   const int threads = 64 * (c.topk + (w2 ? 2 : 0));
@@ -378,7 +378,7 @@ hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w
     attr_set[ai] = true;
   }
   MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, c.topk, w2,
-             out_f32, out_bf16);
+             o);
   return hipGetLastError();
 }
 
@@ -413,15 +413,15 @@ hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const
   }
 }
 
-hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s) {
+hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
+                          hipStream_t s) {
   hipError_t err;
   switch (c.inter / 256) {
-    case 1: err = launch_down_m1_t<1>(ex, c, w, w2, out_f32, out_bf16, s); break;
-    case 2: err = launch_down_m1_t<2>(ex, c, w, w2, out_f32, out_bf16, s); break;
-    case 4: err = launch_down_m1_t<4>(ex, c, w, w2, out_f32, out_bf16, s); break;
-    case 8: err = launch_down_m1_t<8>(ex, c, w, w2, out_f32, out_bf16, s); break;
-    case 16: err = launch_down_m1_t<16>(ex, c, w, w2, out_f32, out_bf16, s); break;
+    case 1: err = launch_down_m1_t<1>(ex, c, w, w2, o, s); break;
+    case 2: err = launch_down_m1_t<2>(ex, c, w, w2, o, s); break;
+    case 4: err = launch_down_m1_t<4>(ex, c, w, w2, o, s); break;
+    case 8: err = launch_down_m1_t<8>(ex, c, w, w2, o, s); break;
+    case 16: err = launch_down_m1_t<16>(ex, c, w, w2, o, s); break;
     default: err = hipErrorInvalidValue; break;
   }
   return err;

@@ -217,8 +217,7 @@ __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, con
 // [moe_v41.rs, fn shared_side: added after the routed experts].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __restrict__ y, int dim, int topk,
-                                                 const float* __restrict__ sd, float* __restrict__ out_f32,
-                                                 uint16_t* __restrict__ out_bf16) {
+                                                 const float* __restrict__ sd, LayerOut o) {
   const int t = blockIdx.y;
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= dim) return;
@@ -228,8 +227,10 @@ __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __r
     if (p >= 0) acc = fadd(acc, fmul(plan.pair_w()[p], y[(int64_t)p * dim + r]));
   }
   if (sd) acc = fadd(acc, sd[(int64_t)t * dim + r]);
-  if (out_f32) out_f32[(int64_t)t * dim + r] = acc;
-  if (out_bf16) out_bf16[(int64_t)t * dim + r] = bf16_rne(acc);
+  const int64_t i = (int64_t)t * dim + r;
+  if (o.f32) o.f32[i] = acc;
+  if (o.bf16) o.bf16[i] = bf16_rne(acc);
+  if (o.next) o.next[i] = bf16_rne(fadd(bf16_f32(o.resid[i]), acc));
 }
 
 constexpr int kGateUpSlots = 3;
@@ -302,10 +303,8 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
   return err;
 }
 
-hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((c.dim + 255) / 256, m), dim3(256), 0, s, w.plan, w.y, c.dim, c.topk, sd,
-                     out_f32, out_bf16);
+hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, const LayerOut& o, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3((c.dim + 255) / 256, m), dim3(256), 0, s, w.plan, w.y, c.dim, c.topk, sd, o);
   return hipGetLastError();
 }
 

@@ -71,6 +71,16 @@ struct Ws {
 bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L);
 Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m);
 
+// Where a layer's result goes: out = the routed sum plus the shared expert
+// (f32 and/or its bf16 rounding), and for a layer stack the residual stream
+// next = bf16(f32(resid) + out). Every pointer may be NULL.
+struct LayerOut {
+  float* f32;
+  uint16_t* bf16;
+  const uint16_t* resid;
+  uint16_t* next;
+};
+
 // ---- launchers (each returns hipError_t of the launch) ----
 // front: status reset, q8_1 of x (and for m = 1 its LDS image), and when
 // gate_w is given the router with its scores; when `sel` is given, the last
@@ -89,8 +99,7 @@ hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const W
 // down: routed Q3_K rows, plus the shared expert's down rows when w2 is given.
 hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
                        hipStream_t s);
-hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, float* out_f32, uint16_t* out_bf16,
-                          hipStream_t s);
+hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, const LayerOut& o, hipStream_t s);
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
 // single token: the gate/up rows of every pick + SwiGLU + q8_1 of h, with the
 // plan selected here from the front launch's scores (`sel` given; the shared
@@ -99,8 +108,8 @@ hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out,
 // the shared expert's down rows + the combine.
 hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const int32_t* hdr_in,
                             const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s);
+hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
+                          hipStream_t s);
 // Zero-fill of `bytes` bytes (a multiple of 16) with a kernel (no memset node).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

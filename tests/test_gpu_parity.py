@@ -318,3 +318,61 @@ def test_single_token_kernel_equals_multi_token_path(shape):
     assert np.array_equal(y1[0].view(np.uint32), y2[0].view(np.uint32))
     assert np.array_equal(y2[0].view(np.uint32), y2[1].view(np.uint32))
     assert rel_l2(o1[0], o2[0]) <= 1e-5 and np.abs(o1[0] - o2[0]).max() <= 1e-3
+
+
+# ------------------------------------------------------------ layer stack
+def _check_stack(specs, xs_np, out_np, hdr_np, layers_checked):
+    """Teacher-forced: the oracle runs layer l on the device's own x_l."""
+    for l in layers_checked:
+        ref = olayer.layer_forward(specs[l], xs_np[l], keep_experts=False)
+        assert np.array_equal(hdr_np[l], ref["header"]), l
+        for t in range(xs_np.shape[1]):
+            err = np.abs(out_np[l, t] - ref["out_f32"][t])
+            assert rel_l2(out_np[l, t], ref["out_f32"][t]) <= 1e-3 and err.max() <= 1e-2, (l, t)
+    for l in range(len(specs)):   # the residual stream is exact given the device's out_l
+        assert np.array_equal(xs_np[l + 1], olayer.residual(xs_np[l], out_np[l])), l
+
+
+def _run_stack(dls, x0, n_layers):
+    c = dls[0].cfg
+    m, dim = x0.shape
+    xs = torch.empty((n_layers + 1, m, dim), dtype=torch.uint16, device="cuda")
+    xs[0] = torch.from_numpy(x0).cuda()
+    out = torch.empty((n_layers, m, dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((n_layers, m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    ws = workspace(c, m)
+    R.stack_forward(c, [d.layer for d in dls], xs, ws, out_f32=out, headers=hdr)
+    torch.cuda.synchronize()
+    return to_np_u16(xs), out.cpu().numpy(), hdr.cpu().numpy()
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_stack_forward_40_small_layers(m):
+    n = 40
+    specs = [synth.LayerSpec(TINY, seed=5, layer=l) for l in range(n)]
+    say(f"stack of {n} layers dim={TINY.dim} m={m}: generating")
+    dls = [DeviceLayer(sp) for sp in specs]
+    x0 = synth.tokens(specs[0], 3, m)
+    xs_np, out_np, hdr_np = _run_stack(dls, x0, n)
+    _check_stack(specs, xs_np, out_np, hdr_np, range(n))
+    del dls
+    torch.cuda.empty_cache()
+
+
+def test_stack_forward_40_full_size_layers():
+    """Forty dim-4096 layers resident at once (~142 GB), one token; the
+    oracle checks a sample of the layers, the residual stream every layer."""
+    n = 40
+    for k in [k for k in _LAYERS if k[0] == DS41]:
+        del _LAYERS[k]
+    torch.cuda.empty_cache()
+    specs = [synth.LayerSpec(DS41, seed=5, layer=l) for l in range(n)]
+    say(f"stack of {n} layers dim={DS41.dim}: generating ~{n * DS41.n_routed * DS41.expert_stride / 1e9:.0f} GB")
+    dls = [DeviceLayer(sp) for sp in specs]
+    torch.cuda.synchronize()
+    x0 = synth.tokens(specs[0], 3, 1)
+    xs_np, out_np, hdr_np = _run_stack(dls, x0, n)
+    say("  oracle on layers 0, 1, 20, 39")
+    _check_stack(specs, xs_np, out_np, hdr_np, (0, 1, 20, 39))
+    del dls
+    torch.cuda.empty_cache()

@@ -206,3 +206,50 @@ def test_plan_weights_are_pick_weights_in_id_order():
         m = dict(zip(picks[t], w[t]))
         assert list(plan[t]) == sorted(picks[t])
         assert [m[e] for e in plan[t]] == [m[e] for e in sorted(picks[t])]
+
+
+# ----------------------------------------------------------------- stack
+def _zeroed_experts(spec):
+    def experts(e):
+        g = synth.expert_blocks(spec, e, "gate").copy()
+        u = synth.expert_blocks(spec, e, "up").copy()
+        d = synth.expert_blocks(spec, e, "down").copy()
+        for arr, nbytes, offs in ((g, 84, (80, 81, 82, 83)), (u, 84, (80, 81, 82, 83)), (d, 110, (108, 109))):
+            v = arr.reshape(-1, nbytes)
+            for o in offs:
+                v[:, o] = 0
+        return g, u, d
+    return experts
+
+
+def test_stack_of_zero_layers_is_the_identity():
+    """Layers whose routed and shared weights are all zero add +0 to the
+    residual stream: every x_l equals x_0 bit for bit (bf16(x + 0) = x)."""
+    specs = [synth.LayerSpec(synth.SHAPE_TINY, seed=21, layer=l) for l in range(3)]
+    s = specs[0].shape
+    zero_sh = (np.zeros((s.inter, s.dim), np.uint16), np.zeros((s.inter, s.dim), np.uint16),
+               np.zeros((s.dim, s.inter), np.uint16))
+    kw = [{"experts": _zeroed_experts(sp), "shared_w": zero_sh} for sp in specs]
+    x0 = synth.tokens(specs[0], 0, 2)
+    r = layer.stack_forward(specs, x0, layer_kwargs=kw)
+    assert np.all(r["out_f32"] == 0.0)
+    for l in range(4):
+        assert np.array_equal(r["xs"][l], x0)
+
+
+def test_stack_residual_against_exact_sums():
+    """x_{l+1} is the bf16 rounding of the exact sum x_l + out_l (an f32 add
+    is exact before its rounding here: both are finite and the sum is
+    rounded once to f32, then once to bf16), and layer l routes on x_l."""
+    specs = [synth.LayerSpec(synth.SHAPE_TINY, seed=22, layer=l) for l in range(3)]
+    x0 = synth.tokens(specs[0], 0, 1)
+    r = layer.stack_forward(specs, x0)
+    for l in range(3):
+        xf = oracle.bf16_to_f32(r["xs"][l]).astype(np.float64)
+        exact = xf + r["out_f32"][l].astype(np.float64)
+        f32 = exact.astype(np.float32)          # one rounding of the exact sum
+        assert np.array_equal(r["xs"][l + 1], oracle.f32_to_bf16(f32))
+        hdr = layer.route(specs[l], r["xs"][l])["header"]
+        assert np.array_equal(r["headers"][l], hdr)
+    # the layers differ (their own seeds): the step is not one layer repeated
+    assert not np.array_equal(r["headers"][0], r["headers"][1])
