@@ -156,7 +156,7 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
                    int32_t* hdr, const Ws& w, hipStream_t s) {
   hipError_t e;
   FrontSelect sel{layer.bias, hdr};
-  if (m == 1) {   // router + q8_1 of x; then the selection, the routed and the shared gate/up in one launch
+  if (m == 1 && c.topk <= kMaxTopkM1) {   // router + q8_1; selection, routed and shared gate/up; down + combine
     if ((e = launch_front(x, 1, layer.gate_w, nullptr, nullptr, nullptr, c, w, nullptr, s)) != hipSuccess)
       return hip_fail(e, "front");
     if ((e = launch_gateup_m1(layer.experts, &sel, nullptr, x, &layer, c, w, s)) != hipSuccess)
@@ -233,7 +233,7 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
-  if (m == 1) {
+  if (m == 1 && cfg->topk <= kMaxTopkM1) {
     if ((e = launch_gateup_m1(*experts, nullptr, header, x, nullptr, *cfg, w, s)) != hipSuccess)
       return hip_fail(e, "gateup_m1");
     if ((e = launch_down_m1(*experts, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) !=

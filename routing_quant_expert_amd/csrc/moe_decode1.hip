@@ -105,7 +105,8 @@ __device__ void plan_m1(int mode, bool writer, const float* __restrict__ scores,
 
 struct GateUp1Args {
   int mode;                 // 0: select from the scores; 1: the caller's header
-  int shared_blocks;        // leading workgroups that run the shared expert's gate/up (mode 0)
+  int shared_blocks;        // leading workgroups that only run shared-expert units (mode 0 with the layer)
+  int shared_units;         // hidden units of the shared expert done here (0: none)
   moe_experts ex;
   const float* bias;
   const int32_t* hdr_in;
@@ -119,100 +120,135 @@ struct GateUp1Args {
   const uint16_t* w3;
 };
 
+// Shared-expert units per workgroup: a routed workgroup's waves 1..3 take one
+// each while wave 0 selects (that wait would otherwise leave them idle);
+// the leading shared-only workgroups take the rest, seven each (two per wave,
+// one after the other). With 384 routed and 128 shared-only workgroups at
+// dim 4096 every workgroup reads about the same number of bytes.
+constexpr int kUnitsRouted = 3;
+constexpr int kUnitsShared = 7;
+
 // ---------------------------------------------------------------------------
 template <int NSB, int SLOTS, int KPER>
 __global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
   using G = GateUpGeom<NSB>;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float gu[2][32];
+  __shared__ float sgu[2][kUnitsShared];
   __shared__ M1Plan P;
   __shared__ __align__(16) uint8_t act_lds[ActLds<NSB>::kBytes];
-  const bool shared = (int)blockIdx.x < a.shared_blocks;
-  const int u0 = blockIdx.x * front::kSharedUnitsPerBlock;
-  if (shared) {
-    front::shared_gu_units_m1(u0, a.x, a.dim, a.inter, a.w1, a.w3, gu[0], gu[1]);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool shared_only = (int)blockIdx.x < a.shared_blocks;
+  const int blk = blockIdx.x - a.shared_blocks;
+  const int routed_blocks = gridDim.x - a.shared_blocks;
+  // first shared unit of this workgroup and how many
+  const int u0 = shared_only ? kUnitsRouted * routed_blocks + kUnitsShared * (int)blockIdx.x : kUnitsRouted * blk;
+  const int nu = max(0, min(shared_only ? kUnitsShared : kUnitsRouted, a.shared_units - u0));
+  if (shared_only) {
+    for (int k = wave; k < nu; k += 4) {
+      float g, u;
+      front::shared_gu_unit(u0 + k, a.x, a.dim, a.w1, a.w3, g, u);
+      if (lane == 0) {
+        sgu[0][k] = g;
+        sgu[1][k] = u;
+      }
+    }
     __syncthreads();
   } else {
-    const int blk = blockIdx.x - a.shared_blocks;
     const int ngr = a.inter / 32;
     const int slot = blk / ngr, grp = blk % ngr;
     const int sb = threadIdx.x % NSB;
-    if (threadIdx.x < 64) {
+    if (wave == 0) {
       plan_m1<KPER>(a.mode, blk == 0, w.scores, a.bias, a.hdr_in, a.n_routed, a.topk, a.norm, a.route_scale,
                     a.hdr_out, w.plan, w.status, P);
-    } else {   // meanwhile the other waves stage the token's q8_1 activation, once for the block
+    } else {   // meanwhile the other waves stage the token's q8_1 activation and run a shared unit each
       for (int i = threadIdx.x - 64; i < ActLds<NSB>::kChunks; i += 192)
         act_piece_to_lds<NSB>(act_lds, w.xq, w.xs, w.xd, i);
+      if (wave - 1 < nu) {
+        float g, u;
+        front::shared_gu_unit(u0 + wave - 1, a.x, a.dim, a.w1, a.w3, g, u);
+        if (lane == 0) {
+          sgu[0][wave - 1] = g;
+          sgu[1][wave - 1] = u;
+        }
+      }
     }
     __syncthreads();   // also completes every wave's outstanding loads: the tile DMA below is all vmcnt sees
     const int e = P.e[slot];
-    if (e < 0) return;
-    Act A;
-    load_act_lds<NSB>(A, act_lds, sb);
-    const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
-    auto tile_src = [&](int c) -> const uint8_t* {
-      const uint64_t off = (c & 1) ? a.ex.up_off : a.ex.gate_off;
-      return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
-    };
-  #pragma unroll
-    for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
-  #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int issued = (c + SLOTS < 4 ? c + SLOTS : 4);
-      const int after = issued - c - 1;
-      if (after == 3) wait_vmcnt<3 * G::kKC>();
-      else if (after == 2) wait_vmcnt<2 * G::kKC>();
-      else if (after == 1) wait_vmcnt<1 * G::kKC>();
-      else wait_vmcnt<0>();
-      block_sync_lds();
-      const uint8_t* sl = lds + (c % SLOTS) * G::kSlotBytes;
-      const int mat = c & 1, r0 = 16 * (c >> 1);
-  #pragma unroll
-      for (int it = 0; it < G::kIters; ++it) {
-        const int i = it * 256 + threadIdx.x;
-        const bool act = i < G::kItems;
-        const int row = i / NSB;
-        double part = act ? dot_q2k(sl + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
-        part = seg_sum_f64<NSB>(part);
-        if (act && sb == 0) gu[mat][r0 + row] = (float)part;
-      }
-      if (c + SLOTS < 4) {
-        wait_lgkm0();
+    if (e >= 0) {
+      Act A;
+      load_act_lds<NSB>(A, act_lds, sb);
+      const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
+      auto tile_src = [&](int c) -> const uint8_t* {
+        const uint64_t off = (c & 1) ? a.ex.up_off : a.ex.gate_off;
+        return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
+      };
+#pragma unroll
+      for (int c = 0; c < SLOTS && c < 4; ++c)
+        dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int issued = (c + SLOTS < 4 ? c + SLOTS : 4);
+        const int after = issued - c - 1;
+        if (after == 3) wait_vmcnt<3 * G::kKC>();
+        else if (after == 2) wait_vmcnt<2 * G::kKC>();
+        else if (after == 1) wait_vmcnt<1 * G::kKC>();
+        else wait_vmcnt<0>();
         block_sync_lds();
-        dma_tile<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kSlotBytes, G::kTileChunks);
+        const uint8_t* sl = lds + (c % SLOTS) * G::kSlotBytes;
+        const int mat = c & 1, r0 = 16 * (c >> 1);
+#pragma unroll
+        for (int it = 0; it < G::kIters; ++it) {
+          const int i = it * 256 + threadIdx.x;
+          const bool act = i < G::kItems;
+          const int row = i / NSB;
+          double part = act ? dot_q2k(sl + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
+          part = seg_sum_f64<NSB>(part);
+          if (act && sb == 0) gu[mat][r0 + row] = (float)part;
+        }
+        if (c + SLOTS < 4) {
+          wait_lgkm0();
+          block_sync_lds();
+          dma_tile<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kSlotBytes, G::kTileChunks);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
-  // one SwiGLU site for both kinds of workgroup (the function is large)
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x, r = lane & 31;
-    const float gv = gu[0][r], uv = gu[1][r];
+  // One SwiGLU site for every pair the workgroup made (the function is
+  // large): lanes 0..31 the routed rows (if any), lanes 32.. (or 0.. in a
+  // shared-only workgroup) the shared units.
+  if (wave == 0) {
+    const int ebl = shared_only ? -1 : P.e[blk / (a.inter / 32)];
+    const int k = shared_only ? lane : lane - 32;
+    const bool is_shared = k >= 0 && k < nu;
+    const bool is_routed = ebl >= 0 && lane < 32;
+    const float gv = is_shared ? sgu[0][k] : (is_routed ? gu[0][lane] : 0.0f);
+    const float uv = is_shared ? sgu[1][k] : (is_routed ? gu[1][lane] : 0.0f);
     const float hv = swiglu(gv, uv, a.L);
-    if (shared) {
-      if (lane < front::kSharedUnitsPerBlock && u0 + lane < a.inter) {
-        w.sg[u0 + lane] = gv;
-        w.su[u0 + lane] = uv;
-        w.sh[u0 + lane] = bf16_rne(hv);
-      }
-      return;
+    if (is_shared) {
+      w.sg[u0 + k] = gv;
+      w.su[u0 + k] = uv;
+      w.sh[u0 + k] = bf16_rne(hv);
     }
-    const int blk = blockIdx.x - a.shared_blocks;
-    const int slot = blk / (a.inter / 32), grp = blk % (a.inter / 32);
-    float am = fabsf(hv);
-    for (int s = 16; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
-    const float d = (float)((double)am / 127.0);
-    const int q = am == 0.0f ? 0 : q8_code(hv, d);
-    int sum = q;
-    for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
-    if (lane < 32) {
-      const int64_t row = (int64_t)slot * a.inter + 32 * grp + r;
-      w.g[row] = gv;
-      w.u[row] = uv;
-      w.h[row] = hv;
-      w.hq[row] = (int8_t)q;
-      if (r == 0) w.hd[(int64_t)slot * (a.inter / 32) + grp] = __builtin_bit_cast(uint16_t, (_Float16)d);
-      if ((r & 15) == 0) w.hs[(int64_t)slot * (a.inter / 16) + 2 * grp + (r >> 4)] = sum;
+    if (!shared_only && ebl >= 0) {   // q8_1 of the 32 h values (one block), lanes 0..31
+      const int slot = blk / (a.inter / 32), grp = blk % (a.inter / 32);
+      const int r = lane & 31;
+      float am = fabsf(hv);
+      for (int s = 16; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
+      const float d = (float)((double)am / 127.0);
+      const int q = am == 0.0f ? 0 : q8_code(hv, d);
+      int sum = q;
+      for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+      if (lane < 32) {
+        const int64_t row = (int64_t)slot * a.inter + 32 * grp + r;
+        w.g[row] = gv;
+        w.u[row] = uv;
+        w.h[row] = hv;
+        w.hq[row] = (int8_t)q;
+        if (r == 0) w.hd[(int64_t)slot * (a.inter / 32) + grp] = __builtin_bit_cast(uint16_t, (_Float16)d);
+        if ((r & 15) == 0) w.hs[(int64_t)slot * (a.inter / 16) + 2 * grp + (r >> 4)] = sum;
+      }
     }
   }
 }
@@ -244,7 +280,7 @@ struct DownM1Geom {
 constexpr int kDownRows = 16;
 
 template <int NSB, bool SHARED>
-__global__ __launch_bounds__(64 * (kMaxTopk + 2)) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
+__global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
                                                  const uint16_t* __restrict__ w2, LayerOut o) {
   using G = DownM1Geom<NSB, kDownRows>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -255,19 +291,30 @@ __global__ __launch_bounds__(64 * (kMaxTopk + 2)) void k_down_m1(moe_experts ex,
   const int row0 = blockIdx.x * kDownRows;
   const int n_u = *w.plan.n_u();
   if (wave < topk) {
-    const int e = wave < n_u ? w.plan.u_expert()[wave] : -1;
+    const int e_slot = w.plan.u_expert()[wave];   // (loaded together with n_u: no dependent round trip)
+    const int e = wave < n_u ? e_slot : -1;
     if (e >= 0) {
       const int sb = lane % NSB;
       uint8_t* mine = lds + wave * G::kWaveBytes;
+      // the rows, then this expert's q8_1(h) into registers: every load is in
+      // flight at once, and one wait covers them all
       dma_wave<G::kChunks>((const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off +
                                (uint64_t)row0 * G::kRowBytes, mine);
-      // this expert's q8_1(h), staged once for the wave while its rows stream in
+      constexpr int kAP = (ActLds<NSB>::kChunks + 63) / 64;
+      u32x4 piece[kAP];
+#pragma unroll
+      for (int k = 0; k < kAP; ++k) {
+        const int i = min(lane + 64 * k, ActLds<NSB>::kChunks - 1);
+        piece[k] = *reinterpret_cast<const u32x4*>(act_piece_src<NSB>(
+            w.hq + (int64_t)wave * inter, w.hs + (int64_t)wave * (inter / 16), w.hd + (int64_t)wave * (inter / 32), i));
+      }
       uint8_t* al = act_lds[wave];
-      for (int i = lane; i < ActLds<NSB>::kChunks; i += 64)
-        act_piece_to_lds<NSB>(al, w.hq + (int64_t)wave * inter, w.hs + (int64_t)wave * (inter / 16),
-                              w.hd + (int64_t)wave * (inter / 32), i);
       wait_vmcnt<0>();
       asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < kAP; ++k)
+        if (lane + 64 * k < ActLds<NSB>::kChunks)
+          *reinterpret_cast<u32x4*>(act_piece_dst<NSB>(al, lane + 64 * k)) = piece[k];
       Act A;
       load_act_lds<NSB>(A, al, sb);
 #pragma unroll
@@ -388,7 +435,10 @@ hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const
                             const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s) {
   GateUp1Args a;
   a.mode = sel ? 0 : 1;
-  a.shared_blocks = (sel && layer) ? (c.inter + front::kSharedUnitsPerBlock - 1) / front::kSharedUnitsPerBlock : 0;
+  const int routed_blocks = c.topk * (c.inter / 32);
+  a.shared_units = (sel && layer) ? c.inter : 0;
+  const int rest = a.shared_units - kUnitsRouted * routed_blocks;
+  a.shared_blocks = rest > 0 ? (rest + kUnitsShared - 1) / kUnitsShared : 0;
   a.ex = ex;
   a.bias = sel ? sel->bias : nullptr;
   a.hdr_in = hdr_in;

@@ -183,56 +183,45 @@ __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, i
   }
 }
 
-// Shared expert gate/up of ONE token for 16 consecutive hidden units from u0,
-// four per wave one after the other (one unit's two rows in flight): the same
-// per-lane summation order and butterfly as shared_gu_rows, so the values
-// equal the multi-token ones. The pairs land in g[k], u[k] (k = unit - u0,
-// LDS); the caller applies the SwiGLU. dim <= 4096.
-constexpr int kSharedUnitsPerBlock = 16;
-
-__device__ void shared_gu_units_m1(int u0, const uint16_t* __restrict__ x, int dim, int inter,
-                                   const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, float* g,
-                                   float* u) {
+// Shared expert gate/up of ONE token for hidden unit `un`, by one wave: the
+// same per-lane summation order and butterfly as shared_gu_rows, so the
+// values equal the multi-token ones. Every lane gets (g, u). dim <= 4096.
+__device__ inline void shared_gu_unit(int un, const uint16_t* __restrict__ x, int dim,
+                                      const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, float& g,
+                                      float& u) {
   constexpr int kC = 8;   // 16-byte chunks per lane and row
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int nch = (dim + 511) / 512;
-#pragma unroll 1
-  for (int q = 0; q < 4; ++q) {   // (one unit at a time keeps the routed part's register budget)
-    const int k0 = 4 * wave + q, un = u0 + k0;
-    if (un >= inter) break;
-    uint4 av[kC], bv[kC];
+  uint4 av[kC], bv[kC];
 #pragma unroll
-    for (int c = 0; c < kC; ++c) {
-      const int k = 512 * c + 8 * lane;
-      const bool in = c < nch && k < dim;
-      av[c] = in ? load_nt16(w1 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
-      bv[c] = in ? load_nt16(w3 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
-    }
-    float pg = 0.0f, pu = 0.0f;
+  for (int c = 0; c < kC; ++c) {
+    const int k = 512 * c + 8 * lane;
+    const bool in = c < nch && k < dim;
+    av[c] = in ? load_nt16(w1 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
+    bv[c] = in ? load_nt16(w3 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
+  }
+  float pg = 0.0f, pu = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kC; ++c) {
-      const int k = 512 * c + 8 * lane;
-      if (c < nch && k < dim) {
-        float fa[8], fb[8], fx[8];
-        bf16x8(av[c], fa);
-        bf16x8(bv[c], fb);
-        bf16x8(*reinterpret_cast<const uint4*>(x + k), fx);
+  for (int c = 0; c < kC; ++c) {
+    const int k = 512 * c + 8 * lane;
+    if (c < nch && k < dim) {
+      float fa[8], fb[8], fx[8];
+      bf16x8(av[c], fa);
+      bf16x8(bv[c], fb);
+      bf16x8(*reinterpret_cast<const uint4*>(x + k), fx);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pg = __builtin_fmaf(fa[j], fx[j], pg);
-          pu = __builtin_fmaf(fb[j], fx[j], pu);
-        }
+      for (int j = 0; j < 8; ++j) {
+        pg = __builtin_fmaf(fa[j], fx[j], pg);
+        pu = __builtin_fmaf(fb[j], fx[j], pu);
       }
     }
-    for (int s = 32; s >= 1; s >>= 1) {
-      pg += __shfl_xor(pg, s);
-      pu += __shfl_xor(pu, s);
-    }
-    if (lane == 0) {
-      g[k0] = pg;
-      u[k0] = pu;
-    }
   }
+  for (int s = 32; s >= 1; s >>= 1) {
+    pg += __shfl_xor(pg, s);
+    pu += __shfl_xor(pu, s);
+  }
+  g = pg;
+  u = pu;
 }
 
 }  // namespace front

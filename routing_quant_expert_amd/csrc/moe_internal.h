@@ -13,6 +13,7 @@ namespace moe {
 
 constexpr int kMaxDecodeTokens = 8;   // the union-of-experts decode path
 constexpr int kMaxTopk = 8;
+constexpr int kMaxTopkM1 = 6;   // the single-token kernels: one wave per pick + two shared-expert waves in 512 threads
 constexpr int kMaxRouted = 1024;
 constexpr int kQ2KBytes = 84;
 constexpr int kQ3KBytes = 110;

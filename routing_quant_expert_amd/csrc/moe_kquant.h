@@ -96,23 +96,29 @@ struct ActLds {
   static constexpr int kChunks = NSB * 21;   // 16-byte pieces: 16 code, 4 sum, 1 scale per sb
 };
 
-// Copies piece i (< ActLds<NSB>::kChunks) of one token's q8_1 activation.
+// Piece i (< ActLds<NSB>::kChunks) of one token's q8_1 activation: where it
+// is in global memory (codes q, per-16 sums s, scales d) and in the LDS image.
+template <int NSB>
+__device__ __forceinline__ const uint4* act_piece_src(const int8_t* q, const int32_t* s, const uint16_t* d, int i) {
+  if (i < NSB * 16) return reinterpret_cast<const uint4*>(q + 16 * i);
+  if (i < NSB * 20) return reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(s) + 16 * (i - NSB * 16));
+  return reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(d) + 16 * (i - NSB * 20));
+}
+template <int NSB>
+__device__ __forceinline__ uint4* act_piece_dst(uint8_t* lds, int i) {
+  using AL = ActLds<NSB>;
+  if (i < NSB * 16) return reinterpret_cast<uint4*>(lds + (i >> 4) * AL::kCodeStride + 16 * (i & 15));
+  if (i < NSB * 20) {
+    const int j = i - NSB * 16;
+    return reinterpret_cast<uint4*>(lds + AL::kQ + (j >> 2) * AL::kQStride + 16 * (j & 3));
+  }
+  return reinterpret_cast<uint4*>(lds + AL::kD + 16 * (i - NSB * 20));
+}
+// Copies piece i of one token's q8_1 activation into the LDS image.
 template <int NSB>
 __device__ __forceinline__ void act_piece_to_lds(uint8_t* lds, const int8_t* q, const int32_t* s, const uint16_t* d,
                                                  int i) {
-  using AL = ActLds<NSB>;
-  if (i < NSB * 16) {
-    *reinterpret_cast<uint4*>(lds + (i >> 4) * AL::kCodeStride + 16 * (i & 15)) =
-        *reinterpret_cast<const uint4*>(q + 16 * i);
-  } else if (i < NSB * 20) {
-    const int j = i - NSB * 16;
-    *reinterpret_cast<uint4*>(lds + AL::kQ + (j >> 2) * AL::kQStride + 16 * (j & 3)) =
-        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(s) + 16 * j);
-  } else {
-    const int j = i - NSB * 20;
-    *reinterpret_cast<uint4*>(lds + AL::kD + 16 * j) =
-        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(d) + 16 * j);
-  }
+  *act_piece_dst<NSB>(lds, i) = *act_piece_src<NSB>(q, s, d, i);
 }
 
 template <int NSB>
