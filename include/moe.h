@@ -105,11 +105,12 @@ int32_t moe_header_words(const moe_cfg* cfg);
 
 /* Bytes of workspace the calls below need for up to max_m tokens (>= 1).
  * Returns 0 for an invalid or unsupported cfg. The workspace must be
- * 256-byte aligned device memory. Its control region (the `ctl` offset of
- * moe_workspace_layout, 256 bytes: the counter through which the last
- * router workgroup of moe_layer_forward learns that it is last) must be zero
- * before the first call: moe_workspace_init does that, and every call leaves
- * it zero again. The rest needs no initialisation. */
+ * 256-byte aligned device memory. Its control region (the first 256 bytes,
+ * for every m: the counter through which the last router workgroup of
+ * moe_layer_forward learns that it is last) must be zero before the first
+ * call: moe_workspace_init does that, and every call leaves it zero again.
+ * The rest needs no initialisation. A workspace sized for max_m serves every
+ * call with m <= max_m. */
 size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m);
 
 /* Zero the workspace's control region (asynchronous, on `stream`, with a
@@ -142,7 +143,8 @@ typedef struct moe_ws_layout {
   uint64_t sd;       /* f32   [max_m][dim]        shared down                      */
   uint64_t yr;       /* f32   [max_m][dim]        routed sum (layer forward)       */
   uint64_t status;   /* int32 [4] device status words (word 0: OR of MOE_STATUS_*) */
-  uint64_t ctl;      /* 256 B control words (zero between calls)                   */
+  uint64_t ctl;      /* 256 B control words (zero between calls); always offset 0  */
+  uint64_t grp;      /* int32 [max_m + 2*n_routed] grouping scratch (prefill)       */
   int32_t max_pairs; /* max_m * topk                                              */
   int32_t plan_words;
 } moe_ws_layout;
@@ -174,10 +176,26 @@ int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uin
 int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const int32_t* header,
                        const moe_experts* experts, float* y_routed, void* ws, size_t ws_bytes, void* stream);
 
-/* The whole layer for m <= 8 tokens (A1-A7): route, routed experts, shared
+/* The routed experts of any number m >= 1 of tokens (prefill, A9): the
+ * same values as moe_experts_decode (each token's output is defined exactly
+ * as at m = 1), computed with the (token, expert) pairs grouped by expert
+ * and each expert's blocks read once per 16 of its tokens: gate/up on Q2_K
+ * and down on Q3_K as int8 MFMA tiles with exact integer block sums and a
+ * float64 epilogue [moe_v41.rs, module doc; Kernels: prefill "group by
+ * expert" with int8 MFMA K-quant tiles]. Arguments and error behaviour as
+ * moe_experts_decode (x bf16 [m][dim], header int32 [m][moe_header_words],
+ * y_routed f32 [m][dim]); the workspace is sized for m. */
+int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const int32_t* header,
+                        const moe_experts* experts, float* y_routed, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer for m >= 1 tokens (A1-A7): route, routed experts, shared
  * expert (bf16 SwiGLU MLP, its SwiGLU output rounded to bf16), and
  * out = acc + shared where acc is the routed sum; the shared output is added
- * after the routed experts [moe_v41.rs, fn shared_side].
+ * after the routed experts [moe_v41.rs, fn shared_side]. m <= 8 runs the
+ * decode kernels (GEMVs over the union of the picked experts); m > 8 runs
+ * the prefill kernels (router waves per 8 tokens, grouping by expert, int8
+ * MFMA expert GEMMs, bf16 MFMA shared expert, A9). Every token's logits,
+ * header, q8_1 codes and GEMV values are the same bits either way.
  *   x        bf16 [m][dim]
  *   out_bf16 bf16 [m][dim] output (round to nearest even of out_f32)
  *   out_f32  f32  [m][dim] output, may be NULL
@@ -185,7 +203,7 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
 int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
                       float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream);
 
-/* One decode step through a stack of n_layers MoE layers for m <= 8 tokens:
+/* One step through a stack of n_layers MoE layers for m >= 1 tokens:
  * for l = 0 .. n_layers-1, out_l = layer l applied to x_l exactly as
  * moe_layer_forward computes it, and x_{l+1} = bf16(f32(x_l) + out_l), the
  * residual stream between layers (the pages' step runs the layers back to
@@ -227,6 +245,8 @@ int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, floa
 #define MOE_K_GATEUP 1
 #define MOE_K_DOWN 2
 #define MOE_K_ROUTER 3
+#define MOE_K_SHARED_GU 4    /* prefill: the shared expert's gate/up GEMM with its SwiGLU */
+#define MOE_K_SHARED_DOWN 5  /* prefill: the shared expert's down GEMM                    */
 int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end);
 
 

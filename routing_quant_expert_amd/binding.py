@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_STATUS_MISS = 1
 MOE_STATUS_NAN_KEY = 2
 MOE_STATUS_BAD_PICK = 4
-MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER = 1, 2, 3
+MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER, MOE_K_SHARED_GU, MOE_K_SHARED_DOWN = 1, 2, 3, 4, 5
 
 
 class MoeError(RuntimeError):
@@ -43,7 +43,7 @@ class Layer(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("total", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u",
                                                  "h", "hq", "hd", "hs", "y", "sg", "su", "sh", "sd", "yr",
-                                                 "status", "ctl")] + [("max_pairs", ctypes.c_int32),
+                                                 "status", "ctl", "grp")] + [("max_pairs", ctypes.c_int32),
                                                                ("plan_words", ctypes.c_int32)]
 
 
@@ -67,6 +67,8 @@ def lib():
                                        ctypes.c_size_t, _VP]
         L.moe_experts_decode.argtypes = [ctypes.POINTER(Cfg), _VP, ctypes.c_int32, _VP, ctypes.POINTER(Experts),
                                          _VP, _VP, ctypes.c_size_t, _VP]
+        L.moe_experts_prefill.argtypes = [ctypes.POINTER(Cfg), _VP, ctypes.c_int32, _VP, ctypes.POINTER(Experts),
+                                          _VP, _VP, ctypes.c_size_t, _VP]
         L.moe_layer_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), _VP, ctypes.c_int32, _VP, _VP,
                                         _VP, _VP, ctypes.c_size_t, _VP]
         L.moe_stack_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), ctypes.c_int32, _VP,
@@ -130,6 +132,12 @@ def experts_decode(cfg: Cfg, x, header, experts: Experts, y_routed, ws, stream=N
     m = x.shape[0]
     _check(lib().moe_experts_decode(ctypes.byref(cfg), _ptr(x), m, _ptr(header), ctypes.byref(experts),
                                     _ptr(y_routed), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def experts_prefill(cfg: Cfg, x, header, experts: Experts, y_routed, ws, stream=None):
+    m = x.shape[0]
+    _check(lib().moe_experts_prefill(ctypes.byref(cfg), _ptr(x), m, _ptr(header), ctypes.byref(experts),
+                                     _ptr(y_routed), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def layer_forward(cfg: Cfg, layer: Layer, x, out_bf16, ws, out_f32=None, header=None, stream=None):

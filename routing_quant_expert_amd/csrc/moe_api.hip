@@ -8,12 +8,13 @@
 
 #include "moe_internal.h"
 #include "moe_math.h"
+#include "moe_prefill.h"
 
 namespace moe {
 namespace {
 
 thread_local std::string g_err;
-constexpr int kTimedKernels = 4;   // MOE_K_* ids 1..3
+constexpr int kTimedKernels = 6;   // MOE_K_* ids 1..5
 thread_local hipEvent_t g_ev_begin[kTimedKernels] = {};
 thread_local hipEvent_t g_ev_end[kTimedKernels] = {};
 
@@ -76,6 +77,7 @@ int check_experts(const moe_experts* ex) {
 bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
   const uint64_t m = max_m, P = (uint64_t)max_m * c.topk;
   uint64_t t = 0;
+  L->ctl = take(t, 256);   // first, so that its place does not depend on m
   L->xq = take(t, m * c.dim);
   L->xd = take(t, m * (c.dim / 32) * 2);
   L->xs = take(t, m * (c.dim / 16) * 4);
@@ -96,7 +98,7 @@ bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
   L->sd = take(t, m * c.dim * 4);
   L->yr = take(t, m * c.dim * 4);
   L->status = take(t, 16 + m * (1 + 3 * c.topk) * 4);   // status words, then a header scratch
-  L->ctl = take(t, 256);
+  L->grp = take(t, (m + 2 * (uint64_t)c.n_routed) * 4);
   L->total = t;
   L->max_pairs = (int32_t)P;
   return true;
@@ -153,9 +155,19 @@ int check_layer(const moe_layer* layer) {
 
 // One layer's launches on `s` (A1-A7), the result to `o`.
 int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, int m, const LayerOut& o,
-                   int32_t* hdr, const Ws& w, hipStream_t s) {
+                   int32_t* hdr, const Ws& w, int32_t* grp, hipStream_t s) {
   hipError_t e;
   FrontSelect sel{layer.bias, hdr};
+  if (m > kMaxDecodeTokens) {   // prefill
+    if ((e = launch_router_pf(x, m, layer.gate_w, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router_pf");
+    if ((e = launch_select(layer.bias, m, c, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
+    if ((e = launch_group(hdr, m, c, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
+    if ((e = launch_gateup_pf(layer.experts, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(layer.experts, m, c, w, s)) != hipSuccess) return hip_fail(e, "down_pf");
+    if ((e = launch_shared_pf(x, m, layer, c, w, s)) != hipSuccess) return hip_fail(e, "shared_pf");
+    if ((e = launch_combine(m, c, w, w.sd, o, s)) != hipSuccess) return hip_fail(e, "combine");
+    return MOE_OK;
+  }
   if (m == 1 && c.topk <= kMaxTopkM1) {   // router + q8_1; selection, routed and shared gate/up; down + combine
     if ((e = launch_front(x, 1, layer.gate_w, nullptr, nullptr, nullptr, c, w, nullptr, s)) != hipSuccess)
       return hip_fail(e, "front");
@@ -249,18 +261,41 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   return MOE_OK;
 }
 
+int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const int32_t* header,
+                        const moe_experts* experts, float* y_routed, void* ws, size_t ws_bytes, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!x || !header || !y_routed) return fail(MOE_EINVAL, "x, header and y_routed must be non-NULL%s%lld");
+  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
+  if (int r = check_experts(experts)) return r;
+  moe_ws_layout L;
+  if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
+  Ws w = ws_view(ws, L, *cfg, m);
+  int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if ((e = launch_group(header, m, *cfg, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
+  if ((e = launch_gateup_pf(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+  if ((e = launch_down_pf(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down_pf");
+  if ((e = launch_combine(m, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) != hipSuccess)
+    return hip_fail(e, "combine");
+  return MOE_OK;
+}
+
 int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
                       float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
   if (!x || !out_bf16) return fail(MOE_EINVAL, "x and out_bf16 must be non-NULL%s%lld");
   if (int r = check_layer(layer)) return r;
-  if (m < 1 || m > kMaxDecodeTokens) return fail(MOE_EINVAL, "decode needs 1 <= m <= 8%s (m %lld)", "", m);
+  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
   if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
   moe_ws_layout L;
   if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
   Ws w = ws_view(ws, L, *cfg, m);
   LayerOut o{out_f32, out_bf16, nullptr, nullptr};
-  return layer_launches(*cfg, *layer, x, m, o, header ? header : w.status + 4, w, (hipStream_t)stream);
+  int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
+  return layer_launches(*cfg, *layer, x, m, o, header ? header : w.status + 4, w, grp, (hipStream_t)stream);
 }
 
 int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_layers, uint16_t* xs, int32_t m,
@@ -268,7 +303,7 @@ int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_lay
   if (int r = check_cfg(cfg)) return r;
   if (!layers || !xs) return fail(MOE_EINVAL, "layers and xs must be non-NULL%s%lld");
   if (n_layers < 1) return fail(MOE_EINVAL, "n_layers must be >= 1%s (n_layers %lld)", "", n_layers);
-  if (m < 1 || m > kMaxDecodeTokens) return fail(MOE_EINVAL, "decode needs 1 <= m <= 8%s (m %lld)", "", m);
+  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
   if (!a16(xs) || ((int64_t)m * cfg->dim * 2) % 16) return fail(MOE_EINVAL, "xs must be 16-byte aligned%s%lld");
   for (int l = 0; l < n_layers; ++l)
     if (int r = check_layer(&layers[l])) return r;
@@ -277,10 +312,11 @@ int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_lay
   Ws w = ws_view(ws, L, *cfg, m);
   const int64_t row = (int64_t)m * cfg->dim;
   const int hw = 1 + 3 * cfg->topk;
+  int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
   for (int l = 0; l < n_layers; ++l) {
     LayerOut o{out_f32 ? out_f32 + l * row : nullptr, nullptr, xs + l * row, xs + (l + 1) * row};
     int32_t* hdr = headers ? headers + (int64_t)l * m * hw : w.status + 4;
-    if (int r = layer_launches(*cfg, layers[l], xs + l * row, m, o, hdr, w, (hipStream_t)stream)) return r;
+    if (int r = layer_launches(*cfg, layers[l], xs + l * row, m, o, hdr, w, grp, (hipStream_t)stream)) return r;
   }
   return MOE_OK;
 }

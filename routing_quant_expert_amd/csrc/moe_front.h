@@ -41,8 +41,8 @@ __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* _
 }
 
 // ---------------------------------------------------------------------------
-// Router GEMV + scores. One wave64 per expert row, all tokens of the call.
-// Lane l accumulates positions 512*i + 8*l + j (i ascending, j = 0..7) in
+// Router GEMV + scores. One wave64 per expert row, for the tokens
+// [t_lo, t_hi) of the call (default: all of them). Lane l accumulates positions 512*i + 8*l + j (i ascending, j = 0..7) in
 // f32 (product, then add: every bf16 x bf16 product is exact), then the 64
 // partials combine as p += shfl_xor(p, s) for s = 32..1 and lane 0 holds the
 // logit. This per-row order is the same for every m, so a token's logits
@@ -53,14 +53,16 @@ constexpr int kLoadAhead = 8;   // 16-byte chunks per lane kept in flight by one
 
 __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int dim,
                             const uint16_t* __restrict__ gate_w, int n_routed, float temp, float* __restrict__ logits,
-                            float* __restrict__ scores, float* __restrict__ logits_out) {
+                            float* __restrict__ scores, float* __restrict__ logits_out, int t_lo = 0,
+                            int t_hi = -1) {
   const int e = blk * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (e >= n_routed) return;
   const uint16_t* wr = gate_w + (int64_t)e * dim;
   const int nch = (dim + 511) / 512;
-  for (int t0 = 0; t0 < m; t0 += kRouterTok) {
-    const int nt = min(kRouterTok, m - t0);
+  if (t_hi < 0) t_hi = m;
+  for (int t0 = t_lo; t0 < t_hi; t0 += kRouterTok) {
+    const int nt = min(kRouterTok, t_hi - t0);
     float p[kRouterTok];
 #pragma unroll
     for (int t = 0; t < kRouterTok; ++t) p[t] = 0.0f;

@@ -1,0 +1,290 @@
+"""GPU parity of the prefill path (m > 8 tokens: grouping by expert, int8
+MFMA expert GEMMs, bf16 MFMA shared expert) against the oracle, through the
+C ABI. The bar is the decode path's: router logits, headers, q8_1 codes and
+scales bit-exact; every GEMV value the correctly rounded exact dot product
+(or its neighbour where the oracle flags a near-midpoint); the layer output
+within rel-L2 1e-3 and max-abs 1e-2. Each token is defined exactly as at
+m = 1, so the oracle checks sampled tokens of the large batches."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routing_quant_expert_amd as R
+import synth
+from oracle import layer as olayer
+from synth.device import DeviceLayer
+from tests.gpu_helpers import f32_accept, host_spec, plan_tables, rel_l2, say, to_np_u16, workspace, ws_array
+
+pytestmark = pytest.mark.gpu
+
+TINY, DS41 = synth.SHAPE_TINY, synth.SHAPE_DS41
+_DL = {}
+
+
+def dev_layer(shape, seed=1, zipf=False):
+    key = (shape, seed, zipf)
+    if key not in _DL:
+        if shape == DS41:
+            for k in [k for k in _DL if k[0] == DS41]:
+                del _DL[k]
+            torch.cuda.empty_cache()
+        say(f"generating layer {shape.dim}x{shape.inter} seed {seed} zipf={zipf} on the device")
+        _DL[key] = DeviceLayer(host_spec(shape, seed, zipf=zipf))
+        torch.cuda.synchronize()
+    return _DL[key]
+
+
+def _ws_views(ws, c, m, shape):
+    L = R.workspace_layout(c, m)
+    P, inter, dim = L["max_pairs"], shape.inter, shape.dim
+    v = {"tab": plan_tables(ws, L, m, shape.topk)}
+    for name, dt, n in (("g", np.float32, inter), ("u", np.float32, inter), ("h", np.float32, inter),
+                        ("hq", np.int8, inter), ("hd", np.uint16, inter // 32), ("hs", np.int32, inter // 16),
+                        ("y", np.float32, dim)):
+        v[name] = ws_array(ws, L, name, dt, P * n).reshape(P, n)
+    v["L"] = L
+    return v
+
+
+def _check_plan(tab, hdr, m, topk, n_routed):
+    """Structure of the plan at any size: pairs sorted by (expert, token),
+    every valid pick of every token present once, tok_pairs pointing back."""
+    status, picks, wts, plan = oracle.header_fields(hdr, topk)
+    n = tab["n_pairs"]
+    assert n == m * topk
+    pe, pt = tab["pair_expert"][:n], tab["pair_tok"][:n]
+    key = pe.astype(np.int64) * (m + 1) + pt
+    assert np.all(np.diff(key) > 0)
+    assert tab["n_u"] == len(np.unique(pe))
+    ue, uf, un = tab["u_expert"][:tab["n_u"]], tab["u_first"][:tab["n_u"]], tab["u_npairs"][:tab["n_u"]]
+    assert np.array_equal(ue, np.unique(pe)) and np.array_equal(np.cumsum(un) - un, uf) and un.sum() == n
+    for t in range(m):
+        ids = plan[t]
+        order = np.argsort(picks[t], kind="stable")
+        for k in range(topk):
+            p = tab["tok_pairs"][t][k]
+            assert pe[p] == ids[k] and pt[p] == t
+            assert tab["pair_w"][p] == wts[t][order][k]
+
+
+def _check_tokens(spec, x_np, toks, v, out_f32, want_key, hdr_dev):
+    """Oracle on the sampled tokens: every pair's GEMV values and q8_1, then the output."""
+    accepted = 0
+    tab = v["tab"]
+    toks = list(toks)
+    ref = olayer.layer_forward(spec, x_np[toks], with_shared=(want_key == "out_f32"))
+    for i, t in enumerate(toks):
+        assert np.array_equal(hdr_dev[t], ref["header"][i]), t
+        for k, e in enumerate(ref["tok"][i]["ids"]):
+            p = int(tab["tok_pairs"][t][k])
+            assert tab["pair_expert"][p] == e and tab["pair_tok"][p] == t
+            ex = ref["tok"][i]["experts"][k]
+            acc = f32_accept(v["g"][p], ex["g"], ex["near_g"], f"g tok {t} e {e}")
+            acc += f32_accept(v["u"][p], ex["u"], ex["near_u"], f"u tok {t} e {e}")
+            if acc == 0:
+                assert np.array_equal(v["h"][p].view(np.uint32), ex["h"].view(np.uint32)), (t, e)
+                assert np.array_equal(v["hq"][p], ex["hq"]) and np.array_equal(v["hd"][p], ex["hd16"]), (t, e)
+                assert np.array_equal(v["hs"][p], ex["hq"].reshape(-1, 16).astype(np.int32).sum(axis=1))
+            acc += f32_accept(v["y"][p], ex["y"], ex["near_y"], f"y tok {t} e {e}")
+            accepted += acc
+        want = ref[want_key][i]
+        err = np.abs(out_f32[t] - want)
+        assert rel_l2(out_f32[t], want) <= 1e-3 and err.max() <= 1e-2, (t, rel_l2(out_f32[t], want), err.max())
+    if accepted:
+        say(f"  {accepted} GEMV outputs took the other correct rounding next to an f32 midpoint")
+
+
+def _run_layer(dl, x_np):
+    c, shape = dl.cfg, dl.spec.shape
+    m = x_np.shape[0]
+    x = torch.from_numpy(x_np).cuda()
+    ws = workspace(c, m)
+    out = torch.empty((m, shape.dim), dtype=torch.uint16, device="cuda")
+    out32 = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr)
+    torch.cuda.synchronize()
+    return ws, out32.cpu().numpy(), to_np_u16(out), hdr.cpu().numpy()
+
+
+@pytest.mark.parametrize("m", [9, 37, 512])
+def test_prefill_layer_small_shape_every_token(m):
+    """dim 512: the oracle checks every token and every pair."""
+    dl = dev_layer(TINY, zipf=True)
+    spec, c, shape = dl.spec, dl.cfg, dl.spec.shape
+    x_np = synth.tokens(spec, 1000, m)
+    say(f"prefill layer_forward dim={shape.dim} m={m}")
+    ws, out32, outb, hdr = _run_layer(dl, x_np)
+    lg = oracle.router_logits(x_np, synth.gate_w(spec))
+    L = R.workspace_layout(c, m)
+    got_lg = ws_array(ws, L, "logits", np.float32, m * shape.n_routed).reshape(m, -1)
+    assert np.array_equal(got_lg.view(np.uint32), lg.view(np.uint32))
+    want_hdr, _ = oracle.select(shape, lg, synth.bias(spec))
+    assert np.array_equal(hdr, want_hdr)
+    v = _ws_views(ws, c, m, shape)
+    _check_plan(v["tab"], hdr, m, shape.topk, shape.n_routed)
+    _check_tokens(spec, x_np, range(m), v, out32, "out_f32", hdr)
+    assert np.array_equal(outb, oracle.f32_to_bf16(out32))
+    xq = ws_array(ws, L, "xq", np.int8, m * shape.dim).reshape(m, -1)
+    xd = ws_array(ws, L, "xd", np.uint16, m * shape.dim // 32).reshape(m, -1)
+    for t in range(0, m, max(1, m // 16)):
+        q, d = oracle.q8_1(oracle.bf16_to_f32(x_np[t]))
+        assert np.array_equal(xq[t], q) and np.array_equal(xd[t], d)
+
+
+def test_prefill_full_size_zipf_512():
+    """The dim-4096 workload: 512 tokens, Zipf-skewed bias. Headers of all
+    tokens bit-exact; the plan's structure checked whole; the oracle checks
+    the GEMV values and outputs of a sample of tokens."""
+    dl = dev_layer(DS41, zipf=True)
+    spec, c, shape = dl.spec, dl.cfg, dl.spec.shape
+    m = 512
+    x_np = synth.tokens(spec, 0, m)
+    say("prefill layer_forward dim=4096 m=512")
+    ws, out32, outb, hdr = _run_layer(dl, x_np)
+    lg = oracle.router_logits(x_np, synth.gate_w(spec))
+    want_hdr, _ = oracle.select(shape, lg, synth.bias(spec))
+    assert np.array_equal(hdr, want_hdr)
+    v = _ws_views(ws, c, m, shape)
+    _check_plan(v["tab"], hdr, m, shape.topk, shape.n_routed)
+    counts = v["tab"]["u_npairs"][:v["tab"]["n_u"]]
+    say(f"  {v['tab']['n_u']} experts used, largest group {counts.max()} tokens")
+    # the sample includes the tokens of the largest group's first and last pair
+    big = int(np.argmax(counts))
+    f0 = int(v["tab"]["u_first"][big])
+    toks = sorted({0, 1, 255, 511, int(v["tab"]["pair_tok"][f0]), int(v["tab"]["pair_tok"][f0 + counts[big] - 1])})
+    say(f"  oracle on tokens {toks}")
+    _check_tokens(spec, x_np, toks, v, out32, "out_f32", hdr)
+    assert np.array_equal(outb, oracle.f32_to_bf16(out32))
+    assert np.all(np.isfinite(out32))
+
+
+def test_prefill_equals_decode_path_per_token():
+    """Tokens in a 512-token prefill give the decode kernels' values: headers
+    and routed GEMV values bitwise, the layer output (shared expert summed
+    in another order) within the tolerance."""
+    dl = dev_layer(DS41, zipf=True)
+    c, shape = dl.cfg, dl.spec.shape
+    x_np = synth.tokens(dl.spec, 0, 512)
+    ws, out32, _, hdr = _run_layer(dl, x_np)
+    v = _ws_views(ws, c, 512, shape)
+    for t0, m in ((0, 1), (100, 8)):
+        ws_d, out_d, _, hdr_d = _run_layer(dl, x_np[t0:t0 + m].copy())
+        assert np.array_equal(hdr_d, hdr[t0:t0 + m])
+        vd = _ws_views(ws_d, c, m, shape)
+        for t in range(m):
+            for k in range(shape.topk):
+                p, pd = int(v["tab"]["tok_pairs"][t0 + t][k]), int(vd["tab"]["tok_pairs"][t][k])
+                for name in ("g", "u", "y"):
+                    a, b = v[name][p], vd[name][pd]
+                    d = a.view(np.uint32).astype(np.int64) - b.view(np.uint32).astype(np.int64)
+                    assert np.abs(d).max() <= 1, (name, t0 + t, k)   # equal, or both sides of a midpoint
+            err = np.abs(out32[t0 + t] - out_d[t])
+            assert rel_l2(out32[t0 + t], out_d[t]) <= 1e-3 and err.max() <= 1e-2
+
+
+def test_prefill_hot_expert_spans_many_chunks():
+    """A bias that makes every token pick expert 7: its group holds all m
+    tokens (several 16-token passes over its blocks)."""
+    dl = dev_layer(TINY)
+    spec, c, shape = dl.spec, dl.cfg, dl.spec.shape
+    m = 70
+    b = synth.bias(spec).copy()
+    b[7] = 50.0
+    bias_dev = torch.from_numpy(b).cuda()
+    layer = R.Layer(dl.gate_w.data_ptr(), bias_dev.data_ptr(), dl.experts, dl.sh_w1.data_ptr(),
+                    dl.sh_w3.data_ptr(), dl.sh_w2.data_ptr())
+    x_np = synth.tokens(spec, 500, m)
+    x = torch.from_numpy(x_np).cuda()
+    ws = workspace(c, m)
+    out = torch.empty((m, shape.dim), dtype=torch.uint16, device="cuda")
+    out32 = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    R.layer_forward(c, layer, x, out, ws, out_f32=out32, header=hdr)
+    torch.cuda.synchronize()
+    hdr_np, out_np = hdr.cpu().numpy(), out32.cpu().numpy()
+    assert np.all(hdr_np[:, 1] == 7)
+    v = _ws_views(ws, c, m, shape)
+    tab = v["tab"]
+    u7 = list(tab["u_expert"][:tab["n_u"]]).index(7)
+    assert tab["u_npairs"][u7] == m
+    ref = olayer.layer_forward(spec, x_np, bias=b)
+    assert np.array_equal(hdr_np, ref["header"])
+    for t in range(m):
+        want = ref["out_f32"][t]
+        assert rel_l2(out_np[t], want) <= 1e-3 and np.abs(out_np[t] - want).max() <= 1e-2, t
+        k = list(ref["tok"][t]["ids"]).index(7)
+        p = int(tab["tok_pairs"][t][k])
+        ex = ref["tok"][t]["experts"][k]
+        f32_accept(v["y"][p], ex["y"], ex["near_y"], f"y tok {t}")
+
+
+@pytest.mark.parametrize("shape,m", [(TINY, 40), (DS41, 64)])
+def test_experts_prefill_matches_oracle(shape, m):
+    dl = dev_layer(shape, zipf=True)
+    spec, c = dl.spec, dl.cfg
+    x_np = synth.tokens(spec, 77, m)
+    lg = oracle.router_logits(x_np, synth.gate_w(spec))
+    hdr_np, _ = oracle.select(shape, lg, synth.bias(spec))
+    ws = workspace(c, m)
+    y = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+    say(f"experts_prefill dim={shape.dim} m={m}")
+    R.experts_prefill(c, torch.from_numpy(x_np).cuda(), torch.from_numpy(hdr_np).cuda(), dl.experts, y, ws)
+    torch.cuda.synchronize()
+    v = _ws_views(ws, c, m, shape)
+    _check_plan(v["tab"], hdr_np, m, shape.topk, shape.n_routed)
+    toks = range(m) if shape == TINY else (0, 5, 31, 63)
+    _check_tokens(spec, x_np, toks, v, y.cpu().numpy(), "y_routed", hdr_np)
+
+
+def test_experts_prefill_rejects_bad_picks():
+    dl = dev_layer(TINY)
+    spec, c, shape = dl.spec, dl.cfg, dl.spec.shape
+    m = 20
+    x_np = synth.tokens(spec, 0, m)
+    lg = oracle.router_logits(x_np, synth.gate_w(spec))
+    hdr_np, _ = oracle.select(shape, lg, synth.bias(spec))
+    hdr_np = hdr_np.copy()
+    hdr_np[3, 2] = shape.n_routed    # out of range
+    hdr_np[11, 4] = hdr_np[11, 1]    # repeated
+    hdr_np[19, 1] = -5
+    ws = workspace(c, m)
+    y = torch.full((m, shape.dim), 7.0, dtype=torch.float32, device="cuda")
+    R.experts_prefill(c, torch.from_numpy(x_np).cuda(), torch.from_numpy(hdr_np).cuda(), dl.experts, y, ws)
+    torch.cuda.synchronize()
+    yy = y.cpu().numpy()
+    for t in (3, 11, 19):
+        assert np.all(yy[t] == 0), t
+    L = R.workspace_layout(c, m)
+    assert ws_array(ws, L, "status", np.int32, 1)[0] & R.MOE_STATUS_BAD_PICK
+    tab = plan_tables(ws, L, m, shape.topk)
+    assert tab["n_pairs"] == (m - 3) * shape.topk
+    ref = olayer.layer_forward(spec, x_np[[0, 12]], with_shared=False)
+    for i, t in enumerate((0, 12)):
+        assert rel_l2(yy[t], ref["y_routed"][i]) < 1e-6
+
+
+@pytest.mark.parametrize("m", [24])
+def test_stack_forward_prefill(m):
+    """Three small layers at m = 24 through the prefill kernels, teacher-forced."""
+    n = 3
+    specs = [synth.LayerSpec(TINY, seed=9, layer=l) for l in range(n)]
+    dls = [DeviceLayer(sp) for sp in specs]
+    c = dls[0].cfg
+    x0 = synth.tokens(specs[0], 3, m)
+    xs = torch.empty((n + 1, m, TINY.dim), dtype=torch.uint16, device="cuda")
+    xs[0] = torch.from_numpy(x0).cuda()
+    out = torch.empty((n, m, TINY.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((n, m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    ws = workspace(c, m)
+    R.stack_forward(c, [d.layer for d in dls], xs, ws, out_f32=out, headers=hdr)
+    torch.cuda.synchronize()
+    xs_np, out_np, hdr_np = to_np_u16(xs), out.cpu().numpy(), hdr.cpu().numpy()
+    for l in range(n):
+        ref = olayer.layer_forward(specs[l], xs_np[l], keep_experts=False)
+        assert np.array_equal(hdr_np[l], ref["header"]), l
+        for t in range(m):
+            assert rel_l2(out_np[l, t], ref["out_f32"][t]) <= 1e-3
+            assert np.abs(out_np[l, t] - ref["out_f32"][t]).max() <= 1e-2
+        assert np.array_equal(xs_np[l + 1], olayer.residual(xs_np[l], out_np[l])), l

@@ -34,11 +34,14 @@ def test_workspace_queries():
     n1, n8 = R.workspace_bytes(c, 1), R.workspace_bytes(c, 8)
     assert 0 < n1 < n8
     L = R.workspace_layout(c, 8)
-    offs = [L[k] for k in ("xq", "xd", "xs", "logits", "scores", "plan", "g", "u", "h", "hq", "hd", "hs", "y",
-                           "sg", "su", "sh", "sd", "yr", "status", "ctl")]
+    offs = [L[k] for k in ("ctl", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u", "h", "hq", "hd", "hs",
+                           "y", "sg", "su", "sh", "sd", "yr", "status", "grp")]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs) and L["total"] == n8
     assert L["max_pairs"] == 48
     assert R.header_words(c) == 19
+    # the control words sit at the start for every m, so a workspace initialised for max_m serves smaller calls
+    assert all(R.workspace_layout(c, m)["ctl"] == 0 for m in (1, 3, 8, 512))
+    assert R.workspace_bytes(c, 512) > n8 and R.workspace_layout(c, 512)["max_pairs"] == 3072
 
 
 @pytest.mark.parametrize("field,value", [("dim", 300), ("dim", 256 * 3), ("dim", 256 * 32), ("inter", 0),
@@ -88,6 +91,14 @@ def test_argument_errors_before_any_launch():
         R.experts_decode(c, x, _FakePtr(8192), R.Experts((1 << 20) + 8, 0, 0, 0, 0), _FakePtr(16384),
                          _FakePtr(1 << 24, n=1 << 30), stream=0)
     assert ei.value.code == -1
+    with pytest.raises(R.MoeError) as ei:   # prefill: misaligned expert arena
+        R.experts_prefill(c, _FakePtr(4096, shape=(64, 512)), _FakePtr(8192), R.Experts((1 << 20) + 8, 0, 0, 0, 0),
+                          _FakePtr(16384), _FakePtr(1 << 24, n=1 << 30), stream=0)
+    assert ei.value.code == -1
+    with pytest.raises(R.MoeError) as ei:   # prefill: workspace sized for fewer tokens
+        R.experts_prefill(c, _FakePtr(4096, shape=(64, 512)), _FakePtr(8192), R.Experts(1 << 20, 0, 0, 0, 0),
+                          _FakePtr(16384), _FakePtr(1 << 24, n=R.workspace_bytes(c, 63)), stream=0)
+    assert ei.value.code == -3
 
 
 def test_library_score_chain_matches_oracle_on_host():
