@@ -183,6 +183,110 @@ def stack_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def prefill_bench(args):
+    """m > 8 tokens per step through the prefill kernels: the dim-4096 layer
+    with the Zipf-skewed correction bias, m independent N(0,1) token rows."""
+    import numpy as np
+    import torch
+
+    import routing_quant_expert_amd as R
+    import synth
+    from synth.device import DeviceLayer
+
+    m = args.m
+    spec = synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed, zipf_bias=True)
+    s = spec.shape
+    print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts, Zipf bias)",
+          file=sys.stderr, flush=True)
+    dl = DeviceLayer(spec)
+    nb = max(1, min(args.tokens, 4))   # distinct batches cycled through
+    xs = torch.from_numpy(synth.tokens(spec, 0, nb * m)).cuda()
+    ws = torch.empty(R.workspace_bytes(dl.cfg, m), dtype=torch.uint8, device="cuda")
+    R.workspace_init(dl.cfg, m, ws)
+    out = torch.empty((m, s.dim), dtype=torch.uint16, device="cuda")
+    hw = R.header_words(dl.cfg)
+    hdrs = torch.empty((nb, m, hw), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i):
+        b = i % nb
+        R.layer_forward(dl.cfg, dl.layer, xs[b * m:(b + 1) * m], out, ws, header=hdrs[b])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    K = args.steps
+    every = max(1, min(args.time_every, 2))
+    nt = (K + every - 1) // every
+    kinds = (("router", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("down", R.MOE_K_DOWN),
+             ("shared_gu", R.MOE_K_SHARED_GU), ("shared_down", R.MOE_K_SHARED_DOWN))
+    evs = {k: ev.create(2 * nt) for k, _ in kinds}
+    L = R.lib()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if i % every == 0:
+            j = i // every
+            for k, which in kinds:
+                L.moe_time_next_launch(which, evs[k][2 * j], evs[k][2 * j + 1])
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms = {k: np.array([ev.elapsed_ms(evs[k][2 * j], evs[k][2 * j + 1]) for j in range(nt)]) for k, _ in kinds}
+    for k, _ in kinds:
+        ev.destroy(evs[k])
+    wall = t1 - t0
+    picks = hdrs[:, :, 1:1 + s.topk].cpu().numpy()
+    n_u = np.array([len(np.unique(p)) for p in picks])
+    counts = np.bincount(picks[0].reshape(-1), minlength=s.n_routed)
+    us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
+    nu = float(n_u.mean())
+    pairs = m * s.topk
+    kbytes = {"router": s.n_routed * s.dim * 2, "gateup": nu * 2 * s.gate_bytes, "down": nu * s.down_bytes,
+              "shared_gu": 2 * s.inter * s.dim * 2, "shared_down": s.inter * s.dim * 2}
+    kops = {"router": 2 * m * s.n_routed * s.dim, "gateup": 2 * pairs * 2 * s.inter * s.dim,
+            "down": 2 * pairs * s.dim * s.inter, "shared_gu": 2 * m * 2 * s.inter * s.dim,
+            "shared_down": 2 * m * s.dim * s.inter}
+    kern = {k: {"avg_us": us[k], "weight_bytes": kbytes[k], "gbs": kbytes[k] / us[k] / 1e3,
+                "tops": kops[k] / us[k] / 1e6} for k, _ in kinds}
+    launch_bytes = kbytes["gateup"]
+    k_avg = us["gateup"] * 1e-6
+    achieved = launch_bytes / k_avg / 1e9
+    step_bytes = sum(kbytes.values())
+    res = {
+        "metric": "MoE-layer prefill tokens/s at m=512 and % of HBM peak on expert-weight bytes",
+        "value": K * m / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"moe_layer_prefill_m{m}_zipf_dim4096_inter2048_e384_top6", "dim": s.dim,
+                   "inter": s.inter, "n_routed": s.n_routed, "topk": s.topk, "m": m, "batches_cycled": nb,
+                   "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_gateup_pf",
+                     "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
+                     "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
+                                           float(np.percentile(k_ms["gateup"], 90) * 1e3)],
+                     "int8_mfma_tops": kops["gateup"] / k_avg / 1e12, "int8_mfma_peak_tops": 5000.0},
+        "detail": {"kernels": kern, "union_experts_mean": nu, "largest_group": int(counts.max()),
+                   "step_weight_bytes": step_bytes, "step_gbs": step_bytes / (wall / K) / 1e9,
+                   "timed_kernels_us": sum(us.values()), "expert_kernels_gbs":
+                       (kbytes["gateup"] + kbytes["down"]) / (us["gateup"] + us["down"]) / 1e3},
+    }
+    if not args.no_cpu:
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,8 +297,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's timed kernel")
-    ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernel; 2..8: the "
-                                                     "multi-token path on correlated rows)")
+    ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernels; 2..8: the "
+                                                     "multi-token decode path on correlated rows; > 8: the "
+                                                     "prefill path, Zipf-skewed bias)")
     ap.add_argument("--layers", type=int, default=1,
                     help="decode through a stack of this many layers per step (each its own seeded weights)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -214,9 +319,13 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
               f"of the layer is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
-    if not 1 <= args.m <= 8:
-        print("bench.py: --m must be 1..8", file=sys.stderr)
+    if args.m < 1:
+        print("bench.py: --m must be >= 1", file=sys.stderr)
         sys.exit(2)
+    if args.m > 8:
+        import torch
+        torch.cuda.set_device(0)
+        return prefill_bench(args)
 
     import numpy as np
     import torch
