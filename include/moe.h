@@ -145,6 +145,8 @@ typedef struct moe_ws_layout {
   uint64_t status;   /* int32 [4] device status words (word 0: OR of MOE_STATUS_*) */
   uint64_t ctl;      /* 256 B control words (zero between calls); always offset 0  */
   uint64_t grp;      /* int32 [max_m + 2*n_routed] grouping scratch (prefill)       */
+  uint64_t xd64;     /* f64   [max_m][dim/32]     q8_1 scales of x (prefill)       */
+  uint64_t hd64;     /* f64   [pairs][inter/32]   q8_1 scales of h (prefill)       */
   int32_t max_pairs; /* max_m * topk                                              */
   int32_t plan_words;
 } moe_ws_layout;

@@ -43,7 +43,7 @@ class Layer(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("total", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u",
                                                  "h", "hq", "hd", "hs", "y", "sg", "su", "sh", "sd", "yr",
-                                                 "status", "ctl", "grp")] + [("max_pairs", ctypes.c_int32),
+                                                 "status", "ctl", "grp", "xd64", "hd64")] + [("max_pairs", ctypes.c_int32),
                                                                ("plan_words", ctypes.c_int32)]
 
 

@@ -21,6 +21,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-command-line-argument"]
 SOURCES = ["moe_api.hip", "moe_route.hip", "moe_experts.hip", "moe_decode1.hip", "moe_prefill.hip"]
+# the prefill kernels consume MFMA results in VALU code: keep them in VGPRs (no accvgpr copies)
+EXTRA = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd, verbose):
@@ -40,7 +42,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     synth_obj = os.path.join(BUILD, "synth_device.o")
     cmds.append([HIPCC, *FLAGS, "-c", SYNTH_SRC, "-o", synth_obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:

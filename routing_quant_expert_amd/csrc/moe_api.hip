@@ -99,6 +99,8 @@ bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
   L->yr = take(t, m * c.dim * 4);
   L->status = take(t, 16 + m * (1 + 3 * c.topk) * 4);   // status words, then a header scratch
   L->grp = take(t, (m + 2 * (uint64_t)c.n_routed) * 4);
+  L->xd64 = take(t, m * (c.dim / 32) * 8);
+  L->hd64 = take(t, P * (c.inter / 32) * 8);
   L->total = t;
   L->max_pairs = (int32_t)P;
   return true;
@@ -127,6 +129,8 @@ Ws ws_view(void* ws, const moe_ws_layout& L, const moe_cfg& c, int max_m) {
   w.yr = reinterpret_cast<float*>(b + L.yr);
   w.status = reinterpret_cast<int32_t*>(b + L.status);
   w.ctl = reinterpret_cast<Ctl*>(b + L.ctl);
+  w.xd64 = reinterpret_cast<double*>(b + L.xd64);
+  w.hd64 = reinterpret_cast<double*>(b + L.hd64);
   return w;
 }
 
@@ -274,7 +278,7 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
   int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  if ((e = launch_router_pf(x, m, nullptr, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
   if ((e = launch_group(header, m, *cfg, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
   if ((e = launch_gateup_pf(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
   if ((e = launch_down_pf(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down_pf");

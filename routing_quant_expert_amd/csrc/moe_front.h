@@ -25,7 +25,7 @@ __device__ inline void bf16x8(uint4 v, float (&f)[8]) {
 // fp16(d), plus the sums of 16 consecutive codes (the q8_1 sum field is not
 // used; the GEMV epilogues need per-16 sums of the codes).
 __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* __restrict__ xq,
-                              uint16_t* __restrict__ xd, int32_t* __restrict__ xs) {
+                              uint16_t* __restrict__ xd, int32_t* __restrict__ xs, double* __restrict__ xd64 = nullptr) {
   const int64_t i = (int64_t)blk * 256 + threadIdx.x;   // m*dim is a multiple of 256
   float v = bf16_f32(x[i]);
   float a = fabsf(v);
@@ -36,7 +36,10 @@ __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* _
   int sum = q;
   for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
   const int lane32 = threadIdx.x & 31;
-  if (lane32 == 0) xd[i >> 5] = fp16_bits(d);
+  if (lane32 == 0) {
+    xd[i >> 5] = fp16_bits(d);
+    if (xd64) xd64[i >> 5] = (double)__builtin_bit_cast(_Float16, fp16_bits(d));
+  }
   if ((lane32 & 15) == 0) xs[i >> 4] = sum;
 }
 

@@ -67,6 +67,8 @@ struct Ws {
   float* yr;
   int32_t* status;
   Ctl* ctl;
+  double* xd64;   // prefill: the q8_1 scales of x as float64 [max_m][dim/32]
+  double* hd64;   // prefill: the q8_1 scales of h as float64 [pairs][inter/32]
 };
 
 bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L);

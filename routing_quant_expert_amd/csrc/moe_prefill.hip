@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_router_pf(const uint16_t* __restrict__ 
     return;
   }
   const int qb = (bx - router_blocks) * gridDim.y + blockIdx.y;
-  if (qb < (int)((int64_t)m * dim / 256)) front::quant_x_block(qb, x, w.xq, w.xd, w.xs);
+  if (qb < (int)((int64_t)m * dim / 256)) front::quant_x_block(qb, x, w.xq, w.xd, w.xs, w.xd64);
 }
 
 // ---------------------------------------------------------------------------
@@ -190,17 +190,23 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
 
 // ---------------------------------------------------------------------------
 // Gate/up on Q2_K with int8 MFMA + clamped SwiGLU + q8_1 of h.
-// Workgroup = (distinct expert u, 32 hidden units). Waves: (gate | up) x
-// (first | second half of the q8_1 blocks of k); each wave computes its 32
-// rows for up to 16 of the expert's tokens at a time, the halves are added
-// in float64 through LDS, then the SwiGLU and the q8_1 of h (32 units = one
-// q8_1 block) are written per pair.
+// Workgroup = (distinct expert u, 64 hidden units): 128 weight rows (the 64
+// gate rows, then the 64 up rows), a wave per 32 rows over the whole k, up
+// to 16 of the expert's tokens per pass. Every operand streams through a
+// 4-slot LDS ring, one 256-weight super-block of k per slot, filled by
+// buffer-to-LDS dword DMA with the step's offset in a scalar register (no
+// VGPRs, no per-step address arithmetic); three steps are in flight while one
+// is computed. A slot holds the 128 rows' super-blocks (84 bytes padded to
+// 96 so that every field is 16-byte aligned), the 16 tokens' 256 q8_1 codes
+// (rows 272 bytes apart: 16-byte reads of 16 tokens hit distinct banks) and
+// their 8 block scales as float64 ([block][token]).
 // ---------------------------------------------------------------------------
 struct GateUpPfArgs {
   moe_experts ex;
   PlanView plan;
   const int8_t* xq;
-  const uint16_t* xd;
+  const double* xd64;
+  int m;
   int inter;
   float L;
   float* g;
@@ -208,48 +214,79 @@ struct GateUpPfArgs {
   float* h;
   int8_t* hq;
   uint16_t* hd;
+  double* hd64;
   int32_t* hs;
 };
 
-// LDS table indexed by a Q2_K scales byte (low nibble sc, high nibble m):
-// word 0 = bytes {0, sc, 2sc, 3sc} (code -> sc * code by v_perm), word 1 = m
-// in every byte.
-__device__ __forceinline__ void q2k_lut_fill(uint32_t (*lut)[2]) {
-  const uint32_t v = threadIdx.x;
-  if (v < 256) {
-    const uint32_t sc = v & 15u, mn = v >> 4;
-    lut[v][0] = (sc * 0x030201u) << 8;
-    lut[v][1] = mn * 0x01010101u;
-  }
+constexpr int kGuRows = 128;
+constexpr int kGuRowBytes = 96;
+constexpr int kGuW = kGuRows * kGuRowBytes;    // 12,288 B: 3072 dwords, 12 per thread
+constexpr int kATok = 272;                     // 256 codes + 16 bytes of padding per token
+constexpr int kGuA = 5 * 1024;                 // 16 * 68 = 1088 dwords rounded up to 5 per thread
+constexpr int kGuD = 8 * kChunk * 8;           // 1,024 B: 256 dwords, 1 per thread
+constexpr int kGuSlot = kGuW + kGuA + kGuD;    // 18,432 B
+constexpr int kGuSlots = 4;
+constexpr int kGuDma = 12 + 5 + 1;             // dword DMAs per thread per step
+constexpr int kGuLds = kGuSlots * kGuSlot + 64;   // + the 16-entry code table
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One dword per lane from `rsrc` at voff + soff into LDS at `wave_base` + 4 * lane.
+__device__ __forceinline__ void dma_dword(__amdgpu_buffer_rsrc_t rsrc, uint8_t* wave_base, uint32_t voff,
+                                          uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)wave_base, 4, voff, soff, 0, 0);
 }
 
 template <int NSB, int G>
-__device__ __forceinline__ void gateup_pf_tile(const uint8_t* __restrict__ wrow, const int8_t* __restrict__ arow,
-                                               const double (*d8)[kChunk], const uint32_t (*lut)[2], int kh,
-                                               double (&y)[4 * G]) {
-  const int lane = threadIdx.x & 63, hl = lane >> 5;
-  constexpr int kSbPer = NSB >= 2 ? NSB / 2 : 1;
-  const int sb0 = NSB >= 2 ? kh * kSbPer : 0;
+__device__ __forceinline__ void gateup_pf_ring(const GateUpPfArgs& a, uint8_t* lds, const uint32_t* lut,
+                                               __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
+                                               __amdgpu_buffer_rsrc_t rd, const uint32_t (&woff)[12],
+                                               const uint32_t (&aoff)[5], uint32_t doff, double (&y)[4 * G]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
+  auto issue = [&](int s) {
+    uint8_t* base = lds + (s % kGuSlots) * kGuSlot + 256 * wave;
+#pragma unroll
+    for (int k = 0; k < 12; ++k) dma_dword(rw, base + 1024 * k, woff[k], (uint32_t)s * kQ2KBytes);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) dma_dword(ra, base + kGuW + 1024 * k, aoff[k], (uint32_t)s * 256);
+    dma_dword(rd, base + kGuW + kGuA, doff, (uint32_t)s * 64);
+  };
 #pragma unroll
   for (int r = 0; r < 4 * G; ++r) y[r] = 0.0;
+  issue(0);
+  if (NSB > 1) issue(1);
+  if (NSB > 2) issue(2);
 #pragma unroll 1
-  for (int sb = sb0; sb < sb0 + kSbPer; ++sb) {
-    const uint8_t* blk = wrow + sb * kQ2KBytes;
-    const u32x4a4 scv = *reinterpret_cast<const u32x4a4*>(blk);
-    const u32x4a4 qv0 = *reinterpret_cast<const u32x4a4*>(blk + 16 + 16 * hl);
-    const u32x4a4 qv1 = *reinterpret_cast<const u32x4a4*>(blk + 48 + 16 * hl);
-    const uint32_t ddw = *reinterpret_cast<const uint32_t*>(blk + 80);
+  for (int s = 0; s < NSB; ++s) {
+    const int after = NSB - 1 - s;   // steps issued after s (at most 2 here)
+    if (after >= 2) wait_vmcnt<2 * kGuDma>();
+    else if (after == 1) wait_vmcnt<kGuDma>();
+    else wait_vmcnt<0>();
+    block_sync_lds();   // every wave's share of step s has landed; every wave is done with step s - 1
+    if (s + 3 < NSB) issue(s + 3);   // into the slot step s - 1 used
+    const uint8_t* sl = lds + (s % kGuSlots) * kGuSlot;
+    const uint8_t* wr = sl + (32 * wave + (lane & 31)) * kGuRowBytes;
+    const u32x4a4 scv = *reinterpret_cast<const u32x4a4*>(wr);
+    const u32x4a4 qv0 = *reinterpret_cast<const u32x4a4*>(wr + 16 + 16 * hl);
+    const u32x4a4 qv1 = *reinterpret_cast<const u32x4a4*>(wr + 48 + 16 * hl);
+    const uint32_t ddw = *reinterpret_cast<const uint32_t*>(wr + 80);
+    const int8_t* ar = reinterpret_cast<const int8_t*>(sl + kGuW) + (lane & 15) * kATok + 16 * hl;
+    const double* dr = reinterpret_cast<const double*>(sl + kGuW + kGuA);
     double accS[4 * G], accM[4 * G];
 #pragma unroll
     for (int r = 0; r < 4 * G; ++r) accS[r] = accM[r] = 0.0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (NSB == 1 && (t >> 2) != kh) continue;   // one super-block: the halves split its q8_1 blocks
-      const int b = 8 * sb + t, j = t & 3;
-      const i32x4 A = *reinterpret_cast<const i32x4*>(arow + 32 * b);
+      const int j = t & 3;
+      const i32x4 A = *reinterpret_cast<const i32x4*>(ar + 32 * t);
       const u32x4a4 qw = t < 4 ? qv0 : qv1;
       const uint32_t sbyte = (scv[t >> 1] >> (8 * (2 * (t & 1) + hl))) & 0xFFu;
-      const uint32_t lut_s = lut[sbyte][0], mrep = lut[sbyte][1];
+      const uint32_t lut_s = lut[sbyte & 15u];
+      const uint32_t mrep = __builtin_amdgcn_perm(0u, sbyte >> 4, 0u);   // the min nibble in every byte
       i32x4 Bs;
 #pragma unroll
       for (int i = 0; i < 4; ++i) Bs[i] = (int)__builtin_amdgcn_perm(lut_s, lut_s, (qw[i] >> (2 * j)) & 0x03030303u);
@@ -258,7 +295,7 @@ __device__ __forceinline__ void gateup_pf_tile(const uint8_t* __restrict__ wrow,
       const i32x16 M = mfma_i8(A, Bm);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const double* dp = &d8[b][8 * g + 4 * hl];
+        const double* dp = dr + t * kChunk + 8 * g + 4 * hl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           accS[4 * g + i] = __builtin_fma(dp[i], (double)S[4 * g + i], accS[4 * g + i]);
@@ -276,77 +313,88 @@ __device__ __forceinline__ void gateup_pf_tile(const uint8_t* __restrict__ wrow,
 template <int NSB>
 __global__ __launch_bounds__(256) void k_gateup_pf(GateUpPfArgs a) {
   constexpr int dim = 256 * NSB, NB = 8 * NSB;
-  __shared__ double d8[NB][kChunk];
-  __shared__ double xch[2][kChunk][32];   // the second half's partial sums
-  __shared__ float gu[2][kChunk][32];
-  __shared__ uint32_t lut[256][2];
-  const int ngr = a.inter / 32;
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint32_t* lut = reinterpret_cast<uint32_t*>(lds + kGuSlots * kGuSlot);
+  float (*gu)[kChunk][64] = reinterpret_cast<float (*)[kChunk][64]>(lds);   // after the k loop: [gate|up][tok][unit]
+  const int ngr = a.inter / 64;
   const int u = blockIdx.x / ngr, grp = blockIdx.x % ngr;
   if (u >= *a.plan.n_u()) return;
   const int e = a.plan.u_expert()[u], first = a.plan.u_first()[u], np = a.plan.u_npairs()[u];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
-  const int mat = wave & 1, kh = wave >> 1;
-  q2k_lut_fill(lut);
-  const uint8_t* wrow = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride + (mat ? a.ex.up_off : a.ex.gate_off) +
-                        (uint64_t)(32 * grp + (lane & 31)) * (NSB * kQ2KBytes);
+  if (tid < 16) lut[tid] = ((uint32_t)tid * 0x030201u) << 8;   // bytes {0, sc, 2sc, 3sc}
+  const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
+  const uint32_t ebytes = (uint32_t)((a.ex.gate_off > a.ex.up_off ? a.ex.gate_off : a.ex.up_off) +
+                                     (uint64_t)a.inter * NSB * kQ2KBytes);
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(ebase, ebytes);
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a.xq, (uint32_t)((uint64_t)a.m * dim));
+  const __amdgpu_buffer_rsrc_t rd = buf_rsrc(a.xd64, (uint32_t)((uint64_t)a.m * NB * 8));
+  // the weight dwords this thread moves every step: slot dword i = row * 24 + k (k < 21 real, else padding)
+  uint32_t woff[12];
+#pragma unroll
+  for (int k = 0; k < 12; ++k) {
+    const int i = tid + 256 * k, r = i / 24, dw = i % 24;
+    const int wr = r >> 5, row = 64 * grp + 32 * (wr & 1) + (r & 31);
+    woff[k] = (uint32_t)(((wr >> 1) ? a.ex.up_off : a.ex.gate_off) + (uint64_t)row * (NSB * kQ2KBytes)) +
+              4u * (uint32_t)(dw < 21 ? dw : 0);
+  }
   for (int c0 = 0; c0 < np; c0 += kChunk) {
     const int nt = min(kChunk, np - c0);
     const int* ptok = a.plan.pair_tok() + first + c0;
-    __syncthreads();   // the previous chunk is done with d8 / gu
-    for (int i = tid; i < NB * kChunk; i += 256) {
-      const int jt = i / NB, b = i % NB;
-      d8[b][jt] = jt < nt ? fp16_f64(a.xd[(int64_t)ptok[jt] * NB + b]) : 0.0;
+    uint32_t aoff[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {   // slot dword i = token * 68 + k (k < 64 real, else padding)
+      const int i = tid + 256 * k, tk = i / 68, dw = i % 68;
+      const int tok = ptok[min(tk, nt - 1)];
+      aoff[k] = (uint32_t)tok * dim + (tk < kChunk && dw < 64 ? 4u * dw : 0u);
     }
-    // token rows past the chunk repeat its last token: their results are never stored
-    const int ja = min(lane & 31, nt - 1);
-    const int8_t* arow = a.xq + (int64_t)ptok[ja] * dim + 16 * hl;
-    __syncthreads();
+    const int dt = tid >> 5, dtok = (tid & 31) >> 1;   // [block][token] float64, two dwords each
+    const uint32_t doff = ((uint32_t)ptok[min(dtok, nt - 1)] * NB + dt) * 8u + 4u * (tid & 1);
+    __syncthreads();   // the previous pass is done with the LDS (its SwiGLU phase reads gu)
     double y[4 * kGroups];
     if (nt > 8) {
-      gateup_pf_tile<NSB, 2>(wrow, arow, d8, lut, kh, y);
+      gateup_pf_ring<NSB, 2>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y);
     } else {
       double y1[4];
-      gateup_pf_tile<NSB, 1>(wrow, arow, d8, lut, kh, y1);
+      gateup_pf_ring<NSB, 1>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[r] = y1[r];
 #pragma unroll
       for (int r = 4; r < 4 * kGroups; ++r) y[r] = 0.0;
     }
-    if (kh == 1) {
+    __syncthreads();   // every wave is done reading the ring
+    {
+      const int mat = wave >> 1, unit = 32 * (wave & 1) + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 4 * kGroups; ++r) xch[mat][tile_tok(r, lane)][lane & 31] = y[r];
+      for (int r = 0; r < 4 * kGroups; ++r) gu[mat][tile_tok(r, lane)][unit] = (float)y[r];
     }
     __syncthreads();
-    if (kh == 0) {
-#pragma unroll
-      for (int r = 0; r < 4 * kGroups; ++r) {
-        const int tt = tile_tok(r, lane);
-        gu[mat][tt][lane & 31] = (float)(y[r] + xch[mat][tt][lane & 31]);
-      }
-    }
-    __syncthreads();
-    // SwiGLU + q8_1 of h: a half-wave per token, a lane per hidden unit
-    const int unit = lane & 31;
+    // SwiGLU + q8_1 of h: a half-wave per (token, 32 units = one q8_1 block), a lane per unit
 #pragma unroll 1
-    for (int tt = 2 * wave + hl; tt < kChunk; tt += 8) {
+    for (int job = 2 * wave + hl; job < 2 * kChunk; job += 8) {
+      const int tt = job >> 1, hb = job & 1, unit = 32 * hb + (lane & 31);
       const bool live = tt < nt;
       const float gv = gu[0][tt][unit], uv = gu[1][tt][unit];
       const float hv = live ? swiglu(gv, uv, a.L) : 0.0f;
       float am = fabsf(hv);
-      for (int s = 16; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
+      for (int sh = 16; sh >= 1; sh >>= 1) am = fmaxf(am, __shfl_xor(am, sh));
       const float d = (float)((double)am / 127.0);
       const int q = am == 0.0f ? 0 : q8_code(hv, d);
       int sum = q;
-      for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+      for (int sh = 8; sh >= 1; sh >>= 1) sum += __shfl_xor(sum, sh);
       if (live) {
         const int64_t pair = first + c0 + tt;
-        const int64_t o = pair * a.inter + 32 * grp + unit;
+        const int64_t o = pair * a.inter + 64 * grp + unit;
+        const int blk = 2 * grp + hb;
         a.g[o] = gv;
         a.u[o] = uv;
         a.h[o] = hv;
         a.hq[o] = (int8_t)q;
-        if (unit == 0) a.hd[pair * (a.inter / 32) + grp] = f32_to_fp16_bits(d);
-        if ((unit & 15) == 0) a.hs[pair * (a.inter / 16) + 2 * grp + (unit >> 4)] = sum;
+        if ((lane & 31) == 0) {
+          const uint16_t d16 = f32_to_fp16_bits(d);
+          a.hd[pair * (a.inter / 32) + blk] = d16;
+          a.hd64[pair * (a.inter / 32) + blk] = fp16_f64(d16);
+        }
+        if ((lane & 15) == 0) a.hs[pair * (a.inter / 16) + 2 * blk + ((lane & 31) >> 4)] = sum;
       }
     }
   }
@@ -365,6 +413,8 @@ struct DownPfArgs {
   PlanView plan;
   const int8_t* hq;
   const uint16_t* hd;
+  const double* hd64;
+  int n_pairs_max;
   int dim;
   float* y;
 };
@@ -442,7 +492,7 @@ __device__ __forceinline__ void down_pf_tile(const uint8_t* __restrict__ wrow, c
 }
 
 template <int NSB>
-__global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
+__global__ __launch_bounds__(256) void k_down_pf_direct(DownPfArgs a) {
   constexpr int inter = 256 * NSB, NB = 8 * NSB;
   __shared__ double d8[NB][kChunk];
   __shared__ uint32_t lut[64][2];
@@ -481,6 +531,146 @@ __global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int tt = tile_tok(r, lane);
         if (tt < nt) a.y[(p0 + tt) * a.dim + row] = (float)y[r];
+      }
+    }
+  }
+}
+
+// The same down GEMM through a 3-slot LDS ring (inter >= 512): a slot holds,
+// for one super-block of k, the 128 rows' 110-byte blocks in 112-byte rows
+// (the DMA window starts on the dword at or before the block, so a block of
+// odd index sits 2 bytes into its row), the 16 pairs' h codes (rows 272
+// bytes apart) and their 8 block scales as float64 ([block][pair]).
+constexpr int kDnRows = 128;
+constexpr int kDnRowBytes = 112;
+constexpr int kDnW = kDnRows * kDnRowBytes;    // 14,336 B: 3584 dwords, 14 per thread
+constexpr int kDnSlot = kDnW + kGuA + kGuD;    // 20,480 B
+constexpr int kDnSlots = 3;
+constexpr int kDnDma = 14 + 5 + 1;
+constexpr int kDnLds = kDnSlots * kDnSlot + 512;   // + the 64-entry scale table
+
+template <int NSB, int G>
+__device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)[2], __amdgpu_buffer_rsrc_t rw,
+                                             __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rd,
+                                             const uint32_t (&woff)[14], const uint32_t (&aoff)[5], uint32_t doff,
+                                             double (&y)[4 * G]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
+  auto issue = [&](int s) {
+    uint8_t* base = lds + (s % kDnSlots) * kDnSlot + 256 * wave;
+    const uint32_t wsoff = (uint32_t)(s * kQ3KBytes - 2 * (s & 1));   // dword-aligned window start
+#pragma unroll
+    for (int k = 0; k < 14; ++k) dma_dword(rw, base + 1024 * k, woff[k], wsoff);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) dma_dword(ra, base + kDnW + 1024 * k, aoff[k], (uint32_t)s * 256);
+    dma_dword(rd, base + kDnW + kGuA, doff, (uint32_t)s * 64);
+  };
+#pragma unroll
+  for (int r = 0; r < 4 * G; ++r) y[r] = 0.0;
+  issue(0);
+  if (NSB > 1) issue(1);
+#pragma unroll 1
+  for (int s = 0; s < NSB; ++s) {
+    if (s + 1 < NSB) wait_vmcnt<kDnDma>();
+    else wait_vmcnt<0>();
+    block_sync_lds();   // step s landed everywhere; step s - 1 is done everywhere
+    if (s + 2 < NSB) issue(s + 2);
+    const uint8_t* sl = lds + (s % kDnSlots) * kDnSlot;
+    const uint8_t* blk = sl + (32 * wave + (lane & 31)) * kDnRowBytes + 2 * (s & 1);
+    const u32x4a2 hmv = *reinterpret_cast<const u32x4a2*>(blk + 16 * hl);
+    const u32x4a2 qv0 = *reinterpret_cast<const u32x4a2*>(blk + 32 + 16 * hl);
+    const u32x4a2 qv1 = *reinterpret_cast<const u32x4a2*>(blk + 64 + 16 * hl);
+    const u32x2a2 sc01 = *reinterpret_cast<const u32x2a2*>(blk + 96);
+    const uint32_t sc2 = *reinterpret_cast<const uint32_t __attribute__((aligned(2)))*>(blk + 104);
+    const uint32_t dbits = *reinterpret_cast<const uint16_t*>(blk + 108);
+    const int8_t* ar = reinterpret_cast<const int8_t*>(sl + kDnW) + (lane & 15) * kATok + 16 * hl;
+    const double* dr = reinterpret_cast<const double*>(sl + kDnW + kGuA);
+    double acc[4 * G];
+#pragma unroll
+    for (int r = 0; r < 4 * G; ++r) acc[r] = 0.0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int h = t >> 2, j = t & 3;
+      const int sl8 = 2 * (t & 3) + hl;
+      const uint32_t lob = ((sl8 < 4 ? sc01[0] : sc01[1]) >> (8 * (sl8 & 3))) & 0xFFu;
+      const uint32_t lo = t < 4 ? (lob & 15u) : (lob >> 4);
+      const uint32_t hib = (sc2 >> (8 * (2 * (t & 1) + hl))) & 0xFFu;
+      const uint32_t hi = (hib >> (2 * (t >> 1))) & 3u;
+      const uint32_t u6 = lo | (hi << 4);
+      const uint32_t lut_lo = lut[u6][0], lut_hi = lut[u6][1];
+      const u32x4a2 qw = t < 4 ? qv0 : qv1;
+      const int hbit = 4 * h + j;
+      i32x4 B;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t q2 = (qw[i] >> (2 * j)) & 0x03030303u;
+        const uint32_t hb = hbit >= 2 ? (hmv[i] >> (hbit - 2)) : (hmv[i] << (2 - hbit));
+        B[i] = (int)__builtin_amdgcn_perm(lut_hi, lut_lo, (hb & 0x04040404u) | q2);
+      }
+      const i32x4 A = *reinterpret_cast<const i32x4*>(ar + 32 * t);
+      const i32x16 S = mfma_i8(A, B);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const double* dp = dr + t * kChunk + 8 * g + 4 * hl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * g + i] = __builtin_fma(dp[i], (double)S[4 * g + i], acc[4 * g + i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const double nd = -fp16_f64(dbits);   // the MFMA sums are -S_b
+#pragma unroll
+    for (int r = 0; r < 4 * G; ++r) y[r] = __builtin_fma(nd, acc[r], y[r]);
+  }
+}
+
+template <int NSB>
+__global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
+  constexpr int inter = 256 * NSB, NB = 8 * NSB;
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint32_t (*lut)[2] = reinterpret_cast<uint32_t (*)[2]>(lds + kDnSlots * kDnSlot);
+  const int nrt = a.dim / kDnRows;
+  const int u = blockIdx.x / nrt, rt = blockIdx.x % nrt;
+  if (u >= *a.plan.n_u()) return;
+  const int e = a.plan.u_expert()[u], first = a.plan.u_first()[u], np = a.plan.u_npairs()[u];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  q3k_lut_fill(lut);
+  const uint8_t* wbase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride + a.ex.down_off;
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wbase, (uint32_t)((uint64_t)a.dim * NSB * kQ3KBytes));
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a.hq, (uint32_t)((uint64_t)a.n_pairs_max * inter));
+  const __amdgpu_buffer_rsrc_t rd = buf_rsrc(a.hd64, (uint32_t)((uint64_t)a.n_pairs_max * NB * 8));
+  uint32_t woff[14];   // slot dword i = row * 28 + k
+#pragma unroll
+  for (int k = 0; k < 14; ++k) {
+    const int i = tid + 256 * k, r = i / 28, dw = i % 28;
+    woff[k] = (uint32_t)(kDnRows * rt + r) * (NSB * kQ3KBytes) + 4u * dw;
+  }
+  const int row = kDnRows * rt + 32 * wave + (lane & 31);
+  for (int c0 = 0; c0 < np; c0 += kChunk) {
+    const int nt = min(kChunk, np - c0);
+    const int p0 = first + c0;
+    uint32_t aoff[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int i = tid + 256 * k, tk = i / 68, dw = i % 68;
+      aoff[k] = (uint32_t)(p0 + min(tk, nt - 1)) * inter + (tk < kChunk && dw < 64 ? 4u * dw : 0u);
+    }
+    const int dt = tid >> 5, dtok = (tid & 31) >> 1;
+    const uint32_t doff = ((uint32_t)(p0 + min(dtok, nt - 1)) * NB + dt) * 8u + 4u * (tid & 1);
+    __syncthreads();
+    if (nt > 8) {
+      double y[8];
+      down_pf_ring<NSB, 2>(lds, lut, rw, ra, rd, woff, aoff, doff, y);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int tt = tile_tok(r, lane);
+        if (tt < nt) a.y[(int64_t)(p0 + tt) * a.dim + row] = (float)y[r];
+      }
+    } else {
+      double y[4];
+      down_pf_ring<NSB, 1>(lds, lut, rw, ra, rd, woff, aoff, doff, y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = tile_tok(r, lane);
+        if (tt < nt) a.y[(int64_t)(p0 + tt) * a.dim + row] = (float)y[r];
       }
     }
   }
@@ -569,21 +759,40 @@ __global__ __launch_bounds__(256) void k_shared_down_pf(const uint16_t* __restri
 
 template <int NSB>
 hipError_t launch_gateup_pf_t(const GateUpPfArgs& a, int max_u, hipStream_t s) {
-  MOE_LAUNCH(MOE_K_GATEUP, k_gateup_pf<NSB>, dim3(max_u * (a.inter / 32)), dim3(256), 0, s, a);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gateup_pf<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kGuLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  MOE_LAUNCH(MOE_K_GATEUP, k_gateup_pf<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLds, s, a);
   return hipGetLastError();
 }
 
 template <int NSB>
 hipError_t launch_down_pf_t(const DownPfArgs& a, int max_u, hipStream_t s) {
-  MOE_LAUNCH(MOE_K_DOWN, k_down_pf<NSB>, dim3(max_u * (a.dim / 128)), dim3(256), 0, s, a);
+  if constexpr (NSB == 1) {   // one super-block of k: the kernel without the ring
+    MOE_LAUNCH(MOE_K_DOWN, k_down_pf_direct<NSB>, dim3(max_u * (a.dim / 128)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  } else {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_down_pf<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kDnLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  MOE_LAUNCH(MOE_K_DOWN, k_down_pf<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), kDnLds, s, a);
   return hipGetLastError();
+  }
 }
 
 }  // namespace
 
 hipError_t launch_router_pf(const uint16_t* x, int m, const uint16_t* gate_w, const moe_cfg& c, const Ws& w,
                             float* logits_out, hipStream_t s) {
-  const int router_blocks = (c.n_routed + 3) / 4;
+  const int router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
   const int tgroups = (m + 7) / 8;
   const int64_t quant = (int64_t)m * c.dim / 256;
   const int quant_cols = (int)((quant + tgroups - 1) / tgroups);
@@ -602,7 +811,7 @@ hipError_t launch_group(const int32_t* header, int m, const moe_cfg& c, const Ws
 
 hipError_t launch_gateup_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
   const int max_u = min(c.n_routed, m * c.topk);
-  GateUpPfArgs a{ex, w.plan, w.xq, w.xd, c.inter, c.swiglu_limit, w.g, w.u, w.h, w.hq, w.hd, w.hs};
+  GateUpPfArgs a{ex, w.plan, w.xq, w.xd64, m, c.inter, c.swiglu_limit, w.g, w.u, w.h, w.hq, w.hd, w.hd64, w.hs};
   switch (c.dim / 256) {
     case 1: return launch_gateup_pf_t<1>(a, max_u, s);
     case 2: return launch_gateup_pf_t<2>(a, max_u, s);
@@ -615,7 +824,7 @@ hipError_t launch_gateup_pf(const moe_experts& ex, int m, const moe_cfg& c, cons
 
 hipError_t launch_down_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
   const int max_u = min(c.n_routed, m * c.topk);
-  DownPfArgs a{ex, w.plan, w.hq, w.hd, c.dim, w.y};
+  DownPfArgs a{ex, w.plan, w.hq, w.hd, w.hd64, m * c.topk, c.dim, w.y};
   switch (c.inter / 256) {
     case 1: return launch_down_pf_t<1>(a, max_u, s);
     case 2: return launch_down_pf_t<2>(a, max_u, s);

@@ -35,7 +35,7 @@ def test_workspace_queries():
     assert 0 < n1 < n8
     L = R.workspace_layout(c, 8)
     offs = [L[k] for k in ("ctl", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u", "h", "hq", "hd", "hs",
-                           "y", "sg", "su", "sh", "sd", "yr", "status", "grp")]
+                           "y", "sg", "su", "sh", "sd", "yr", "status", "grp", "xd64", "hd64")]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs) and L["total"] == n8
     assert L["max_pairs"] == 48
     assert R.header_words(c) == 19
