@@ -20,7 +20,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-command-line-argument"]
-SOURCES = ["moe_api.hip", "moe_route.hip", "moe_experts.hip", "moe_decode1.hip", "moe_prefill.hip"]
+SOURCES = ["moe_api.hip", "moe_route.hip", "moe_experts.hip", "moe_decode1.hip", "moe_prefill.hip",
+           "moe_shared_pf.hip"]
 # the prefill kernels consume MFMA results in VALU code: keep them in VGPRs (no accvgpr copies)
 EXTRA = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

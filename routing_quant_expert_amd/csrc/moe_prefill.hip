@@ -10,8 +10,7 @@
 //  * k_gateup_pf: gate/up GEMMs on raw Q2_K blocks with int8 MFMA, fused
 //    clamped SwiGLU and q8_1 of h;
 //  * k_down_pf: down GEMMs on raw Q3_K blocks with int8 MFMA;
-//  * k_shared_gu_pf / k_shared_down_pf: the bf16 shared expert as two bf16
-//    MFMA GEMMs (f32 accumulation), SwiGLU fused into the first.
+//  (the bf16 shared expert's two GEMMs are in moe_shared_pf.hip).
 // The weighted combine in plan order is the decode path's k_combine.
 //
 // Numerics of the K-quant GEMMs (the same values as the decode GEMVs): an
@@ -37,11 +36,9 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));   // 16 bytes, 4-byte aligned
 typedef uint32_t u32x4a2 __attribute__((ext_vector_type(4), aligned(2)));   // 16 bytes, 2-byte aligned
 typedef uint32_t u32x2a2 __attribute__((ext_vector_type(2), aligned(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChunk = 16;   // tokens of one expert per MFMA pass (rows 16..31 of the token operand are zero)
 constexpr int kGroups = kChunk / 8;
@@ -56,18 +53,98 @@ __device__ __forceinline__ i32x16 mfma_i8(i32x4 a, i32x4 b) {
 __device__ __forceinline__ int tile_tok(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // ---------------------------------------------------------------------------
-// Router + q8_1 of x for m tokens. Grid (router rows / 4, ceil(m / 8)) plus
-// the quantisation workgroups in the first grid row.
+// Router + q8_1 of x for m tokens. A wave computes 4 expert rows for 8
+// tokens (each converted bf16 chunk of x serves 4 rows, each of w 8 tokens);
+// every (row, token) is summed in the decode router's order: lane l adds
+// fmul(x, w) for positions 512*i + 8*l + j, i ascending, j = 0..7, in f32
+// without contraction, then the 64 partials combine by p += shfl_xor(p, s)
+// for s = 32 .. 1, so a token's logits are the same bits at any m. Grid
+// (router groups of 16 rows, ceil(m / 8)) plus the quantisation workgroups.
 // ---------------------------------------------------------------------------
+constexpr int kRpRows = 4;
+constexpr int kRpTok = 8;
+
+__device__ inline void bf16x8_f32(uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+}
+
+__device__ void router_rows4(int e0, int t0, const uint16_t* __restrict__ x, int m, int dim,
+                             const uint16_t* __restrict__ gate_w, int n_routed, float temp,
+                             float* __restrict__ logits, float* __restrict__ scores,
+                             float* __restrict__ logits_out) {
+  const int lane = threadIdx.x & 63;
+  const int nt = min(kRpTok, m - t0);
+  float p[kRpRows][kRpTok];
+#pragma unroll
+  for (int r = 0; r < kRpRows; ++r)
+#pragma unroll
+    for (int t = 0; t < kRpTok; ++t) p[r][t] = 0.0f;
+  const int nch = dim / 512;   // dim is a multiple of 256; a half chunk is handled below
+#pragma unroll 1
+  for (int c = 0; c * 512 < dim; ++c) {
+    const int k = 512 * c + 8 * lane;
+    const bool in = k < dim;
+    float wf[kRpRows][8];
+#pragma unroll
+    for (int r = 0; r < kRpRows; ++r) {
+      const int e = min(e0 + r, n_routed - 1);
+      const uint4 v = in ? *reinterpret_cast<const uint4*>(gate_w + (int64_t)e * dim + k) : make_uint4(0, 0, 0, 0);
+      bf16x8_f32(v, wf[r]);
+    }
+#pragma unroll
+    for (int t = 0; t < kRpTok; ++t) {
+      const int tt = min(t0 + t, m - 1);
+      const uint4 v = in ? *reinterpret_cast<const uint4*>(x + (int64_t)tt * dim + k) : make_uint4(0, 0, 0, 0);
+      float xf[8];
+      bf16x8_f32(v, xf);
+#pragma unroll
+      for (int r = 0; r < kRpRows; ++r) {
+        float acc = p[r][t];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fadd(acc, fmul(xf[j], wf[r][j]));   // zero padding adds +0: exact
+        p[r][t] = acc;
+      }
+    }
+  }
+  (void)nch;
+#pragma unroll
+  for (int r = 0; r < kRpRows; ++r)
+#pragma unroll
+    for (int t = 0; t < kRpTok; ++t) {
+      float v = p[r][t];
+      for (int s = 32; s >= 1; s >>= 1) v = fadd(v, __shfl_xor(v, s));
+      p[r][t] = v;
+    }
+  // lane 8r + t writes (row e0 + r, token t0 + t)
+  if (lane < kRpRows * kRpTok) {
+    const int r = lane >> 3, t = lane & 7;
+    float lg = 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < kRpRows; ++rr)
+#pragma unroll
+      for (int q = 0; q < kRpTok; ++q)
+        if (rr == r && q == t) lg = p[rr][q];
+    const int e = e0 + r;
+    if (t < nt && e < n_routed) {
+      const int64_t o = (int64_t)(t0 + t) * n_routed + e;
+      logits[o] = lg;
+      if (logits_out) logits_out[o] = lg;
+      scores[o] = score_of(lg, temp);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_router_pf(const uint16_t* __restrict__ x, int m, int dim,
                                                    const uint16_t* __restrict__ gate_w, int n_routed, float temp,
                                                    int router_blocks, Ws w, float* __restrict__ logits_out) {
   const int bx = blockIdx.x;
   if (bx == 0 && blockIdx.y == 0 && threadIdx.x < 4) w.status[threadIdx.x] = 0;   // every entry point starts here
   if (bx < router_blocks) {
-    const int t_lo = 8 * blockIdx.y;
-    front::router_rows(bx, x, m, dim, gate_w, n_routed, temp, w.logits, w.scores, logits_out, t_lo,
-                       min(m, t_lo + 8));
+    const int e0 = (4 * bx + (threadIdx.x >> 6)) * kRpRows;
+    if (e0 < n_routed)
+      router_rows4(e0, kRpTok * blockIdx.y, x, m, dim, gate_w, n_routed, temp, w.logits, w.scores, logits_out);
     return;
   }
   const int qb = (bx - router_blocks) * gridDim.y + blockIdx.y;
@@ -676,87 +753,6 @@ __global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Shared expert, bf16 MFMA (v_mfma_f32_32x32x16_bf16: lane l holds 8
-// consecutive k of operand row l%32 at k offset 8*(l/32)); f32 accumulation
-// in the MFMA's order [moe_v41.rs, module doc: the shared expert runs on the
-// dense bf16 GEMM].
-// gate/up: a wave = 32 tokens x 32 hidden units, gate and up; a workgroup =
-// 4 waves over 128 units sharing the token rows; then sh = bf16(SwiGLU).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(p));
-}
-
-__global__ __launch_bounds__(256) void k_shared_gu_pf(const uint16_t* __restrict__ x, int m, int dim, int inter,
-                                                      const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
-                                                      float* __restrict__ sg, float* __restrict__ su,
-                                                      uint16_t* __restrict__ sh, float L) {
-  __shared__ float tile[2][32][128 + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
-  const int tok0 = 32 * blockIdx.y, unit0 = 128 * blockIdx.x;
-  const int ta = tok0 + (lane & 31);
-  const int un = unit0 + 32 * wave + (lane & 31);
-  const uint16_t* xa = x + (int64_t)min(ta, m - 1) * dim + 8 * hl;
-  const uint16_t* ga = w1 + (int64_t)un * dim + 8 * hl;
-  const uint16_t* ua = w3 + (int64_t)un * dim + 8 * hl;
-  f32x16 cg = {}, cu = {};
-  const bool arow_ok = ta < m;
-#pragma unroll 4
-  for (int k = 0; k < dim; k += 16) {
-    bf16x8 av = ld_bf16x8(xa + k);
-    if (!arow_ok) av = bf16x8{};
-    cg = mfma_bf16(av, ld_bf16x8(ga + k), cg);
-    cu = mfma_bf16(av, ld_bf16x8(ua + k), cu);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    tile[0][tile_tok(r, lane)][32 * wave + (lane & 31)] = cg[r];
-    tile[1][tile_tok(r, lane)][32 * wave + (lane & 31)] = cu[r];
-  }
-  __syncthreads();
-#pragma unroll 1
-  for (int i = tid; i < 32 * 128; i += 256) {
-    const int tt = i >> 7, uu = i & 127;
-    const int t = tok0 + tt;
-    if (t >= m) continue;
-    const float gv = tile[0][tt][uu], uv = tile[1][tt][uu];
-    const int64_t o = (int64_t)t * inter + unit0 + uu;
-    sg[o] = gv;
-    su[o] = uv;
-    sh[o] = bf16_rne(swiglu(gv, uv, L));
-  }
-}
-
-// down: sd = W2s . sh; a wave = 32 tokens x 32 output rows, a workgroup = 4
-// waves over 128 rows sharing the token rows.
-__global__ __launch_bounds__(256) void k_shared_down_pf(const uint16_t* __restrict__ sh, int m, int dim, int inter,
-                                                        const uint16_t* __restrict__ w2, float* __restrict__ sd) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
-  const int tok0 = 32 * blockIdx.y;
-  const int ta = tok0 + (lane & 31);
-  const int row = 128 * blockIdx.x + 32 * wave + (lane & 31);
-  const uint16_t* ha = sh + (int64_t)min(ta, m - 1) * inter + 8 * hl;
-  const uint16_t* wa = w2 + (int64_t)row * inter + 8 * hl;
-  const bool arow_ok = ta < m;
-  f32x16 c = {};
-#pragma unroll 4
-  for (int k = 0; k < inter; k += 16) {
-    bf16x8 av = ld_bf16x8(ha + k);
-    if (!arow_ok) av = bf16x8{};
-    c = mfma_bf16(av, ld_bf16x8(wa + k), c);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = tok0 + tile_tok(r, lane);
-    if (t < m) sd[(int64_t)t * dim + row] = c[r];
-  }
-}
-
 template <int NSB>
 hipError_t launch_gateup_pf_t(const GateUpPfArgs& a, int max_u, hipStream_t s) {
   static bool attr_set = false;
@@ -792,7 +788,7 @@ hipError_t launch_down_pf_t(const DownPfArgs& a, int max_u, hipStream_t s) {
 
 hipError_t launch_router_pf(const uint16_t* x, int m, const uint16_t* gate_w, const moe_cfg& c, const Ws& w,
                             float* logits_out, hipStream_t s) {
-  const int router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
+  const int router_blocks = gate_w ? (c.n_routed + 4 * kRpRows - 1) / (4 * kRpRows) : 0;
   const int tgroups = (m + 7) / 8;
   const int64_t quant = (int64_t)m * c.dim / 256;
   const int quant_cols = (int)((quant + tgroups - 1) / tgroups);
@@ -833,18 +829,6 @@ hipError_t launch_down_pf(const moe_experts& ex, int m, const moe_cfg& c, const 
     case 16: return launch_down_pf_t<16>(a, max_u, s);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_shared_pf(const uint16_t* x, int m, const moe_layer& layer, const moe_cfg& c, const Ws& w,
-                            hipStream_t s) {
-  const int tt = (m + 31) / 32;
-  MOE_LAUNCH(MOE_K_SHARED_GU, k_shared_gu_pf, dim3(c.inter / 128, tt), dim3(256), 0, s, x, m, c.dim, c.inter,
-             layer.sh_w1, layer.sh_w3, w.sg, w.su, w.sh, c.swiglu_limit);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  MOE_LAUNCH(MOE_K_SHARED_DOWN, k_shared_down_pf, dim3(c.dim / 128, tt), dim3(256), 0, s, w.sh, m, c.dim, c.inter,
-             layer.sh_w2, w.sd);
-  return hipGetLastError();
 }
 
 }  // namespace moe
