@@ -32,6 +32,11 @@ int fail(int code, const char* fmt, const char* a = "", long long b = 0) {
 
 bool pow2_upto16(int v) { return v >= 1 && v <= 16 && (v & (v - 1)) == 0; }
 
+// The single-token kernels: up to 6 picks (a wave each) and down rows of at
+// most 8 Q3_K super-blocks (each pick's 16-row tile is staged whole in LDS);
+// other shapes take the union path, which is correct for every m <= 8.
+bool single_token_fits(const moe_cfg& c) { return c.topk <= kMaxTopkM1 && c.inter / 256 <= 8; }
+
 int check_cfg(const moe_cfg* c) {
   if (!c) return fail(MOE_EINVAL, "cfg is NULL%s%lld");
   if (!(c->gate_temp > 0.0f) || !std::isfinite(c->gate_temp) || !std::isfinite(c->route_scale) ||
@@ -172,7 +177,7 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
     if ((e = launch_combine(m, c, w, w.sd, o, s)) != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
   }
-  if (m == 1 && c.topk <= kMaxTopkM1) {   // router + q8_1; selection, routed and shared gate/up; down + combine
+  if (m == 1 && single_token_fits(c)) {   // router + q8_1; selection, routed and shared gate/up; down + combine
     if ((e = launch_front(x, 1, layer.gate_w, nullptr, nullptr, nullptr, c, w, nullptr, s)) != hipSuccess)
       return hip_fail(e, "front");
     if ((e = launch_gateup_m1(layer.experts, &sel, nullptr, x, &layer, c, w, s)) != hipSuccess)
@@ -249,7 +254,7 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
-  if (m == 1 && cfg->topk <= kMaxTopkM1) {
+  if (m == 1 && single_token_fits(*cfg)) {
     if ((e = launch_gateup_m1(*experts, nullptr, header, x, nullptr, *cfg, w, s)) != hipSuccess)
       return hip_fail(e, "gateup_m1");
     if ((e = launch_down_m1(*experts, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) !=
