@@ -29,30 +29,31 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("moe_decode1.hip", "moe_kquant.h", "moe_math.h", "moe_internal.h")
+PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h")
 
 
-def kernel_source_sha() -> str:
-    """Hash of the sources of the single-token expert kernels (ties measured counters to a kernel version)."""
+def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
+    """Hash of a kernel's sources (ties measured counters to a kernel version)."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "routing_quant_expert_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, summary: str = "hbm_traffic_decode_m1_dim4096.md", sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     import re
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_decode_m1_dim4096.md")
+    path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(\{.*?\})\n```", open(path).read(), re.S)
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("kernel") != kernel or d.get("source_sha") != kernel_source_sha():
+    if d.get("kernel") != kernel or d.get("source_sha") != kernel_source_sha(sources):
         return None
     return d.get("traffic_bytes")
 
@@ -271,7 +272,10 @@ def prefill_bench(args):
                    "inter": s.inter, "n_routed": s.n_routed, "topk": s.topk, "m": m, "batches_cycled": nb,
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_gateup_pf",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("k_gateup_pf", "hbm_traffic_prefill_m512_dim4096.md",
+                                                 PREFILL_SOURCES) if m == 512 else None,
+                     "kernel": "k_gateup_pf",
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
                      "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
                                            float(np.percentile(k_ms["gateup"], 90) * 1e3)],
