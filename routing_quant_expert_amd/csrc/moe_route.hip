@@ -26,14 +26,14 @@ using front::shared_gu_rows;
 // [device_route.rs, fn parse_header] and, for the plan, the picks/weights.
 // ---------------------------------------------------------------------------
 template <int KPER>
-__device__ void select_token(const float* __restrict__ sc, const float* __restrict__ bias, int n_routed, int topk,
-                             int norm, float route_scale, int32_t* __restrict__ hd, int* picks_out, float* w_out,
+__device__ void select_token(const float (&sc)[KPER], const float (&bs)[KPER], int n_routed, int topk, int norm,
+                             float route_scale, int32_t* __restrict__ hd, int* picks_out, float* w_out,
                              int32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63;
   int picks[kMaxTopk];
   float wts[kMaxTopk];
   bool nan_any = false;
-  select_topk<KPER>(sc, bias, n_routed, topk, norm, route_scale, picks, wts, nan_any);
+  select_topk_from<KPER>(sc, bs, n_routed, topk, norm, route_scale, picks, wts, nan_any);
   int mypick = 0;
   float wv = 0.0f;
 #pragma unroll
@@ -61,55 +61,84 @@ __device__ void select_token(const float* __restrict__ sc, const float* __restri
   }
 }
 
+// Inclusive prefix sum of v over the 64 lanes by DPP: row_shr 1, 2, 4, 8
+// within each row of 16 lanes, then row_bcast:15 and row_bcast:31 across rows
+// (out-of-row sources and disabled rows add 0).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
-// Plan tables for m <= 8 tokens, one wave (pairs q = t*topk + r <= 64): the
-// valid (expert, token) pairs sorted by expert id then token, the distinct
-// experts, and per token its pairs in plan order (ascending id)
+// Plan tables for m <= 8 tokens, one wave, one lane per pick q = t*topk + r
+// (q < 64): the valid (expert, token) pairs sorted by expert id then token,
+// the distinct experts, and per token its pairs in plan order (ascending id)
 // [device_route.rs, fn device_route_check: weights and pointers in plan order].
+// An expert map in LDS (one word per expert id, emap >= 64*KPER words) first
+// collects each expert's token mask; a wave scan over the ids (lane l owns ids
+// KPER*l .. KPER*l + KPER-1) turns it into, per id, the number of pairs and of
+// distinct experts with a smaller id. A pair's position is then its expert's
+// pair count plus the tokens below it in the mask.
 // ---------------------------------------------------------------------------
+template <int KPER>
 __device__ void build_plan(const int* picks, const float* wts, const int* tok_ok, int m, int topk, PlanView plan,
-                           int* first_flag) {
+                           uint32_t* emap) {
+  static_assert(kMaxDecodeTokens <= 8, "token masks are 8 bits");
   const int lane = threadIdx.x & 63;
   const int P = m * topk;
   const bool mine = lane < P;
   const int t = mine ? lane / topk : 0;
   const bool valid = mine && tok_ok[t];
-  const int e = mine ? picks[lane] : 0;
-  int pos = 0, cnt = 0;
-  bool first = valid;
-  for (int q = 0; q < P; ++q) {
-    const int t2 = q / topk;
-    if (!tok_ok[t2]) continue;
-    const int e2 = picks[q];
-    if (e2 < e || (e2 == e && t2 < t)) ++pos;
-    if (e2 == e) ++cnt;
-    if (e2 == e && t2 < t) first = false;
-  }
-  if (mine) first_flag[lane] = first ? 1 : 0;
+  const int e = valid ? picks[lane] : 0;   // a disabled token's picks may be out of range
+#pragma unroll
+  for (int c = 0; c < KPER; ++c) emap[KPER * lane + c] = 0u;
   __builtin_amdgcn_wave_barrier();
-  int uid = 0;
-  for (int q = 0; q < P; ++q)
-    if (first_flag[q] && picks[q] < e) ++uid;
+  if (valid) atomicOr(&emap[e], 1u << t);
+  __builtin_amdgcn_wave_barrier();
+  // per id: token mask (bits 0-7), pairs below (bits 8-15), distinct experts below (bits 16-23)
+  uint32_t mk[KPER];
+  uint32_t own = 0;   // this lane's ids: pairs (low half) and distinct experts (high half)
+#pragma unroll
+  for (int c = 0; c < KPER; ++c) {
+    mk[c] = emap[KPER * lane + c];
+    own += (uint32_t)__popc(mk[c]) | (mk[c] ? 0x10000u : 0u);
+  }
+  const uint32_t incl = wave_incl_sum(own);
+  uint32_t run = incl - own;
+#pragma unroll
+  for (int c = 0; c < KPER; ++c) {
+    emap[KPER * lane + c] = mk[c] | (run & 0xffu) << 8 | ((run >> 16) & 0xffu) << 16;
+    run += (uint32_t)__popc(mk[c]) | (mk[c] ? 0x10000u : 0u);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t v = emap[e];
+  const uint32_t below = v & ((1u << t) - 1u);   // tokens below t that picked e
+  const int pos = (int)((v >> 8) & 0xffu) + __popc(below);
+  int rk = 0;   // rank of e among its token's picks
+  for (int r2 = 0; r2 < topk; ++r2) rk += __shfl(e, t * topk + r2) < e ? 1 : 0;
   if (valid) {
     plan.pair_tok()[pos] = t;
     plan.pair_expert()[pos] = e;
     plan.pair_w()[pos] = wts[lane];
-    if (first) {
+    if (below == 0) {
+      const int uid = (int)((v >> 16) & 0xffu);
       plan.u_expert()[uid] = e;
       plan.u_first()[uid] = pos;
-      plan.u_npairs()[uid] = cnt;
+      plan.u_npairs()[uid] = __popc(v & 0xffu);
     }
-    int rk = 0;
-    for (int r2 = 0; r2 < topk; ++r2) rk += picks[t * topk + r2] < e ? 1 : 0;
     plan.tok_pairs()[t * topk + rk] = pos;
   } else if (mine) {
     plan.tok_pairs()[lane] = -1;
   }
   const unsigned long long vb = __ballot(valid);
-  const unsigned long long fb = __ballot(mine && first);
   if (lane == 0) {
     *plan.n_pairs() = __popcll(vb);
-    *plan.n_u() = __popcll(fb);
+    *plan.n_u() = (int32_t)(__builtin_amdgcn_readlane((int)incl, 63) >> 16);
   }
 }
 
@@ -126,23 +155,31 @@ struct FrontArgs {
   int router_blocks, shared_blocks;
 };
 
-// Every token's selection (one wave per token, four waves) and the plan
-// [moe_v41.rs, fn route_from_logits; device_route.rs, fn device_route_check].
+// Every token's selection and the plan [moe_v41.rs, fn route_from_logits;
+// device_route.rs, fn device_route_check]: wave w of the four selects tokens
+// w and w + 4, with both rows' loads issued before either selection.
 template <int KPER>
 __device__ void select_all(const FrontArgs& a, const Ws& w) {
+  static_assert(kMaxDecodeTokens <= 8, "two tokens per wave");
   __shared__ int picks[64];
   __shared__ float wts[64];
   __shared__ int tok_ok[kMaxDecodeTokens];
-  __shared__ int first_flag[64];
+  __shared__ uint32_t emap[64 * KPER];
   const int wave = threadIdx.x >> 6;
   const int hw = 1 + 3 * a.topk;
-  for (int t = wave; t < a.m; t += 4) {
-    select_token<KPER>(w.scores + (int64_t)t * a.n_routed, a.bias, a.n_routed, a.topk, a.norm, a.route_scale,
-                       a.header + (int64_t)t * hw, picks + t * a.topk, wts + t * a.topk, w.status);
-    if ((threadIdx.x & 63) == 0) tok_ok[t] = 1;
-  }
+  const int t0 = wave, t1 = wave + 4;
+  float sc0[KPER], bs0[KPER], sc1[KPER], bs1[KPER];
+  select_load<KPER>(w.scores + (int64_t)min(t0, a.m - 1) * a.n_routed, a.bias, a.n_routed, sc0, bs0);
+  select_load<KPER>(w.scores + (int64_t)min(t1, a.m - 1) * a.n_routed, a.bias, a.n_routed, sc1, bs1);
+  if (t0 < a.m)
+    select_token<KPER>(sc0, bs0, a.n_routed, a.topk, a.norm, a.route_scale, a.header + (int64_t)t0 * hw,
+                       picks + t0 * a.topk, wts + t0 * a.topk, w.status);
+  if (t1 < a.m)
+    select_token<KPER>(sc1, bs1, a.n_routed, a.topk, a.norm, a.route_scale, a.header + (int64_t)t1 * hw,
+                       picks + t1 * a.topk, wts + t1 * a.topk, w.status);
+  if (threadIdx.x < a.m) tok_ok[threadIdx.x] = 1;
   __syncthreads();
-  if (wave == 0) build_plan(picks, wts, tok_ok, a.m, a.topk, w.plan, first_flag);
+  if (wave == 0) build_plan<KPER>(picks, wts, tok_ok, a.m, a.topk, w.plan, emap);
 }
 
 __global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
@@ -184,18 +221,21 @@ __global__ __launch_bounds__(64) void k_select(const float* __restrict__ scores,
                                                int n_routed, int topk, int norm, float route_scale,
                                                int32_t* __restrict__ header, int32_t* __restrict__ status) {
   const int t = blockIdx.x;
-  select_token<KPER>(scores + (int64_t)t * n_routed, bias, n_routed, topk, norm, route_scale,
-                     header + (int64_t)t * (1 + 3 * topk), nullptr, nullptr, status);
+  float sc[KPER], bs[KPER];
+  select_load<KPER>(scores + (int64_t)t * n_routed, bias, n_routed, sc, bs);
+  select_token<KPER>(sc, bs, n_routed, topk, norm, route_scale, header + (int64_t)t * (1 + 3 * topk), nullptr,
+                     nullptr, status);
 }
 
 // Plan tables from headers given by the caller (m <= 8): picks outside
 // [0, n_routed) or repeated within a token disable that token.
+template <int KPER>
 __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ header, int m, int topk, int n_routed,
                                                    PlanView plan, int32_t* __restrict__ status) {
   __shared__ int picks[64];
   __shared__ float wts[64];
   __shared__ int tok_ok[kMaxDecodeTokens];
-  __shared__ int first_flag[64];
+  __shared__ uint32_t emap[64 * KPER];
   const int lane = threadIdx.x;
   const int hw = 1 + 3 * topk;
   if (lane < m * topk) {
@@ -216,7 +256,7 @@ __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ h
     if (!ok) atomicOr(status, MOE_STATUS_BAD_PICK);
   }
   __builtin_amdgcn_wave_barrier();
-  build_plan(picks, wts, tok_ok, m, topk, plan, first_flag);
+  build_plan<KPER>(picks, wts, tok_ok, m, topk, plan, emap);
 }
 
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, int64_t n, float temp,
@@ -265,7 +305,10 @@ hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w
 }
 
 hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan_small, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
+  if (c.n_routed <= 384)
+    hipLaunchKernelGGL(k_plan_small<6>, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
+  else
+    hipLaunchKernelGGL(k_plan_small<16>, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
   return hipGetLastError();
 }
 

@@ -33,24 +33,33 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// The wave selects `topk` experts from scores[0..n_routed) (this token's row)
-// with bias. On return every lane holds the same picks[] (rank order) and
-// weights[]; nan_any tells whether any key was NaN. KPER = ceil(n_routed/64).
-// A round takes the wave maximum of the available keys' order bits, then the
-// smallest id holding that maximum (one ballot per register column, in id
-// order), which is exactly the pages' stable descending sort.
+// This lane's keys' inputs: scores and bias of experts lane + 64c. Every
+// load is issued before any is used (indices clamped, no branches), so a
+// wave can issue the loads of several tokens before selecting any of them.
 template <int KPER>
-__device__ __forceinline__ void select_topk(const float* __restrict__ scores, const float* __restrict__ bias,
-                                            int n_routed, int topk, int norm, float route_scale,
-                                            int (&picks)[kMaxTopk], float (&weights)[kMaxTopk], bool& nan_any) {
+__device__ __forceinline__ void select_load(const float* __restrict__ scores, const float* __restrict__ bias,
+                                            int n_routed, float (&sc)[KPER], float (&bs)[KPER]) {
   const int lane = threadIdx.x & 63;
-  float sc[KPER], bs[KPER];
 #pragma unroll
-  for (int c = 0; c < KPER; ++c) {   // every load issued before any is used (indices clamped, no branches)
+  for (int c = 0; c < KPER; ++c) {
     const int e = min(lane + 64 * c, n_routed - 1);
     sc[c] = scores[e];
     bs[c] = bias[e];
   }
+}
+
+// The wave selects `topk` experts from one token's scores (loaded by
+// select_load) with bias. On return every lane holds the same picks[] (rank
+// order) and weights[]; nan_any tells whether any key was NaN.
+// KPER = ceil(n_routed/64). A round takes the wave maximum of the available
+// keys' order bits, then the smallest id holding that maximum (one ballot per
+// register column, in id order), which is exactly the pages' stable
+// descending sort.
+template <int KPER>
+__device__ __forceinline__ void select_topk_from(const float (&sc)[KPER], const float (&bs)[KPER], int n_routed,
+                                                 int topk, int norm, float route_scale, int (&picks)[kMaxTopk],
+                                                 float (&weights)[kMaxTopk], bool& nan_any) {
+  const int lane = threadIdx.x & 63;
   uint32_t ko[KPER];
   uint32_t avail = 0;                // bit c: expert lane + 64c still available
   bool has_nan = false;
@@ -98,6 +107,16 @@ __device__ __forceinline__ void select_topk(const float* __restrict__ scores, co
 #pragma unroll
   for (int r = 0; r < kMaxTopk; ++r)
     if (r < topk) weights[r] = fmul(weights[r], route_scale);
+}
+
+// select_load + select_topk_from for one token's row of scores.
+template <int KPER>
+__device__ __forceinline__ void select_topk(const float* __restrict__ scores, const float* __restrict__ bias,
+                                            int n_routed, int topk, int norm, float route_scale,
+                                            int (&picks)[kMaxTopk], float (&weights)[kMaxTopk], bool& nan_any) {
+  float sc[KPER], bs[KPER];
+  select_load<KPER>(scores, bias, n_routed, sc, bs);
+  select_topk_from<KPER>(sc, bs, n_routed, topk, norm, route_scale, picks, weights, nan_any);
 }
 
 }  // namespace moe
