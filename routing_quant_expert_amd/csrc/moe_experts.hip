@@ -26,7 +26,11 @@ namespace {
 // every token that picked u, as four 16-row tiles (gate 0-15, up 0-15, gate
 // 16-31, up 16-31) through a ring of SLOTS LDS slots, the next tiles in flight
 // while one is computed. A row's NSB super-blocks go to NSB consecutive lanes
-// and are summed by a float64 butterfly.
+// (a lane group) and are summed by a float64 butterfly. With np tokens on the
+// expert (np <= 8), the 256/NSB lane groups are split into np_pad = the power
+// of two >= np token slots: group g takes token g % np_pad and, of each tile,
+// the rows r with r % RG == g / np_pad (RG = groups / np_pad). Each lane
+// thus loads its token's activation once and keeps it for every tile.
 // ---------------------------------------------------------------------------
 template <int NSB, int SLOTS>
 __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, const int8_t* __restrict__ xq,
@@ -36,26 +40,32 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
                                                 int8_t* __restrict__ hq, uint16_t* __restrict__ hd,
                                                 int32_t* __restrict__ hs, float L) {
   using G = GateUpGeom<NSB>;
+  static_assert(NSB <= 16 && kMaxDecodeTokens <= 8, "lane groups per token slot");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float gu[2][kMaxDecodeTokens][32];
   const int ngr = inter / 32;
   const int u = blockIdx.x / ngr, grp = blockIdx.x % ngr;
   if (u >= *plan.n_u()) return;
-  const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];
-  const int sb = threadIdx.x % NSB;
+  const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];   // 1 <= np <= 8
+  const int np_pad = np <= 1 ? 1 : (np <= 2 ? 2 : (np <= 4 ? 4 : 8));
+  constexpr int kGroups = 256 / NSB;
+  const int sb = threadIdx.x % NSB, g = threadIdx.x / NSB;
+  const int j = g % np_pad, rg = g / np_pad, RG = kGroups / np_pad;
+  const bool has = j < np;
   const uint8_t* ebase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride;
   auto tile_src = [&](int c) -> const uint8_t* {
     const uint64_t off = (c & 1) ? ex.up_off : ex.gate_off;
     return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
   };
   Act A;
-  if (np == 1) {
-    const int tok = plan.pair_tok()[first];
+  {
+    const int tok = plan.pair_tok()[first + (has ? j : 0)];
     load_act(A, xq + (int64_t)tok * dim, xd + (int64_t)tok * (dim / 32), xs + (int64_t)tok * (dim / 16), sb);
   }
   __syncthreads();   // completes the activation loads: the tile DMA below is all vmcnt sees
 #pragma unroll
-  for (int c = 0; c < SLOTS && c < 4; ++c) dma_tile<G::kKC>(tile_src(c), lds + c * G::kSlotBytes, G::kTileChunks);
+  for (int c = 0; c < SLOTS && c < 4; ++c)
+    dma_tile_exact<G::kKC>(tile_src(c), lds + c * G::kTileBytes, G::kTileChunks);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     // tiles issued after tile c and still allowed in flight
@@ -66,27 +76,18 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
     else if (after == 1) wait_vmcnt<1 * G::kKC>();
     else wait_vmcnt<0>();
     block_sync_lds();
-    const uint8_t* slot = lds + (c % SLOTS) * G::kSlotBytes;
+    const uint8_t* slot = lds + (c % SLOTS) * G::kTileBytes;
     const int mat = c & 1, r0 = 16 * (c >> 1);
-    for (int j = 0; j < np; ++j) {
-      if (np > 1) {
-        const int tok = plan.pair_tok()[first + j];
-        load_act(A, xq + (int64_t)tok * dim, xd + (int64_t)tok * (dim / 32), xs + (int64_t)tok * (dim / 16), sb);
-      }
-#pragma unroll
-      for (int it = 0; it < G::kIters; ++it) {
-        const int i = it * 256 + threadIdx.x;
-        const bool act = i < G::kItems;
-        const int row = i / NSB;
-        double part = act ? dot_q2k(slot + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
-        part = seg_sum_f64<NSB>(part);
-        if (act && sb == 0) gu[mat][j][r0 + row] = (float)part;
-      }
+    for (int row = rg; row - rg < 16; row += RG) {   // the same trip count on every lane
+      const bool on = has && row < 16;
+      double part = on ? dot_q2k(slot + row * G::kRowBytes + kQ2KBytes * sb, A) : 0.0;
+      part = seg_sum_f64<NSB>(part);
+      if (on && sb == 0) gu[mat][j][r0 + row] = (float)part;
     }
     if (c + SLOTS < 4) {
       wait_lgkm0();
       block_sync_lds();
-      dma_tile<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kSlotBytes, G::kTileChunks);
+      dma_tile_exact<G::kKC>(tile_src(c + SLOTS), lds + (c % SLOTS) * G::kTileBytes, G::kTileChunks);
     }
   }
   __syncthreads();
@@ -239,7 +240,7 @@ template <int NSB>
 hipError_t launch_gateup_t(const moe_experts& ex, int max_u, const moe_cfg& c, const Ws& w, hipStream_t s) {
   using G = GateUpGeom<NSB>;
   auto kern = k_gateup<NSB, kGateUpSlots>;
-  size_t shm = (size_t)kGateUpSlots * G::kSlotBytes;
+  const size_t shm = (size_t)kGateUpSlots * G::kTileBytes;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -281,7 +282,6 @@ hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const W
     case 4: err = launch_gateup_t<4>(ex, max_u, c, w, s); break;
     case 8: err = launch_gateup_t<8>(ex, max_u, c, w, s); break;
     case 16: err = launch_gateup_t<16>(ex, max_u, c, w, s); break;
-    case 32: err = launch_gateup_t<32>(ex, max_u, c, w, s); break;
     default: err = hipErrorInvalidValue; break;
   }
   return err;
@@ -297,7 +297,6 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
     case 4: err = launch_down_t<4>(ex, m, max_u, c, w, w2, s); break;
     case 8: err = launch_down_t<8>(ex, m, max_u, c, w, w2, s); break;
     case 16: err = launch_down_t<16>(ex, m, max_u, c, w, w2, s); break;
-    case 32: err = launch_down_t<32>(ex, m, max_u, c, w, w2, s); break;
     default: err = hipErrorInvalidValue; break;
   }
   return err;

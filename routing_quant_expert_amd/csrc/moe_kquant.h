@@ -48,6 +48,20 @@ __device__ __forceinline__ void dma_tile(const uint8_t* g, uint8_t* slot, int nc
   }
 }
 
+// As dma_tile, but the tile occupies exactly nchunks*16 bytes (nchunks >= 64,
+// no padding): an instruction that would run past the end copies the tile's
+// last 64 chunks instead (the same bytes again to the same place).
+template <int KC>
+__device__ __forceinline__ void dma_tile_exact(const uint8_t* g, uint8_t* slot, int nchunks) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int base = min(w * 64 + 256 * k, nchunks - 64);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * (base + lane)),
+                                     (__attribute__((address_space(3))) void*)(slot + 16 * base), 16, 0, 0);
+  }
+}
+
 // The activation of one token for the super-block `sb`: 64 words of int8
 // codes, the 16 per-16 code sums, the 8 q8_1 scales as float64.
 struct Act {
@@ -288,6 +302,7 @@ struct GateUpGeom {
   static constexpr int kTileChunks = 16 * kRowBytes / 16;        // 16 rows per tile
   static constexpr int kKC = (kTileChunks + 255) / 256;
   static constexpr int kSlotBytes = kKC * 4096;
+  static constexpr int kTileBytes = 16 * kRowBytes;               // an exact (unpadded) slot
   static constexpr int kItems = 16 * NSB;                         // (row, super-block) per tile
   static constexpr int kIters = (kItems + 255) / 256;
 };
