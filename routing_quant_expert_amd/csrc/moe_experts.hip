@@ -117,8 +117,10 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
 // ---------------------------------------------------------------------------
 // Down on Q3_K: workgroup = (distinct expert u, 32 output rows) for every token
 // that picked u (both 16-row tiles in flight at once); y[pair][row] =
-// RN32(the row's float64 sum). Workgroups past the routed ones compute the
-// shared expert's down rows: sd = W2s . sh, one wave per row, f32.
+// RN32(the row's float64 sum). The lane groups (NSB lanes per row) are split
+// across the expert's tokens as in the gate/up kernel, so each lane loads its
+// token's q8_1(h) once. The first workgroups compute the shared expert's down
+// rows (sd = W2s . sh in f32), alongside the routed ones.
 // ---------------------------------------------------------------------------
 template <int NSB>
 struct DownGeom {
@@ -126,8 +128,6 @@ struct DownGeom {
   static constexpr int kTileChunks = 16 * kRowBytes / 16;
   static constexpr int kKC = (kTileChunks + 255) / 256;
   static constexpr int kSlotBytes = kKC * 4096;
-  static constexpr int kItems = 32 * NSB;
-  static constexpr int kIters = (kItems + 255) / 256;
 };
 
 __device__ inline void bf16x8(uint4 v, float (&f)[8]) {
@@ -136,79 +136,124 @@ __device__ inline void bf16x8(uint4 v, float (&f)[8]) {
   for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
 }
 
+// Shared expert down rows for the m tokens: every token's sh is staged in LDS
+// once per workgroup; a wave computes kRw rows with all of their weight loads
+// in flight at once. Lane l sums positions 8l + 512c + (0..7) (c ascending) by
+// FMA for each token, then the 64 lanes combine by a butterfly.
+template <int NSB>
+struct SharedDownGeom {
+  static constexpr int kCh = NSB >= 2 ? NSB / 2 : 1;    // 16-byte chunks of a row per lane (inter = 256*NSB)
+  static constexpr int kRw = kCh >= 8 ? 2 : 4;          // rows per wave
+  static constexpr int kRows = 4 * kRw;                 // rows per workgroup
+};
+
+template <int NSB>
 __device__ void shared_down_rows(int blk, int m, int dim, int inter, const uint16_t* __restrict__ w2,
-                                 const uint16_t* __restrict__ sh, float* __restrict__ sd) {
-  const int r = blk * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= dim) return;
-  float p[kMaxDecodeTokens];
+                                 const uint16_t* __restrict__ sh, float* __restrict__ sd, uint8_t* lds) {
+  using S = SharedDownGeom<NSB>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rbase = blk * S::kRows + S::kRw * wave;   // dim is a multiple of kRows
+  uint4 wv[S::kRw][S::kCh];
 #pragma unroll
-  for (int t = 0; t < kMaxDecodeTokens; ++t) p[t] = 0.0f;
-  const uint16_t* row = w2 + (int64_t)r * inter;
-  for (int k = 8 * lane; k < inter; k += 512) {
-    float a[8];
-    bf16x8(load_nt16(row + k), a);
+  for (int c = 0; c < S::kCh; ++c) {
+    const int k = 8 * lane + 512 * c;
 #pragma unroll
-    for (int t = 0; t < kMaxDecodeTokens; ++t) {
-      if (t < m) {
-        float hv[8];
-        bf16x8(*reinterpret_cast<const uint4*>(sh + (int64_t)t * inter + k), hv);
+    for (int r = 0; r < S::kRw; ++r)
+      wv[r][c] = k < inter ? load_nt16(w2 + (int64_t)(rbase + r) * inter + k) : make_uint4(0, 0, 0, 0);
+  }
+  // every token's sh into LDS: each thread's pieces loaded together, then stored
+  constexpr int kStage = (kMaxDecodeTokens * 256 * NSB / 8 + 255) / 256;
+  uint16_t* shl = reinterpret_cast<uint16_t*>(lds);
+  const int n16 = m * inter / 8;
+  uint4 st[kStage];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[t] = __builtin_fmaf(a[j], hv[j], p[t]);
+  for (int k = 0; k < kStage; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    st[k] = i < n16 ? *reinterpret_cast<const uint4*>(sh + 8 * i) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n16) *reinterpret_cast<uint4*>(shl + 8 * i) = st[k];
+  }
+  __syncthreads();
+  float p[S::kRw][kMaxDecodeTokens];
+#pragma unroll
+  for (int r = 0; r < S::kRw; ++r)
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTokens; ++t) p[r][t] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < S::kCh; ++c) {
+    const int k = 8 * lane + 512 * c;
+    if (k < inter) {
+      float a[S::kRw][8];
+#pragma unroll
+      for (int r = 0; r < S::kRw; ++r) bf16x8(wv[r][c], a[r]);
+#pragma unroll
+      for (int t = 0; t < kMaxDecodeTokens; ++t) {
+        if (t < m) {
+          float hv[8];
+          bf16x8(*reinterpret_cast<const uint4*>(shl + t * inter + k), hv);
+#pragma unroll
+          for (int r = 0; r < S::kRw; ++r)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[r][t] = __builtin_fmaf(a[r][j], hv[j], p[r][t]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < kMaxDecodeTokens; ++t)
-    for (int s = 32; s >= 1; s >>= 1) p[t] += __shfl_xor(p[t], s);
-  if (lane < m) {
-    float v = 0.0f;
+  for (int r = 0; r < S::kRw; ++r) {
 #pragma unroll
     for (int t = 0; t < kMaxDecodeTokens; ++t)
-      if (t == lane) v = p[t];
-    sd[(int64_t)lane * dim + r] = v;
+      if (t < m)
+        for (int s = 32; s >= 1; s >>= 1) p[r][t] += __shfl_xor(p[r][t], s);
+    if (lane < m) {
+      float v = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMaxDecodeTokens; ++t)
+        if (t == lane) v = p[r][t];
+      sd[(int64_t)lane * dim + rbase + r] = v;
+    }
   }
 }
 
 template <int NSB>
 __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, const int8_t* __restrict__ hq,
                                               const uint16_t* __restrict__ hd, const int32_t* __restrict__ hs,
-                                              int dim, int inter, float* __restrict__ y, int routed_blocks, int m,
+                                              int dim, int inter, float* __restrict__ y, int shared_blocks, int m,
                                               const uint16_t* __restrict__ w2, const uint16_t* __restrict__ sh,
                                               float* __restrict__ sd) {
   using G = DownGeom<NSB>;
+  static_assert(NSB <= 16 && kMaxDecodeTokens <= 8, "lane groups per token slot");
   extern __shared__ __align__(16) uint8_t lds[];
-  if ((int)blockIdx.x >= routed_blocks) {
-    shared_down_rows(blockIdx.x - routed_blocks, m, dim, inter, w2, sh, sd);
+  if ((int)blockIdx.x < shared_blocks) {   // first, so that they run alongside the routed rows
+    shared_down_rows<NSB>(blockIdx.x, m, dim, inter, w2, sh, sd, lds);
     return;
   }
   const int ngr = dim / 32;
-  const int u = blockIdx.x / ngr, grp = blockIdx.x % ngr;
+  const int u = (blockIdx.x - shared_blocks) / ngr, grp = (blockIdx.x - shared_blocks) % ngr;
   if (u >= *plan.n_u()) return;
-  const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];
-  const int sb = threadIdx.x % NSB;
+  const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];   // 1 <= np <= 8
+  const int np_pad = np <= 1 ? 1 : (np <= 2 ? 2 : (np <= 4 ? 4 : 8));
+  constexpr int kGroups = 256 / NSB;
+  const int sb = threadIdx.x % NSB, g = threadIdx.x / NSB;
+  const int j = g % np_pad, rg = g / np_pad, RG = kGroups / np_pad;
+  const bool has = j < np;
+  const int pair = first + (has ? j : 0);
   const uint8_t* mbase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off;
   Act A;
-  if (np == 1) load_act(A, hq + (int64_t)first * inter, hd + (int64_t)first * (inter / 32),
-                        hs + (int64_t)first * (inter / 16), sb);
+  load_act(A, hq + (int64_t)pair * inter, hd + (int64_t)pair * (inter / 32), hs + (int64_t)pair * (inter / 16), sb);
   dma_tile<G::kKC>(mbase + (uint64_t)(32 * grp) * G::kRowBytes, lds, G::kTileChunks);
   dma_tile<G::kKC>(mbase + (uint64_t)(32 * grp + 16) * G::kRowBytes, lds + G::kSlotBytes, G::kTileChunks);
   wait_vmcnt<0>();
   block_sync_lds();
-  for (int j = 0; j < np; ++j) {
-    const int pair = first + j;
-    if (np > 1)
-      load_act(A, hq + (int64_t)pair * inter, hd + (int64_t)pair * (inter / 32), hs + (int64_t)pair * (inter / 16), sb);
-#pragma unroll
-    for (int it = 0; it < G::kIters; ++it) {
-      const int i = it * 256 + threadIdx.x;
-      const bool act = i < G::kItems;
-      const int row = i / NSB;                       // 0..31
-      const uint8_t* p = lds + (row >> 4) * G::kSlotBytes + (row & 15) * G::kRowBytes + kQ3KBytes * sb;
-      double part = act ? dot_q3k(p, A) : 0.0;
-      part = seg_sum_f64<NSB>(part);
-      if (act && sb == 0) y[(int64_t)pair * dim + 32 * grp + row] = (float)part;
-    }
+  for (int row = rg; row - rg < 32; row += RG) {   // the same trip count on every lane
+    const bool on = has && row < 32;
+    const int rr = on ? row : 0;
+    double part = on ? dot_q3k(lds + (rr >> 4) * G::kSlotBytes + (rr & 15) * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
+    part = seg_sum_f64<NSB>(part);
+    if (on && sb == 0) y[(int64_t)pair * dim + 32 * grp + row] = (float)part;
   }
 }
 
@@ -257,17 +302,20 @@ hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg&
                          hipStream_t s) {
   using G = DownGeom<NSB>;
   auto kern = k_down<NSB>;
-  size_t shm = (size_t)2 * G::kSlotBytes;
+  // the two routed tiles, or (shared rows) every token's sh
+  const size_t tiles = (size_t)2 * G::kSlotBytes, shs = (size_t)m * c.inter * 2;
+  const size_t shm = w2 && shs > tiles ? shs : tiles;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    const size_t most = (size_t)kMaxDecodeTokens * 256 * NSB * 2 > tiles ? (size_t)kMaxDecodeTokens * 256 * NSB * 2 : tiles;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int routed_blocks = max_u * (c.dim / 32);
-  const int shared_blocks = w2 ? (c.dim + 3) / 4 : 0;
+  const int shared_blocks = w2 ? c.dim / SharedDownGeom<NSB>::kRows : 0;
   MOE_LAUNCH(MOE_K_DOWN, kern, dim3(routed_blocks + shared_blocks), dim3(256), shm, s, ex, w.plan, w.hq, w.hd, w.hs,
-             c.dim, c.inter, w.y, routed_blocks, m, w2, w.sh, w.sd);
+             c.dim, c.inter, w.y, shared_blocks, m, w2, w.sh, w.sd);
   return hipGetLastError();
 }
 
