@@ -44,14 +44,10 @@ __device__ void plan_m1(int mode, bool writer, const float* __restrict__ scores,
   bool nan_any = false, ok = true;
   if (mode == 0) {
     int picks[kMaxTopk];
-    float wts[kMaxTopk];
-    select_topk<KPER>(scores, bias, n_routed, topk, norm, route_scale, picks, wts, nan_any);
+    select_topk<KPER>(scores, bias, n_routed, topk, norm, route_scale, picks, wv, nan_any);
 #pragma unroll
     for (int r = 0; r < kMaxTopk; ++r)
-      if (r == lane) {
-        pick = picks[r];
-        wv = wts[r];
-      }
+      if (r == lane) pick = picks[r];
   } else {
     const int li = min(lane, topk - 1);
     pick = header_in[1 + li];

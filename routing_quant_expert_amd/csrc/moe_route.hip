@@ -31,17 +31,13 @@ __device__ void select_token(const float (&sc)[KPER], const float (&bs)[KPER], i
                              int32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63;
   int picks[kMaxTopk];
-  float wts[kMaxTopk];
-  bool nan_any = false;
-  select_topk_from<KPER>(sc, bs, n_routed, topk, norm, route_scale, picks, wts, nan_any);
-  int mypick = 0;
   float wv = 0.0f;
+  bool nan_any = false;
+  select_topk_from<KPER>(sc, bs, n_routed, topk, norm, route_scale, picks, wv, nan_any);
+  int mypick = 0;
 #pragma unroll
   for (int r = 0; r < kMaxTopk; ++r)
-    if (r == lane) {
-      mypick = picks[r];
-      wv = wts[r];
-    }
+    if (r == lane) mypick = picks[r];
   int rank = 0;
 #pragma unroll
   for (int r = 0; r < kMaxTopk; ++r)

@@ -20,9 +20,10 @@ __device__ __forceinline__ uint32_t key_order_bits(float k) {
   return (u >> 31) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum of v over the 64 lanes, returned uniformly (from lane 63), by a
-// DPP reduction: quad_perm [1,0,3,2], [2,3,0,1], row_shr:4, row_shr:8,
-// row_bcast:15, row_bcast:31.
+// Maximum (minimum) of v over the 64 lanes, returned uniformly (from lane
+// 63), by a DPP reduction: quad_perm [1,0,3,2], [2,3,0,1], row_shr:4,
+// row_shr:8, row_bcast:15, row_bcast:31. Lanes without a source take the
+// neutral value (0 for the maximum, all ones for the minimum).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
@@ -31,6 +32,29 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0xb1, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x4e, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// This lane's best available key: the largest order bits, and of equal ones
+// the smallest column c (expert lane + 64c); bc = -1 when none is left.
+template <int KPER>
+__device__ __forceinline__ void lane_best(const uint32_t (&ko)[KPER], uint32_t avail, uint32_t& bko, int& bc) {
+  bko = 0u;
+  bc = -1;
+#pragma unroll
+  for (int c = KPER - 1; c >= 0; --c) {
+    const bool take = ((avail >> c) & 1u) && ko[c] >= bko;
+    bko = take ? ko[c] : bko;
+    bc = take ? c : bc;
+  }
 }
 
 // This lane's keys' inputs: scores and bias of experts lane + 64c. Every
@@ -50,15 +74,16 @@ __device__ __forceinline__ void select_load(const float* __restrict__ scores, co
 
 // The wave selects `topk` experts from one token's scores (loaded by
 // select_load) with bias. On return every lane holds the same picks[] (rank
-// order) and weights[]; nan_any tells whether any key was NaN.
-// KPER = ceil(n_routed/64). A round takes the wave maximum of the available
-// keys' order bits, then the smallest id holding that maximum (one ballot per
-// register column, in id order), which is exactly the pages' stable
-// descending sort.
+// order); lane r < topk holds in `weight` the weight of picks[r]; nan_any
+// tells whether any key was NaN. KPER = ceil(n_routed/64). Each lane keeps
+// its own best available key; a round takes the wave maximum of those, then
+// the smallest expert id holding it (a wave minimum over the lanes' best
+// ids), which is exactly the pages' stable descending sort. Only the winning
+// lane's best changes.
 template <int KPER>
 __device__ __forceinline__ void select_topk_from(const float (&sc)[KPER], const float (&bs)[KPER], int n_routed,
                                                  int topk, int norm, float route_scale, int (&picks)[kMaxTopk],
-                                                 float (&weights)[kMaxTopk], bool& nan_any) {
+                                                 float& weight, bool& nan_any) {
   const int lane = threadIdx.x & 63;
   uint32_t ko[KPER];
   uint32_t avail = 0;                // bit c: expert lane + 64c still available
@@ -72,51 +97,49 @@ __device__ __forceinline__ void select_topk_from(const float (&sc)[KPER], const 
     avail |= in ? (1u << c) : 0u;
   }
   nan_any = __any(has_nan);
+  uint32_t bko;
+  int bc;
+  lane_best<KPER>(ko, avail, bko, bc);
+  float sraw[kMaxTopk];   // the picks' unbiased scores, uniform
 #pragma unroll
   for (int r = 0; r < kMaxTopk; ++r) {
+    sraw[r] = 0.0f;
+    picks[r] = 0;
     if (r < topk) {
-      uint32_t best = 0;
+      const uint32_t top = wave_max_u32(bko);
+      const uint32_t id = wave_min_u32(bc >= 0 && bko == top ? (uint32_t)(lane + 64 * bc) : 0xFFFFFFFFu);
+      const int wl = (int)(id & 63u);
+      float s_best = sc[0];
 #pragma unroll
-      for (int c = 0; c < KPER; ++c) best = ((avail >> c) & 1u) ? max(best, ko[c]) : best;
-      const uint32_t top = wave_max_u32(best);
-      int id = -1;
-#pragma unroll
-      for (int c = 0; c < KPER; ++c) {
-        const unsigned long long b = __ballot(((avail >> c) & 1u) && ko[c] == top);
-        if (id < 0 && b) id = 64 * c + __builtin_ctzll(b);
-      }
-      const int wc = id >> 6, wl = id & 63;
-      float s_here = sc[0];
-#pragma unroll
-      for (int c = 1; c < KPER; ++c) s_here = (c == wc) ? sc[c] : s_here;
-      weights[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_here), wl));
-      picks[r] = id;
-      if (lane == wl) avail &= ~(1u << wc);
+      for (int c = 1; c < KPER; ++c) s_best = (c == bc) ? sc[c] : s_best;
+      sraw[r] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s_best), wl));
+      picks[r] = (int)id;
+      if (lane == wl) avail &= ~(1u << bc);
+      lane_best<KPER>(ko, avail, bko, bc);
     }
   }
+  float w = sraw[0];
+#pragma unroll
+  for (int r = 1; r < kMaxTopk; ++r) w = (r == lane) ? sraw[r] : w;
   if (norm && topk > 1) {
     float sum = 0.0f;
 #pragma unroll
     for (int r = 0; r < kMaxTopk; ++r)
-      if (r < topk) sum = fadd(sum, weights[r]);
+      if (r < topk) sum = fadd(sum, sraw[r]);
     sum = fadd(sum, 1e-20f);
-#pragma unroll
-    for (int r = 0; r < kMaxTopk; ++r)
-      if (r < topk) weights[r] = (float)((double)weights[r] / (double)sum);
+    w = (float)((double)w / (double)sum);
   }
-#pragma unroll
-  for (int r = 0; r < kMaxTopk; ++r)
-    if (r < topk) weights[r] = fmul(weights[r], route_scale);
+  weight = fmul(w, route_scale);
 }
 
 // select_load + select_topk_from for one token's row of scores.
 template <int KPER>
 __device__ __forceinline__ void select_topk(const float* __restrict__ scores, const float* __restrict__ bias,
                                             int n_routed, int topk, int norm, float route_scale,
-                                            int (&picks)[kMaxTopk], float (&weights)[kMaxTopk], bool& nan_any) {
+                                            int (&picks)[kMaxTopk], float& weight, bool& nan_any) {
   float sc[KPER], bs[KPER];
   select_load<KPER>(scores, bias, n_routed, sc, bs);
-  select_topk_from<KPER>(sc, bs, n_routed, topk, norm, route_scale, picks, weights, nan_any);
+  select_topk_from<KPER>(sc, bs, n_routed, topk, norm, route_scale, picks, weight, nan_any);
 }
 
 }  // namespace moe
