@@ -28,8 +28,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("moe_decode1.hip", "moe_kquant.h", "moe_math.h", "moe_internal.h")
-PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h")
+# a kernel's source file and every header it includes (the counters are tied to these)
+KERNEL_SOURCES = ("moe_decode1.hip", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h", "moe_select.h",
+                  "../../include/moe.h")
+PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h",
+                   "../../include/moe.h")
 
 
 def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
