@@ -115,13 +115,15 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
 }
 
 // ---------------------------------------------------------------------------
-// Down on Q3_K: workgroup = (distinct expert u, 32 output rows) for every token
-// that picked u (both 16-row tiles in flight at once); y[pair][row] =
+// Down on Q3_K: workgroup = (distinct expert u, 64 output rows) for every token
+// that picked u (all four 16-row tiles in flight at once); y[pair][row] =
 // RN32(the row's float64 sum). The lane groups (NSB lanes per row) are split
 // across the expert's tokens as in the gate/up kernel, so each lane loads its
 // token's q8_1(h) once. The first workgroups compute the shared expert's down
 // rows (sd = W2s . sh in f32), alongside the routed ones.
 // ---------------------------------------------------------------------------
+constexpr int kDownRows = 64;   // output rows per routed workgroup: 16-row tiles, all in flight at once
+
 template <int NSB>
 struct DownGeom {
   static constexpr int kRowBytes = NSB * kQ3KBytes;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, con
     shared_down_rows<NSB>(blockIdx.x, m, dim, inter, w2, sh, sd, lds);
     return;
   }
-  const int ngr = dim / 32;
+  const int ngr = dim / kDownRows;
   const int u = (blockIdx.x - shared_blocks) / ngr, grp = (blockIdx.x - shared_blocks) % ngr;
   if (u >= *plan.n_u()) return;
   const int e = plan.u_expert()[u], first = plan.u_first()[u], np = plan.u_npairs()[u];   // 1 <= np <= 8
@@ -244,16 +246,18 @@ __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, con
   const uint8_t* mbase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off;
   Act A;
   load_act(A, hq + (int64_t)pair * inter, hd + (int64_t)pair * (inter / 32), hs + (int64_t)pair * (inter / 16), sb);
-  dma_tile<G::kKC>(mbase + (uint64_t)(32 * grp) * G::kRowBytes, lds, G::kTileChunks);
-  dma_tile<G::kKC>(mbase + (uint64_t)(32 * grp + 16) * G::kRowBytes, lds + G::kSlotBytes, G::kTileChunks);
+#pragma unroll
+  for (int c = 0; c < kDownRows / 16; ++c)
+    dma_tile<G::kKC>(mbase + (uint64_t)(kDownRows * grp + 16 * c) * G::kRowBytes, lds + c * G::kSlotBytes,
+                     G::kTileChunks);
   wait_vmcnt<0>();
   block_sync_lds();
-  for (int row = rg; row - rg < 32; row += RG) {   // the same trip count on every lane
-    const bool on = has && row < 32;
+  for (int row = rg; row - rg < kDownRows; row += RG) {   // the same trip count on every lane
+    const bool on = has && row < kDownRows;
     const int rr = on ? row : 0;
     double part = on ? dot_q3k(lds + (rr >> 4) * G::kSlotBytes + (rr & 15) * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
     part = seg_sum_f64<NSB>(part);
-    if (on && sb == 0) y[(int64_t)pair * dim + 32 * grp + row] = (float)part;
+    if (on && sb == 0) y[(int64_t)pair * dim + kDownRows * grp + row] = (float)part;
   }
 }
 
@@ -303,7 +307,7 @@ hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg&
   using G = DownGeom<NSB>;
   auto kern = k_down<NSB>;
   // the two routed tiles, or (shared rows) every token's sh
-  const size_t tiles = (size_t)2 * G::kSlotBytes, shs = (size_t)m * c.inter * 2;
+  const size_t tiles = (size_t)(kDownRows / 16) * G::kSlotBytes, shs = (size_t)m * c.inter * 2;
   const size_t shm = w2 && shs > tiles ? shs : tiles;
   static bool attr_set = false;
   if (!attr_set) {
@@ -312,7 +316,7 @@ hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg&
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int routed_blocks = max_u * (c.dim / 32);
+  const int routed_blocks = max_u * (c.dim / kDownRows);
   const int shared_blocks = w2 ? c.dim / SharedDownGeom<NSB>::kRows : 0;
   MOE_LAUNCH(MOE_K_DOWN, kern, dim3(routed_blocks + shared_blocks), dim3(256), shm, s, ex, w.plan, w.hq, w.hd, w.hs,
              c.dim, c.inter, w.y, shared_blocks, m, w2, w.sh, w.sd);
