@@ -203,6 +203,32 @@ def test_layer_forward_matches_oracle(shape, m):
         assert rel_l2(sg[t], ref["shared"][t]["sg"]) < 1e-5
 
 
+@pytest.mark.parametrize("shape,rows", [(TINY, [0, 0, 0]), (TINY, [0, 0, 0, 0, 0, 1, 1, 2]),
+                                        (DS41, [0, 0, 0, 0, 0, 1, 1, 2]), (DS41, [0] * 8)])
+def test_layer_forward_repeated_tokens(shape, rows):
+    """Union path with experts shared by many tokens: repeated rows give each
+    expert np = 1..8 tokens (np = 3, 5, 6, 7 leave some of the power-of-two
+    token slots of the union kernels' lane groups empty)."""
+    dl = device_layer(shape)
+    c = dl.cfg
+    m = len(rows)
+    base = synth.tokens(dl.spec, 23, max(rows) + 1)
+    x_np = np.ascontiguousarray(base[rows])
+    x = torch.from_numpy(x_np).cuda()
+    ws = workspace(c, m)
+    out = torch.empty((m, shape.dim), dtype=torch.uint16, device="cuda")
+    out32 = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((m, 19), dtype=torch.int32, device="cuda")
+    say(f"layer_forward dim={shape.dim} rows={rows}")
+    R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr)
+    torch.cuda.synchronize()
+    o = out32.cpu().numpy()
+    _check_layer(dl, x_np, m, o, to_np_u16(out), hdr.cpu().numpy(), ws)
+    for t in range(1, m):   # equal rows give equal outputs, bit for bit
+        if rows[t] == rows[0]:
+            assert np.array_equal(o[t].view(np.uint32), o[0].view(np.uint32))
+
+
 @pytest.mark.parametrize("shape,m", [(TINY, 1), (TINY, 3), (DS41, 1), (DS41, 2)])
 def test_experts_decode_matches_oracle(shape, m):
     dl = device_layer(shape)
