@@ -303,7 +303,7 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--time-every", type=int, default=8, help="bracket every n-th step's timed kernel")
+    ap.add_argument("--time-every", type=int, default=32, help="bracket every n-th step's timed kernel")
     ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernels; 2..8: the "
                                                      "multi-token decode path on correlated rows; > 8: the "
                                                      "prefill path, Zipf-skewed bias)")
