@@ -241,27 +241,37 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
   int pos = e_first[e];
   const int hw = 1 + 3 * topk;
   const int64_t P = (int64_t)m * topk;
-  for (int64_t q0 = 0; q0 < P; q0 += 64) {
-    const int64_t q = q0 + lane;
-    int t = 0, r = 0;
-    bool hit = false;
-    if (q < P) {
-      t = (int)(q / topk);
-      r = (int)(q - (int64_t)t * topk);
-      hit = header[(int64_t)t * hw + 1 + r] == e && tok_ok[t] != 0;
+  // kB rows of 64 picks at a time: their loads are all issued before any
+  // ballot (the plan stores in between would otherwise keep each row's loads
+  // waiting behind the previous row's)
+  constexpr int kB = 16;
+  for (int64_t q0 = 0; q0 < P; q0 += 64 * kB) {
+    int pk[kB], ok[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int64_t q = min(q0 + 64 * b + lane, P - 1);
+      const int t = (int)(q / topk), r = (int)(q - (int64_t)t * topk);
+      pk[b] = header[(int64_t)t * hw + 1 + r];
+      ok[b] = tok_ok[t];
     }
-    const unsigned long long mask = __ballot(hit);
-    if (hit) {
-      const int p = pos + __popcll(mask & ((1ull << lane) - 1ull));
-      const int32_t* h = header + (int64_t)t * hw;
-      plan.pair_tok()[p] = t;
-      plan.pair_expert()[p] = e;
-      plan.pair_w()[p] = __builtin_bit_cast(float, h[1 + topk + r]);
-      int slot = 0;
-      for (int r2 = 0; r2 < topk; ++r2) slot += h[1 + r2] < e ? 1 : 0;
-      plan.tok_pairs()[(int64_t)t * topk + slot] = p;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int64_t q = q0 + 64 * b + lane;
+      const bool hit = q < P && pk[b] == e && ok[b] != 0;
+      const unsigned long long mask = __ballot(hit);
+      if (hit) {
+        const int t = (int)(q / topk), r = (int)(q - (int64_t)t * topk);
+        const int p = pos + __popcll(mask & ((1ull << lane) - 1ull));
+        const int32_t* h = header + (int64_t)t * hw;
+        plan.pair_tok()[p] = t;
+        plan.pair_expert()[p] = e;
+        plan.pair_w()[p] = __builtin_bit_cast(float, h[1 + topk + r]);
+        int slot = 0;
+        for (int r2 = 0; r2 < topk; ++r2) slot += h[1 + r2] < e ? 1 : 0;
+        plan.tok_pairs()[(int64_t)t * topk + slot] = p;
+      }
+      pos += __popcll(mask);
     }
-    pos += __popcll(mask);
   }
 }
 
