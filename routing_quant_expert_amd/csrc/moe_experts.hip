@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __r
   if (o.next) o.next[i] = bf16_rne(fadd(bf16_f32(o.resid[i]), acc));
 }
 
-constexpr int kGateUpSlots = 3;
+constexpr int kGateUpSlots = 2;
 
 template <int NSB>
 hipError_t launch_gateup_t(const moe_experts& ex, int max_u, const moe_cfg& c, const Ws& w, hipStream_t s) {
