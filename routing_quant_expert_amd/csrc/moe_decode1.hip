@@ -157,12 +157,26 @@ __global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
     if (wave == 0) {
       plan_m1<KPER>(a.mode, blk == 0, w.scores, a.bias, a.hdr_in, a.n_routed, a.topk, a.norm, a.route_scale,
                     a.hdr_out, w.plan, w.status, P);
-    } else {   // meanwhile the other waves stage the token's q8_1 activation and run a shared unit each
-      for (int i = threadIdx.x - 64; i < ActLds<NSB>::kChunks; i += 192)
-        act_piece_to_lds<NSB>(act_lds, w.xq, w.xs, w.xd, i);
-      if (wave - 1 < nu) {
+    } else {   // meanwhile the other waves stage the token's q8_1 activation and run a shared unit each;
+               // the unit's loads and the activation's are in flight together
+      const bool unit = wave - 1 < nu;
+      front::SharedUnitLoads SL;
+      if (unit) front::shared_gu_issue(u0 + wave - 1, a.x, a.dim, a.w1, a.w3, SL);
+      constexpr int kAP = (ActLds<NSB>::kChunks + 191) / 192;
+      u32x4 piece[kAP];
+#pragma unroll
+      for (int k = 0; k < kAP; ++k) {
+        const int i = min((int)threadIdx.x - 64 + 192 * k, ActLds<NSB>::kChunks - 1);
+        piece[k] = *reinterpret_cast<const u32x4*>(act_piece_src<NSB>(w.xq, w.xs, w.xd, i));
+      }
+#pragma unroll
+      for (int k = 0; k < kAP; ++k) {
+        const int i = (int)threadIdx.x - 64 + 192 * k;
+        if (i < ActLds<NSB>::kChunks) *reinterpret_cast<u32x4*>(act_piece_dst<NSB>(act_lds, i)) = piece[k];
+      }
+      if (unit) {
         float g, u;
-        front::shared_gu_unit(u0 + wave - 1, a.x, a.dim, a.w1, a.w3, g, u);
+        front::shared_gu_sum(SL, a.dim, g, u);
         if (lane == 0) {
           sgu[0][wave - 1] = g;
           sgu[1][wave - 1] = u;

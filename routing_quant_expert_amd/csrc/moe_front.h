@@ -191,29 +191,40 @@ __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, i
 // Shared expert gate/up of ONE token for hidden unit `un`, by one wave: the
 // same per-lane summation order and butterfly as shared_gu_rows, so the
 // values equal the multi-token ones. Every lane gets (g, u). dim <= 4096.
-__device__ inline void shared_gu_unit(int un, const uint16_t* __restrict__ x, int dim,
-                                      const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, float& g,
-                                      float& u) {
-  constexpr int kC = 8;   // 16-byte chunks per lane and row
+// In two parts, so that a caller can put other loads in flight between the
+// issue of the unit's loads and their use.
+struct SharedUnitLoads {
+  static constexpr int kC = 8;   // 16-byte chunks per lane and row
+  uint4 a[kC], b[kC], x[kC];
+};
+
+__device__ inline void shared_gu_issue(int un, const uint16_t* __restrict__ x, int dim,
+                                       const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
+                                       SharedUnitLoads& L) {
   const int lane = threadIdx.x & 63;
   const int nch = (dim + 511) / 512;
-  uint4 av[kC], bv[kC];
 #pragma unroll
-  for (int c = 0; c < kC; ++c) {
+  for (int c = 0; c < SharedUnitLoads::kC; ++c) {
     const int k = 512 * c + 8 * lane;
     const bool in = c < nch && k < dim;
-    av[c] = in ? load_nt16(w1 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
-    bv[c] = in ? load_nt16(w3 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
+    L.a[c] = in ? load_nt16(w1 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
+    L.b[c] = in ? load_nt16(w3 + (int64_t)un * dim + k) : make_uint4(0, 0, 0, 0);
+    L.x[c] = in ? *reinterpret_cast<const uint4*>(x + k) : make_uint4(0, 0, 0, 0);
   }
+}
+
+__device__ inline void shared_gu_sum(const SharedUnitLoads& L, int dim, float& g, float& u) {
+  const int lane = threadIdx.x & 63;
+  const int nch = (dim + 511) / 512;
   float pg = 0.0f, pu = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kC; ++c) {
+  for (int c = 0; c < SharedUnitLoads::kC; ++c) {
     const int k = 512 * c + 8 * lane;
     if (c < nch && k < dim) {
       float fa[8], fb[8], fx[8];
-      bf16x8(av[c], fa);
-      bf16x8(bv[c], fb);
-      bf16x8(*reinterpret_cast<const uint4*>(x + k), fx);
+      bf16x8(L.a[c], fa);
+      bf16x8(L.b[c], fb);
+      bf16x8(L.x[c], fx);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         pg = __builtin_fmaf(fa[j], fx[j], pg);
@@ -227,6 +238,14 @@ __device__ inline void shared_gu_unit(int un, const uint16_t* __restrict__ x, in
   }
   g = pg;
   u = pu;
+}
+
+__device__ inline void shared_gu_unit(int un, const uint16_t* __restrict__ x, int dim,
+                                      const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3, float& g,
+                                      float& u) {
+  SharedUnitLoads L;
+  shared_gu_issue(un, x, dim, w1, w3, L);
+  shared_gu_sum(L, dim, g, u);
 }
 
 }  // namespace front
