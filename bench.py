@@ -223,8 +223,9 @@ def prefill_bench(args):
     K = args.steps
     every = max(1, min(args.time_every, 2))
     nt = (K + every - 1) // every
-    kinds = (("router", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("down", R.MOE_K_DOWN),
-             ("shared_gu", R.MOE_K_SHARED_GU), ("shared_down", R.MOE_K_SHARED_DOWN))
+    kinds = (("router", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("gateup2", R.MOE_K_GATEUP2),
+             ("down", R.MOE_K_DOWN), ("down2", R.MOE_K_DOWN2), ("shared_gu", R.MOE_K_SHARED_GU),
+             ("shared_down", R.MOE_K_SHARED_DOWN))
     evs = {k: ev.create(2 * nt) for k, _ in kinds}
     L = R.lib()
     torch.cuda.synchronize()
@@ -245,6 +246,11 @@ def prefill_bench(args):
     n_u = np.array([len(np.unique(p)) for p in picks])
     counts = np.bincount(picks[0].reshape(-1), minlength=s.n_routed)
     us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
+    print("bench: gate/up small %.1f us, large %.1f us; down small %.1f us, large %.1f us" %
+          (us["gateup"], us["gateup2"], us["down"], us["down2"]), file=sys.stderr, flush=True)
+    us["gateup"] += us.pop("gateup2")
+    us["down"] += us.pop("down2")
+    kinds = tuple(kv for kv in kinds if kv[0] not in ("gateup2", "down2"))
     nu = float(n_u.mean())
     pairs = m * s.topk
     kbytes = {"router": s.n_routed * s.dim * 2, "gateup": nu * 2 * s.gate_bytes, "down": nu * s.down_bytes,

@@ -249,6 +249,10 @@ int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, floa
 #define MOE_K_ROUTER 3
 #define MOE_K_SHARED_GU 4    /* prefill: the shared expert's gate/up GEMM with its SwiGLU */
 #define MOE_K_SHARED_DOWN 5  /* prefill: the shared expert's down GEMM                    */
+#define MOE_K_GATEUP2 6      /* prefill: the gate/up kernel of the experts with more than 8 pairs
+                                (MOE_K_GATEUP is then the one of the experts with at most 8) */
+#define MOE_K_DOWN2 7        /* prefill: the down kernel of the experts with more than 8 pairs
+                                (MOE_K_DOWN is then the one of the experts with at most 8)   */
 int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end);
 
 

@@ -15,7 +15,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_STATUS_MISS = 1
 MOE_STATUS_NAN_KEY = 2
 MOE_STATUS_BAD_PICK = 4
-MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER, MOE_K_SHARED_GU, MOE_K_SHARED_DOWN = 1, 2, 3, 4, 5
+MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER, MOE_K_SHARED_GU, MOE_K_SHARED_DOWN, MOE_K_GATEUP2, MOE_K_DOWN2 = (
+    1, 2, 3, 4, 5, 6, 7)
 
 
 class MoeError(RuntimeError):

@@ -14,7 +14,7 @@ namespace moe {
 namespace {
 
 thread_local std::string g_err;
-constexpr int kTimedKernels = 6;   // MOE_K_* ids 1..5
+constexpr int kTimedKernels = 8;   // MOE_K_* ids 1..7
 thread_local hipEvent_t g_ev_begin[kTimedKernels] = {};
 thread_local hipEvent_t g_ev_end[kTimedKernels] = {};
 

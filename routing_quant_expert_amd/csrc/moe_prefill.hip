@@ -308,13 +308,21 @@ struct GateUpPfArgs {
 constexpr int kGuRows = 128;
 constexpr int kGuRowBytes = 96;
 constexpr int kGuW = kGuRows * kGuRowBytes;    // 12,288 B: 3072 dwords, 12 per thread
-constexpr int kATok = 272;                     // 256 codes + 16 bytes of padding per token
-constexpr int kGuA = 5 * 1024;                 // 16 * 68 = 1088 dwords rounded up to 5 per thread
+// The codes of a pass's T tokens, chunk-major: 16-byte chunk c (codes
+// 16c..16c+15 of the step's super-block) of token i at 16 * (T * c + i), so
+// that the lanes reading chunk c of T tokens read consecutive 16-byte pieces
+// (no bank conflicts, no padding).
+constexpr int kGuA = 16 * 256;                 // 16 tokens: 1024 dwords, 4 per thread
 constexpr int kGuD = 8 * kChunk * 8;           // 1,024 B: 256 dwords, 1 per thread
-constexpr int kGuSlot = kGuW + kGuA + kGuD;    // 18,432 B
-constexpr int kGuSlots = 4;
-constexpr int kGuDma = 12 + 5 + 1;             // dword DMAs per thread per step
-constexpr int kGuLds = kGuSlots * kGuSlot + 64;   // + the 16-entry code table
+constexpr int kGuSlot = kGuW + kGuA + kGuD;    // 17,408 B
+constexpr int kGuSlots = 3;
+constexpr int kGuLds = kGuSlots * kGuSlot + 64;   // + the 16-entry code table: 52,288 B, three workgroups per CU
+// Experts with at most 8 pairs run in a kernel of their own (one pass of 8
+// token rows, no 16-token result registers to carry).
+constexpr int kGuASmall = 8 * 256;
+constexpr int kGuSlotSmall = kGuW + kGuASmall + kGuD;   // 15,360 B
+constexpr int kGuSlotsSmall = 3;
+constexpr int kGuLdsSmall = kGuSlotsSmall * kGuSlotSmall + 64;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -328,48 +336,54 @@ __device__ __forceinline__ void dma_dword(__amdgpu_buffer_rsrc_t rsrc, uint8_t* 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)wave_base, 4, voff, soff, 0, 0);
 }
 
-template <int NSB, int G>
+// The ring: SLOTS slots of one super-block step each (the 128 rows, the
+// codes of the pass's tokens in NA dwords per thread, the block scales),
+// SLOTS - 1 steps in flight ahead of the one being computed.
+template <int NSB, int G, int SLOTS, int NA>
 __device__ __forceinline__ void gateup_pf_ring(const GateUpPfArgs& a, uint8_t* lds, const uint32_t* lut,
                                                __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ra,
                                                __amdgpu_buffer_rsrc_t rd, const uint32_t (&woff)[12],
-                                               const uint32_t (&aoff)[5], uint32_t doff, double (&y)[4 * G]) {
+                                               const uint32_t (&aoff)[NA], uint32_t doff, double (&y)[4 * G]) {
+  constexpr int kA = NA * 1024, kSlot = kGuW + kA + kGuD, kDma = 12 + NA + 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
   auto issue = [&](int s) {
-    uint8_t* base = lds + (s % kGuSlots) * kGuSlot + 256 * wave;
+    uint8_t* base = lds + (s % SLOTS) * kSlot + 256 * wave;
 #pragma unroll
     for (int k = 0; k < 12; ++k) dma_dword(rw, base + 1024 * k, woff[k], (uint32_t)s * kQ2KBytes);
 #pragma unroll
-    for (int k = 0; k < 5; ++k) dma_dword(ra, base + kGuW + 1024 * k, aoff[k], (uint32_t)s * 256);
-    dma_dword(rd, base + kGuW + kGuA, doff, (uint32_t)s * 64);
+    for (int k = 0; k < NA; ++k) dma_dword(ra, base + kGuW + 1024 * k, aoff[k], (uint32_t)s * 256);
+    dma_dword(rd, base + kGuW + kA, doff, (uint32_t)s * 64);
   };
 #pragma unroll
   for (int r = 0; r < 4 * G; ++r) y[r] = 0.0;
-  issue(0);
-  if (NSB > 1) issue(1);
-  if (NSB > 2) issue(2);
+#pragma unroll
+  for (int s = 0; s < SLOTS - 1; ++s)
+    if (s < NSB) issue(s);
 #pragma unroll 1
   for (int s = 0; s < NSB; ++s) {
-    const int after = NSB - 1 - s;   // steps issued after s (at most 2 here)
-    if (after >= 2) wait_vmcnt<2 * kGuDma>();
-    else if (after == 1) wait_vmcnt<kGuDma>();
+    const int after = min(NSB - 1 - s, SLOTS - 2);   // steps issued after s
+    if (after >= 2) wait_vmcnt<2 * kDma>();
+    else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
     block_sync_lds();   // every wave's share of step s has landed; every wave is done with step s - 1
-    if (s + 3 < NSB) issue(s + 3);   // into the slot step s - 1 used
-    const uint8_t* sl = lds + (s % kGuSlots) * kGuSlot;
+    if (s + SLOTS - 1 < NSB) issue(s + SLOTS - 1);   // into the slot step s - 1 used
+    const uint8_t* sl = lds + (s % SLOTS) * kSlot;
     const uint8_t* wr = sl + (32 * wave + (lane & 31)) * kGuRowBytes;
     const u32x4a4 scv = *reinterpret_cast<const u32x4a4*>(wr);
     const u32x4a4 qv0 = *reinterpret_cast<const u32x4a4*>(wr + 16 + 16 * hl);
     const u32x4a4 qv1 = *reinterpret_cast<const u32x4a4*>(wr + 48 + 16 * hl);
     const uint32_t ddw = *reinterpret_cast<const uint32_t*>(wr + 80);
-    const int8_t* ar = reinterpret_cast<const int8_t*>(sl + kGuW) + (lane & 15) * kATok + 16 * hl;
-    const double* dr = reinterpret_cast<const double*>(sl + kGuW + kGuA);
+    // token rows of the MFMA operand: 8G tokens, repeated (results of the repeats are not used)
+    constexpr int T = 4 * NA;   // tokens the slot holds
+    const int8_t* ar = reinterpret_cast<const int8_t*>(sl + kGuW) + 16 * (lane & (8 * G - 1)) + 16 * T * hl;
+    const double* dr = reinterpret_cast<const double*>(sl + kGuW + kA);
     double accS[4 * G], accM[4 * G];
 #pragma unroll
     for (int r = 0; r < 4 * G; ++r) accS[r] = accM[r] = 0.0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int j = t & 3;
-      const i32x4 A = *reinterpret_cast<const i32x4*>(ar + 32 * t);
+      const i32x4 A = *reinterpret_cast<const i32x4*>(ar + 32 * T * t);
       const u32x4a4 qw = t < 4 ? qv0 : qv1;
       const uint32_t sbyte = (scv[t >> 1] >> (8 * (2 * (t & 1) + hl))) & 0xFFu;
       const uint32_t lut_s = lut[sbyte & 15u];
@@ -397,16 +411,19 @@ __device__ __forceinline__ void gateup_pf_ring(const GateUpPfArgs& a, uint8_t* l
   }
 }
 
-template <int NSB>
-__global__ __launch_bounds__(256) void k_gateup_pf(GateUpPfArgs a) {
+// SMALL: the experts with at most 8 pairs (one pass, the small ring);
+// otherwise the others (passes of 16 pairs, the 4-slot ring).
+template <int NSB, bool SMALL>
+__device__ __forceinline__ void gateup_pf_body(const GateUpPfArgs& a, uint8_t* lds) {
   constexpr int dim = 256 * NSB, NB = 8 * NSB;
-  extern __shared__ __align__(16) uint8_t lds[];
-  uint32_t* lut = reinterpret_cast<uint32_t*>(lds + kGuSlots * kGuSlot);
+  constexpr int NA = SMALL ? 2 : 4;
+  uint32_t* lut = reinterpret_cast<uint32_t*>(lds + (SMALL ? kGuSlotsSmall * kGuSlotSmall : kGuSlots * kGuSlot));
   float (*gu)[kChunk][64] = reinterpret_cast<float (*)[kChunk][64]>(lds);   // after the k loop: [gate|up][tok][unit]
   const int ngr = a.inter / 64;
   const int u = blockIdx.x / ngr, grp = blockIdx.x % ngr;
   if (u >= *a.plan.n_u()) return;
   const int e = a.plan.u_expert()[u], first = a.plan.u_first()[u], np = a.plan.u_npairs()[u];
+  if (SMALL ? np > 8 : np <= 8) return;   // the other kernel's expert
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
   if (tid < 16) lut[tid] = ((uint32_t)tid * 0x030201u) << 8;   // bytes {0, sc, 2sc, 3sc}
   const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
@@ -427,22 +444,23 @@ __global__ __launch_bounds__(256) void k_gateup_pf(GateUpPfArgs a) {
   for (int c0 = 0; c0 < np; c0 += kChunk) {
     const int nt = min(kChunk, np - c0);
     const int* ptok = a.plan.pair_tok() + first + c0;
-    uint32_t aoff[5];
+    uint32_t aoff[NA];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {   // slot dword i = token * 68 + k (k < 64 real, else padding)
-      const int i = tid + 256 * k, tk = i / 68, dw = i % 68;
+    for (int k = 0; k < NA; ++k) {   // slot dword i: chunk i / (4T), token (i / 4) % T, dword i % 4 (T = 4 NA)
+      const int i = tid + 256 * k, c = i / (16 * NA), tk = (i >> 2) % (4 * NA);
       const int tok = ptok[min(tk, nt - 1)];
-      aoff[k] = (uint32_t)tok * dim + (tk < kChunk && dw < 64 ? 4u * dw : 0u);
+      aoff[k] = (uint32_t)tok * dim + 16u * c + 4u * (i & 3);
     }
     const int dt = tid >> 5, dtok = (tid & 31) >> 1;   // [block][token] float64, two dwords each
     const uint32_t doff = ((uint32_t)ptok[min(dtok, nt - 1)] * NB + dt) * 8u + 4u * (tid & 1);
     __syncthreads();   // the previous pass is done with the LDS (its SwiGLU phase reads gu)
     double y[4 * kGroups];
-    if (nt > 8) {
-      gateup_pf_ring<NSB, 2>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y);
+    if (!SMALL && nt > 8) {
+      gateup_pf_ring<NSB, 2, kGuSlots, NA>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y);
     } else {
       double y1[4];
-      gateup_pf_ring<NSB, 1>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y1);
+      if (SMALL) gateup_pf_ring<NSB, 1, kGuSlotsSmall, NA>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y1);
+      else gateup_pf_ring<NSB, 1, kGuSlots, NA>(a, lds, lut, rw, ra, rd, woff, aoff, doff, y1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[r] = y1[r];
 #pragma unroll
@@ -457,7 +475,7 @@ __global__ __launch_bounds__(256) void k_gateup_pf(GateUpPfArgs a) {
     __syncthreads();
     // SwiGLU + q8_1 of h: a half-wave per (token, 32 units = one q8_1 block), a lane per unit
 #pragma unroll 1
-    for (int job = 2 * wave + hl; job < 2 * kChunk; job += 8) {
+    for (int job = 2 * wave + hl; job < 2 * (SMALL ? 8 : kChunk); job += 8) {
       const int tt = job >> 1, hb = job & 1, unit = 32 * hb + (lane & 31);
       const bool live = tt < nt;
       const float gv = gu[0][tt][unit], uv = gu[1][tt][unit];
@@ -485,6 +503,18 @@ __global__ __launch_bounds__(256) void k_gateup_pf(GateUpPfArgs a) {
       }
     }
   }
+}
+
+template <int NSB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gateup_pf(GateUpPfArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  gateup_pf_body<NSB, false>(a, lds);
+}
+
+template <int NSB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gateup_pf_small(GateUpPfArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  gateup_pf_body<NSB, true>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -631,25 +661,30 @@ __global__ __launch_bounds__(256) void k_down_pf_direct(DownPfArgs a) {
 constexpr int kDnRows = 128;
 constexpr int kDnRowBytes = 112;
 constexpr int kDnW = kDnRows * kDnRowBytes;    // 14,336 B: 3584 dwords, 14 per thread
-constexpr int kDnSlot = kDnW + kGuA + kGuD;    // 20,480 B
 constexpr int kDnSlots = 3;
-constexpr int kDnDma = 14 + 5 + 1;
-constexpr int kDnLds = kDnSlots * kDnSlot + 512;   // + the 64-entry scale table
+// The pairs' h codes are chunk-major as in the gate/up ring (T = 16 pairs: 4
+// dwords per thread; T = 8 in the kernel of the experts with at most 8
+// pairs: 2 dwords per thread, 52,736 B of LDS, three workgroups per CU).
+template <int NA>
+constexpr int dn_slot() { return kDnW + NA * 1024 + kGuD; }
+template <int NA>
+constexpr int dn_lds() { return kDnSlots * dn_slot<NA>() + 512; }   // + the 64-entry scale table
 
-template <int NSB, int G>
+template <int NSB, int G, int NA>
 __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)[2], __amdgpu_buffer_rsrc_t rw,
                                              __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rd,
-                                             const uint32_t (&woff)[14], const uint32_t (&aoff)[5], uint32_t doff,
+                                             const uint32_t (&woff)[14], const uint32_t (&aoff)[NA], uint32_t doff,
                                              double (&y)[4 * G]) {
+  constexpr int kA = NA * 1024, kSlot = dn_slot<NA>(), kDnDma = 14 + NA + 1, T = 4 * NA;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
   auto issue = [&](int s) {
-    uint8_t* base = lds + (s % kDnSlots) * kDnSlot + 256 * wave;
+    uint8_t* base = lds + (s % kDnSlots) * kSlot + 256 * wave;
     const uint32_t wsoff = (uint32_t)(s * kQ3KBytes - 2 * (s & 1));   // dword-aligned window start
 #pragma unroll
     for (int k = 0; k < 14; ++k) dma_dword(rw, base + 1024 * k, woff[k], wsoff);
 #pragma unroll
-    for (int k = 0; k < 5; ++k) dma_dword(ra, base + kDnW + 1024 * k, aoff[k], (uint32_t)s * 256);
-    dma_dword(rd, base + kDnW + kGuA, doff, (uint32_t)s * 64);
+    for (int k = 0; k < NA; ++k) dma_dword(ra, base + kDnW + 1024 * k, aoff[k], (uint32_t)s * 256);
+    dma_dword(rd, base + kDnW + kA, doff, (uint32_t)s * 64);
   };
 #pragma unroll
   for (int r = 0; r < 4 * G; ++r) y[r] = 0.0;
@@ -661,7 +696,7 @@ __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)
     else wait_vmcnt<0>();
     block_sync_lds();   // step s landed everywhere; step s - 1 is done everywhere
     if (s + 2 < NSB) issue(s + 2);
-    const uint8_t* sl = lds + (s % kDnSlots) * kDnSlot;
+    const uint8_t* sl = lds + (s % kDnSlots) * kSlot;
     const uint8_t* blk = sl + (32 * wave + (lane & 31)) * kDnRowBytes + 2 * (s & 1);
     const u32x4a2 hmv = *reinterpret_cast<const u32x4a2*>(blk + 16 * hl);
     const u32x4a2 qv0 = *reinterpret_cast<const u32x4a2*>(blk + 32 + 16 * hl);
@@ -669,8 +704,8 @@ __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)
     const u32x2a2 sc01 = *reinterpret_cast<const u32x2a2*>(blk + 96);
     const uint32_t sc2 = *reinterpret_cast<const uint32_t __attribute__((aligned(2)))*>(blk + 104);
     const uint32_t dbits = *reinterpret_cast<const uint16_t*>(blk + 108);
-    const int8_t* ar = reinterpret_cast<const int8_t*>(sl + kDnW) + (lane & 15) * kATok + 16 * hl;
-    const double* dr = reinterpret_cast<const double*>(sl + kDnW + kGuA);
+    const int8_t* ar = reinterpret_cast<const int8_t*>(sl + kDnW) + 16 * (lane & (8 * G - 1)) + 16 * T * hl;
+    const double* dr = reinterpret_cast<const double*>(sl + kDnW + kA);
     double acc[4 * G];
 #pragma unroll
     for (int r = 0; r < 4 * G; ++r) acc[r] = 0.0;
@@ -693,7 +728,7 @@ __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)
         const uint32_t hb = hbit >= 2 ? (hmv[i] >> (hbit - 2)) : (hmv[i] << (2 - hbit));
         B[i] = (int)__builtin_amdgcn_perm(lut_hi, lut_lo, (hb & 0x04040404u) | q2);
       }
-      const i32x4 A = *reinterpret_cast<const i32x4*>(ar + 32 * t);
+      const i32x4 A = *reinterpret_cast<const i32x4*>(ar + 32 * T * t);
       const i32x16 S = mfma_i8(A, B);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -709,15 +744,17 @@ __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)
   }
 }
 
-template <int NSB>
-__global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
+// SMALL: the experts with at most 8 pairs; otherwise the others.
+template <int NSB, bool SMALL>
+__device__ __forceinline__ void down_pf_body(const DownPfArgs& a, uint8_t* lds) {
   constexpr int inter = 256 * NSB, NB = 8 * NSB;
-  extern __shared__ __align__(16) uint8_t lds[];
-  uint32_t (*lut)[2] = reinterpret_cast<uint32_t (*)[2]>(lds + kDnSlots * kDnSlot);
+  constexpr int NA = SMALL ? 2 : 4;
+  uint32_t (*lut)[2] = reinterpret_cast<uint32_t (*)[2]>(lds + kDnSlots * dn_slot<NA>());
   const int nrt = a.dim / kDnRows;
   const int u = blockIdx.x / nrt, rt = blockIdx.x % nrt;
   if (u >= *a.plan.n_u()) return;
   const int e = a.plan.u_expert()[u], first = a.plan.u_first()[u], np = a.plan.u_npairs()[u];
+  if (SMALL ? np > 8 : np <= 8) return;   // the other kernel's expert
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   q3k_lut_fill(lut);
   const uint8_t* wbase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride + a.ex.down_off;
@@ -734,18 +771,18 @@ __global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
   for (int c0 = 0; c0 < np; c0 += kChunk) {
     const int nt = min(kChunk, np - c0);
     const int p0 = first + c0;
-    uint32_t aoff[5];
+    uint32_t aoff[NA];
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const int i = tid + 256 * k, tk = i / 68, dw = i % 68;
-      aoff[k] = (uint32_t)(p0 + min(tk, nt - 1)) * inter + (tk < kChunk && dw < 64 ? 4u * dw : 0u);
+    for (int k = 0; k < NA; ++k) {   // slot dword i: chunk i / (4T), pair (i / 4) % T, dword i % 4 (T = 4 NA)
+      const int i = tid + 256 * k, c = i / (16 * NA), tk = (i >> 2) % (4 * NA);
+      aoff[k] = (uint32_t)(p0 + min(tk, nt - 1)) * inter + 16u * c + 4u * (i & 3);
     }
     const int dt = tid >> 5, dtok = (tid & 31) >> 1;
     const uint32_t doff = ((uint32_t)(p0 + min(dtok, nt - 1)) * NB + dt) * 8u + 4u * (tid & 1);
     __syncthreads();
-    if (nt > 8) {
+    if (!SMALL && nt > 8) {
       double y[8];
-      down_pf_ring<NSB, 2>(lds, lut, rw, ra, rd, woff, aoff, doff, y);
+      down_pf_ring<NSB, 2, NA>(lds, lut, rw, ra, rd, woff, aoff, doff, y);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int tt = tile_tok(r, lane);
@@ -753,7 +790,7 @@ __global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
       }
     } else {
       double y[4];
-      down_pf_ring<NSB, 1>(lds, lut, rw, ra, rd, woff, aoff, doff, y);
+      down_pf_ring<NSB, 1, NA>(lds, lut, rw, ra, rd, woff, aoff, doff, y);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = tile_tok(r, lane);
@@ -764,15 +801,31 @@ __global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
 }
 
 template <int NSB>
+__global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  down_pf_body<NSB, false>(a, lds);
+}
+
+template <int NSB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_down_pf_small(DownPfArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  down_pf_body<NSB, true>(a, lds);
+}
+
+template <int NSB>
 hipError_t launch_gateup_pf_t(const GateUpPfArgs& a, int max_u, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_gateup_pf<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        kGuLds);
     if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_gateup_pf_small<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kGuLdsSmall);
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(MOE_K_GATEUP, k_gateup_pf<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLds, s, a);
+  MOE_LAUNCH(MOE_K_GATEUP, k_gateup_pf_small<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLdsSmall, s, a);
+  MOE_LAUNCH(MOE_K_GATEUP2, k_gateup_pf<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLds, s, a);
   return hipGetLastError();
 }
 
@@ -785,11 +838,15 @@ hipError_t launch_down_pf_t(const DownPfArgs& a, int max_u, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_down_pf<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kDnLds);
+                                       dn_lds<4>());
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_down_pf_small<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            dn_lds<2>());
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(MOE_K_DOWN, k_down_pf<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), kDnLds, s, a);
+  MOE_LAUNCH(MOE_K_DOWN, k_down_pf_small<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), dn_lds<2>(), s, a);
+  MOE_LAUNCH(MOE_K_DOWN2, k_down_pf<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), dn_lds<4>(), s, a);
   return hipGetLastError();
   }
 }

@@ -288,3 +288,44 @@ def test_stack_forward_prefill(m):
             assert rel_l2(out_np[l, t], ref["out_f32"][t]) <= 1e-3
             assert np.abs(out_np[l, t] - ref["out_f32"][t]).max() <= 1e-2
         assert np.array_equal(xs_np[l + 1], olayer.residual(xs_np[l], out_np[l])), l
+
+
+@pytest.mark.parametrize("shape", [synth.Shape(dim=1024, inter=512), DS41], ids=lambda s: f"{s.dim}x{s.inter}")
+def test_prefill_group_sizes_at_the_kernel_split(shape):
+    """Experts with at most 8 pairs run in the small-group gate/up and down
+    kernels, the others in the 16-token-pass kernels. Rows repeated 8, 9 and
+    16 times (shuffled) give every expert of a row at least that many pairs:
+    groups of exactly 8, 9 and 16 when the rows' picks are disjoint, and of
+    17 or more (a 16-token pass and a remainder) where they overlap. Equal
+    rows must give equal results; each distinct row is checked against the
+    oracle (every pair's GEMV values and the layer output)."""
+    dl = dev_layer(shape, seed=3)
+    spec, c = dl.spec, dl.cfg
+    rows = synth.tokens(spec, 900, 3)
+    reps = np.repeat(np.arange(3), [8, 9, 16])
+    perm = np.random.default_rng(5).permutation(len(reps))
+    which = reps[perm]
+    x_np = rows[which]
+    m = len(which)
+    say(f"prefill group sizes dim={shape.dim} m={m}")
+    ws, out32, _, hdr = _run_layer(dl, x_np)
+    v = _ws_views(ws, c, m, shape)
+    tab = v["tab"]
+    sizes = sorted(int(n) for n in tab["u_npairs"][:tab["n_u"]])
+    say(f"  group sizes {sizes}")
+    assert max(sizes) >= 16 and min(sizes) >= 8 and any(n <= 8 for n in sizes) and any(n > 8 for n in sizes)
+    first = [int(np.flatnonzero(which == r)[0]) for r in range(3)]
+    ref = olayer.layer_forward(spec, rows)
+    for r, t0 in enumerate(first):
+        assert np.array_equal(hdr[t0], ref["header"][r])
+        for t in np.flatnonzero(which == r):
+            assert np.array_equal(out32[t].view(np.uint32), out32[t0].view(np.uint32)), (r, t)
+            assert np.array_equal(hdr[t], hdr[t0])
+        for k, e in enumerate(ref["tok"][r]["ids"]):
+            p = int(tab["tok_pairs"][t0][k])
+            ex = ref["tok"][r]["experts"][k]
+            f32_accept(v["g"][p], ex["g"], ex["near_g"], f"g row {r} e {e}")
+            f32_accept(v["u"][p], ex["u"], ex["near_u"], f"u row {r} e {e}")
+            f32_accept(v["y"][p], ex["y"], ex["near_y"], f"y row {r} e {e}")
+        want = ref["out_f32"][r]
+        assert rel_l2(out32[t0], want) <= 1e-3 and np.abs(out32[t0] - want).max() <= 1e-2, r
