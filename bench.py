@@ -245,12 +245,13 @@ def prefill_bench(args):
     picks = hdrs[:, :, 1:1 + s.topk].cpu().numpy()
     n_u = np.array([len(np.unique(p)) for p in picks])
     counts = np.bincount(picks[0].reshape(-1), minlength=s.n_routed)
-    us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
-    print("bench: gate/up small %.1f us, large %.1f us; down small %.1f us, large %.1f us" %
-          (us["gateup"], us["gateup2"], us["down"], us["down2"]), file=sys.stderr, flush=True)
-    us["gateup"] += us.pop("gateup2")
-    us["down"] += us.pop("down2")
+    # the gate/up and the down stage are two launches each: the experts with at most 8 pairs, then the others
+    split = {"gateup_small": float(k_ms["gateup"].mean()) * 1e3, "gateup_large": float(k_ms["gateup2"].mean()) * 1e3,
+             "down_small": float(k_ms["down"].mean()) * 1e3, "down_large": float(k_ms["down2"].mean()) * 1e3}
+    k_ms["gateup"] = k_ms["gateup"] + k_ms.pop("gateup2")
+    k_ms["down"] = k_ms["down"] + k_ms.pop("down2")
     kinds = tuple(kv for kv in kinds if kv[0] not in ("gateup2", "down2"))
+    us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
     nu = float(n_u.mean())
     pairs = m * s.topk
     kbytes = {"router": s.n_routed * s.dim * 2, "gateup": nu * 2 * s.gate_bytes, "down": nu * s.down_bytes,
@@ -282,14 +283,15 @@ def prefill_bench(args):
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("k_gateup_pf", "hbm_traffic_prefill_m512_dim4096.md",
+                     "traffic": measured_traffic("k_gateup_pf_small+k_gateup_pf", "hbm_traffic_prefill_m512_dim4096.md",
                                                  PREFILL_SOURCES) if m == 512 else None,
-                     "kernel": "k_gateup_pf",
+                     "kernel": "k_gateup_pf_small+k_gateup_pf",
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
                      "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
                                            float(np.percentile(k_ms["gateup"], 90) * 1e3)],
                      "int8_mfma_tops": kops["gateup"] / k_avg / 1e12, "int8_mfma_peak_tops": 5000.0},
-        "detail": {"kernels": kern, "union_experts_mean": nu, "largest_group": int(counts.max()),
+        "detail": {"kernels": kern, "split_launch_us": split, "union_experts_mean": nu,
+                   "largest_group": int(counts.max()),
                    "step_weight_bytes": step_bytes, "step_gbs": step_bytes / (wall / K) / 1e9,
                    "timed_kernels_us": sum(us.values()), "expert_kernels_gbs":
                        (kbytes["gateup"] + kbytes["down"]) / (us["gateup"] + us["down"]) / 1e3},

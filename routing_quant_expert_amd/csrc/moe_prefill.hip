@@ -321,7 +321,7 @@ constexpr int kGuLds = kGuSlots * kGuSlot + 64;   // + the 16-entry code table: 
 // token rows, no 16-token result registers to carry).
 constexpr int kGuASmall = 8 * 256;
 constexpr int kGuSlotSmall = kGuW + kGuASmall + kGuD;   // 15,360 B
-constexpr int kGuSlotsSmall = 3;
+constexpr int kGuSlotsSmall = 2;
 constexpr int kGuLdsSmall = kGuSlotsSmall * kGuSlotSmall + 64;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -362,7 +362,9 @@ __device__ __forceinline__ void gateup_pf_ring(const GateUpPfArgs& a, uint8_t* l
 #pragma unroll 1
   for (int s = 0; s < NSB; ++s) {
     const int after = min(NSB - 1 - s, SLOTS - 2);   // steps issued after s
-    if (after >= 2) wait_vmcnt<2 * kDma>();
+    static_assert(SLOTS - 2 <= 3 && 3 * kDma < 64, "vmcnt range");
+    if (after >= 3) wait_vmcnt<3 * kDma>();
+    else if (after == 2) wait_vmcnt<2 * kDma>();
     else if (after == 1) wait_vmcnt<kDma>();
     else wait_vmcnt<0>();
     block_sync_lds();   // every wave's share of step s has landed; every wave is done with step s - 1
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 }
 
 template <int NSB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gateup_pf_small(GateUpPfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup_pf_small(GateUpPfArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   gateup_pf_body<NSB, true>(a, lds);
 }
@@ -661,16 +663,17 @@ __global__ __launch_bounds__(256) void k_down_pf_direct(DownPfArgs a) {
 constexpr int kDnRows = 128;
 constexpr int kDnRowBytes = 112;
 constexpr int kDnW = kDnRows * kDnRowBytes;    // 14,336 B: 3584 dwords, 14 per thread
-constexpr int kDnSlots = 3;
+constexpr int kDnSlots = 3;        // experts with more than 8 pairs
+constexpr int kDnSlotsSmall = 2;   // the others: one step ahead, more workgroups per CU
 // The pairs' h codes are chunk-major as in the gate/up ring (T = 16 pairs: 4
 // dwords per thread; T = 8 in the kernel of the experts with at most 8
 // pairs: 2 dwords per thread, 52,736 B of LDS, three workgroups per CU).
 template <int NA>
 constexpr int dn_slot() { return kDnW + NA * 1024 + kGuD; }
 template <int NA>
-constexpr int dn_lds() { return kDnSlots * dn_slot<NA>() + 512; }   // + the 64-entry scale table
+constexpr int dn_lds() { return (NA == 2 ? kDnSlotsSmall : kDnSlots) * dn_slot<NA>() + 512; }   // + the scale table
 
-template <int NSB, int G, int NA>
+template <int NSB, int G, int NA, int SLOTS = (NA == 2 ? kDnSlotsSmall : kDnSlots)>
 __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)[2], __amdgpu_buffer_rsrc_t rw,
                                              __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rd,
                                              const uint32_t (&woff)[14], const uint32_t (&aoff)[NA], uint32_t doff,
@@ -678,7 +681,7 @@ __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)
   constexpr int kA = NA * 1024, kSlot = dn_slot<NA>(), kDnDma = 14 + NA + 1, T = 4 * NA;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
   auto issue = [&](int s) {
-    uint8_t* base = lds + (s % kDnSlots) * kSlot + 256 * wave;
+    uint8_t* base = lds + (s % SLOTS) * kSlot + 256 * wave;
     const uint32_t wsoff = (uint32_t)(s * kQ3KBytes - 2 * (s & 1));   // dword-aligned window start
 #pragma unroll
     for (int k = 0; k < 14; ++k) dma_dword(rw, base + 1024 * k, woff[k], wsoff);
@@ -688,15 +691,18 @@ __device__ __forceinline__ void down_pf_ring(uint8_t* lds, const uint32_t (*lut)
   };
 #pragma unroll
   for (int r = 0; r < 4 * G; ++r) y[r] = 0.0;
-  issue(0);
-  if (NSB > 1) issue(1);
+#pragma unroll
+  for (int s = 0; s < SLOTS - 1; ++s)
+    if (s < NSB) issue(s);
 #pragma unroll 1
   for (int s = 0; s < NSB; ++s) {
-    if (s + 1 < NSB) wait_vmcnt<kDnDma>();
+    const int after = min(NSB - 1 - s, SLOTS - 2);   // steps issued after s
+    static_assert(SLOTS - 2 <= 1, "wait cases");
+    if (after >= 1) wait_vmcnt<kDnDma>();
     else wait_vmcnt<0>();
     block_sync_lds();   // step s landed everywhere; step s - 1 is done everywhere
-    if (s + 2 < NSB) issue(s + 2);
-    const uint8_t* sl = lds + (s % kDnSlots) * kSlot;
+    if (s + SLOTS - 1 < NSB) issue(s + SLOTS - 1);   // into the slot step s - 1 used
+    const uint8_t* sl = lds + (s % SLOTS) * kSlot;
     const uint8_t* blk = sl + (32 * wave + (lane & 31)) * kDnRowBytes + 2 * (s & 1);
     const u32x4a2 hmv = *reinterpret_cast<const u32x4a2*>(blk + 16 * hl);
     const u32x4a2 qv0 = *reinterpret_cast<const u32x4a2*>(blk + 32 + 16 * hl);
@@ -749,7 +755,7 @@ template <int NSB, bool SMALL>
 __device__ __forceinline__ void down_pf_body(const DownPfArgs& a, uint8_t* lds) {
   constexpr int inter = 256 * NSB, NB = 8 * NSB;
   constexpr int NA = SMALL ? 2 : 4;
-  uint32_t (*lut)[2] = reinterpret_cast<uint32_t (*)[2]>(lds + kDnSlots * dn_slot<NA>());
+  uint32_t (*lut)[2] = reinterpret_cast<uint32_t (*)[2]>(lds + dn_lds<NA>() - 512);
   const int nrt = a.dim / kDnRows;
   const int u = blockIdx.x / nrt, rt = blockIdx.x % nrt;
   if (u >= *a.plan.n_u()) return;
@@ -807,7 +813,7 @@ __global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
 }
 
 template <int NSB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_down_pf_small(DownPfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_down_pf_small(DownPfArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   down_pf_body<NSB, true>(a, lds);
 }
