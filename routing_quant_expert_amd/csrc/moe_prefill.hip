@@ -663,11 +663,13 @@ __global__ __launch_bounds__(256) void k_down_pf_direct(DownPfArgs a) {
 constexpr int kDnRows = 128;
 constexpr int kDnRowBytes = 112;
 constexpr int kDnW = kDnRows * kDnRowBytes;    // 14,336 B: 3584 dwords, 14 per thread
-constexpr int kDnSlots = 3;        // experts with more than 8 pairs
-constexpr int kDnSlotsSmall = 2;   // the others: one step ahead, more workgroups per CU
+// Both down rings keep one step in flight ahead: the 16-pair kernel (at most
+// 168 VGPRs) then runs three workgroups per CU, the 8-pair one four.
+constexpr int kDnSlots = 2;        // experts with more than 8 pairs
+constexpr int kDnSlotsSmall = 2;   // the others
 // The pairs' h codes are chunk-major as in the gate/up ring (T = 16 pairs: 4
 // dwords per thread; T = 8 in the kernel of the experts with at most 8
-// pairs: 2 dwords per thread, 52,736 B of LDS, three workgroups per CU).
+// pairs: 2 dwords per thread).
 template <int NA>
 constexpr int dn_slot() { return kDnW + NA * 1024 + kGuD; }
 template <int NA>
@@ -807,7 +809,7 @@ __device__ __forceinline__ void down_pf_body(const DownPfArgs& a, uint8_t* lds) 
 }
 
 template <int NSB>
-__global__ __launch_bounds__(256) void k_down_pf(DownPfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_down_pf(DownPfArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   down_pf_body<NSB, false>(a, lds);
 }
