@@ -119,3 +119,26 @@ def test_library_swiglu_matches_oracle_on_host():
     g = np.concatenate([rng.normal(0, 2, 200_000), rng.uniform(-120, 20, 50_000)]).astype(np.float32)
     u = rng.normal(0, 4, g.size).astype(np.float32)
     assert np.array_equal(R.swiglu_host(g, u, 7.0).view(np.uint32), oracle.swiglu(g, u, 7.0).view(np.uint32))
+
+
+def test_empty_batch_is_rejected_by_every_entry_point():
+    """m = 0 is out of range for every call (MOE_EINVAL, checked before any
+    launch); so is a stack of zero layers."""
+    c = R.cfg_from_shape(synth.SHAPE_TINY)
+    ws = _FakePtr(1 << 20, n=1 << 30)
+    x0 = _FakePtr(4096, shape=(0, 512))
+    ex = R.Experts(1 << 20, 0, 0, 0, 0)
+    layer = R.Layer(8192, 16384, ex, 1 << 21, 1 << 22, 1 << 23)
+    calls = [
+        lambda: R.route_select(c, x0, _FakePtr(8192), _FakePtr(16384), _FakePtr(32768), ws, stream=0),
+        lambda: R.experts_decode(c, x0, _FakePtr(8192), ex, _FakePtr(16384), ws, stream=0),
+        lambda: R.experts_prefill(c, x0, _FakePtr(8192), ex, _FakePtr(16384), ws, stream=0),
+        lambda: R.layer_forward(c, layer, x0, _FakePtr(16384), ws, stream=0),
+        lambda: R.stack_forward(c, [layer], _FakePtr(4096, shape=(2, 0, 512)), ws, stream=0),
+        lambda: R.stack_forward(c, [], _FakePtr(4096, shape=(1, 1, 512)), ws, stream=0),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(R.MoeError) as ei:
+            call()
+        assert ei.value.code == -1, i
+    assert R.workspace_bytes(c, 0) == 0
