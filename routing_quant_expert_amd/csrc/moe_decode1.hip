@@ -141,12 +141,26 @@ __global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
   const int u0 = shared_only ? kUnitsRouted * routed_blocks + kUnitsShared * (int)blockIdx.x : kUnitsRouted * blk;
   const int nu = max(0, min(shared_only ? kUnitsShared : kUnitsRouted, a.shared_units - u0));
   if (shared_only) {
-    for (int k = wave; k < nu; k += 4) {
+    // wave k takes units k and k + 4, both units' loads in flight together
+    static_assert(kUnitsShared <= 8, "two units per wave");
+    front::SharedUnitLoads L0, L1;
+    const bool has0 = wave < nu, has1 = wave + 4 < nu;
+    if (has0) front::shared_gu_issue(u0 + wave, a.x, a.dim, a.w1, a.w3, L0);
+    if (has1) front::shared_gu_issue(u0 + wave + 4, a.x, a.dim, a.w1, a.w3, L1);
+    if (has0) {
       float g, u;
-      front::shared_gu_unit(u0 + k, a.x, a.dim, a.w1, a.w3, g, u);
+      front::shared_gu_sum(L0, a.dim, g, u);
       if (lane == 0) {
-        sgu[0][k] = g;
-        sgu[1][k] = u;
+        sgu[0][wave] = g;
+        sgu[1][wave] = u;
+      }
+    }
+    if (has1) {
+      float g, u;
+      front::shared_gu_sum(L1, a.dim, g, u);
+      if (lane == 0) {
+        sgu[0][wave + 4] = g;
+        sgu[1][wave + 4] = u;
       }
     }
     __syncthreads();
