@@ -259,15 +259,26 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
       const int64_t q = q0 + 64 * b + lane;
       const bool hit = q < P && pk[b] == e && ok[b] != 0;
       const unsigned long long mask = __ballot(hit);
+      const int t = (int)(min(q, P - 1) / topk), r = (int)(min(q, P - 1) - (int64_t)t * topk);
+      // the token's picks sit in lanes lane - r .. lane - r + topk - 1 of this row unless the token
+      // straddles two rows: its slot (rank of e among its picks) from the neighbours' registers
+      const bool in_row = lane - r >= 0 && lane - r + topk <= 64;
+      int slot = 0;
+#pragma unroll
+      for (int r2 = 0; r2 < kMaxTopk; ++r2) {
+        const int v = __shfl(pk[b], min(max(lane - r + r2, 0), 63));
+        if (r2 < topk) slot += v < e ? 1 : 0;
+      }
       if (hit) {
-        const int t = (int)(q / topk), r = (int)(q - (int64_t)t * topk);
         const int p = pos + __popcll(mask & ((1ull << lane) - 1ull));
         const int32_t* h = header + (int64_t)t * hw;
         plan.pair_tok()[p] = t;
         plan.pair_expert()[p] = e;
         plan.pair_w()[p] = __builtin_bit_cast(float, h[1 + topk + r]);
-        int slot = 0;
-        for (int r2 = 0; r2 < topk; ++r2) slot += h[1 + r2] < e ? 1 : 0;
+        if (!in_row) {
+          slot = 0;
+          for (int r2 = 0; r2 < topk; ++r2) slot += h[1 + r2] < e ? 1 : 0;
+        }
         plan.tok_pairs()[(int64_t)t * topk + slot] = p;
       }
       pos += __popcll(mask);
@@ -279,14 +290,14 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
 // Gate/up on Q2_K with int8 MFMA + clamped SwiGLU + q8_1 of h.
 // Workgroup = (distinct expert u, 64 hidden units): 128 weight rows (the 64
 // gate rows, then the 64 up rows), a wave per 32 rows over the whole k, up
-// to 16 of the expert's tokens per pass. Every operand streams through a
-// 4-slot LDS ring, one 256-weight super-block of k per slot, filled by
-// buffer-to-LDS dword DMA with the step's offset in a scalar register (no
-// VGPRs, no per-step address arithmetic); three steps are in flight while one
-// is computed. A slot holds the 128 rows' super-blocks (84 bytes padded to
-// 96 so that every field is 16-byte aligned), the 16 tokens' 256 q8_1 codes
-// (rows 272 bytes apart: 16-byte reads of 16 tokens hit distinct banks) and
-// their 8 block scales as float64 ([block][token]).
+// to 16 of the expert's tokens per pass (8 in the kernel of the experts with
+// at most 8 pairs). Every operand streams through an LDS ring (3 slots, or 2
+// in the small-group kernel), one 256-weight super-block of k per slot,
+// filled by buffer-to-LDS dword DMA with the step's offset in a scalar
+// register (no VGPRs, no per-step address arithmetic). A slot holds the 128
+// rows' super-blocks (84 bytes padded to 96 so that every field is 16-byte
+// aligned), the tokens' 256 q8_1 codes (chunk-major, below) and their 8
+// block scales as float64 ([block][token]).
 // ---------------------------------------------------------------------------
 struct GateUpPfArgs {
   moe_experts ex;
