@@ -244,22 +244,36 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
   // kB rows of 64 picks at a time: their loads are all issued before any
   // ballot (the plan stores in between would otherwise keep each row's loads
   // waiting behind the previous row's)
+  // (token, slot) of pick q advances by (64 / topk, 64 % topk) per row of 64: one division per batch
   constexpr int kB = 16;
+  const int dt = 64 / topk, dr = 64 - dt * topk;
   for (int64_t q0 = 0; q0 < P; q0 += 64 * kB) {
-    int pk[kB], ok[kB];
+    int pk[kB], ok[kB], wbits[kB], tb[kB], rb[kB];
+    const int qb = (int)q0 + lane;   // P = m * topk < 2^31
+    int t = qb / topk, r = qb - t * topk;
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int64_t q = min(q0 + 64 * b + lane, P - 1);
-      const int t = (int)(q / topk), r = (int)(q - (int64_t)t * topk);
-      pk[b] = header[(int64_t)t * hw + 1 + r];
-      ok[b] = tok_ok[t];
+      const int tc = min(t, m - 1);   // rows past the end read the last token (no hit there)
+      const int32_t* h = header + (int64_t)tc * hw;
+      pk[b] = h[1 + r];
+      wbits[b] = h[1 + topk + r];
+      ok[b] = tok_ok[tc];
+      tb[b] = t;
+      rb[b] = r;
+      t += dt;
+      r += dr;
+      if (r >= topk) {
+        r -= topk;
+        ++t;
+      }
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const int64_t q = q0 + 64 * b + lane;
       const bool hit = q < P && pk[b] == e && ok[b] != 0;
       const unsigned long long mask = __ballot(hit);
-      const int t = (int)(min(q, P - 1) / topk), r = (int)(min(q, P - 1) - (int64_t)t * topk);
+      if (mask == 0ull) continue;   // (wave-uniform) no pair of e in this row
+      const int t = tb[b], r = rb[b];
       // the token's picks sit in lanes lane - r .. lane - r + topk - 1 of this row unless the token
       // straddles two rows: its slot (rank of e among its picks) from the neighbours' registers
       const bool in_row = lane - r >= 0 && lane - r + topk <= 64;
@@ -274,7 +288,7 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
         const int32_t* h = header + (int64_t)t * hw;
         plan.pair_tok()[p] = t;
         plan.pair_expert()[p] = e;
-        plan.pair_w()[p] = __builtin_bit_cast(float, h[1 + topk + r]);
+        plan.pair_w()[p] = __builtin_bit_cast(float, wbits[b]);
         if (!in_row) {
           slot = 0;
           for (int r2 = 0; r2 < topk; ++r2) slot += h[1 + r2] < e ? 1 : 0;
