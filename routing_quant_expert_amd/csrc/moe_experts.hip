@@ -266,21 +266,48 @@ __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, con
 // acc = acc + w*y; then acc = acc + sd when the shared expert is present
 // [moe_v41.rs, fn shared_side: added after the routed experts].
 // ---------------------------------------------------------------------------
+// Four consecutive output elements per thread (16-byte loads of y and sd);
+// every element is summed exactly as one at a time: plan order, then sd.
 __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __restrict__ y, int dim, int topk,
                                                  const float* __restrict__ sd, LayerOut o) {
   const int t = blockIdx.y;
-  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int r = 4 * (blockIdx.x * 256 + threadIdx.x);   // dim is a multiple of 256
   if (r >= dim) return;
-  float acc = 0.0f;
-  for (int i = 0; i < topk; ++i) {
-    int p = plan.tok_pairs()[t * topk + i];
-    if (p >= 0) acc = fadd(acc, fmul(plan.pair_w()[p], y[(int64_t)p * dim + r]));
+  int pp[kMaxTopk];
+  float pw[kMaxTopk];
+#pragma unroll
+  for (int i = 0; i < kMaxTopk; ++i) {
+    pp[i] = i < topk ? plan.tok_pairs()[t * topk + i] : -1;
+    pw[i] = pp[i] >= 0 ? plan.pair_w()[pp[i]] : 0.0f;
   }
-  if (sd) acc = fadd(acc, sd[(int64_t)t * dim + r]);
-  const int64_t i = (int64_t)t * dim + r;
-  if (o.f32) o.f32[i] = acc;
-  if (o.bf16) o.bf16[i] = bf16_rne(acc);
-  if (o.next) o.next[i] = bf16_rne(fadd(bf16_f32(o.resid[i]), acc));
+  float4 yv[kMaxTopk];
+#pragma unroll
+  for (int i = 0; i < kMaxTopk; ++i)
+    yv[i] = pp[i] >= 0 ? *reinterpret_cast<const float4*>(y + (int64_t)pp[i] * dim + r) : make_float4(0, 0, 0, 0);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kMaxTopk; ++i) {
+    if (pp[i] >= 0) {
+      const float v[4] = {yv[i].x, yv[i].y, yv[i].z, yv[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fadd(acc[j], fmul(pw[i], v[j]));
+    }
+  }
+  const int64_t i0 = (int64_t)t * dim + r;
+  if (sd) {
+    const float4 s4 = *reinterpret_cast<const float4*>(sd + i0);
+    const float v[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fadd(acc[j], v[j]);
+  }
+  const bool f32_vec = o.f32 && (((uintptr_t)o.f32 & 15) == 0);   // the caller's buffer: any 4-byte alignment
+  if (f32_vec) *reinterpret_cast<float4*>(o.f32 + i0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (o.f32 && !f32_vec) o.f32[i0 + j] = acc[j];
+    if (o.bf16) o.bf16[i0 + j] = bf16_rne(acc[j]);
+    if (o.next) o.next[i0 + j] = bf16_rne(fadd(bf16_f32(o.resid[i0 + j]), acc[j]));
+  }
 }
 
 constexpr int kGateUpSlots = 2;
@@ -355,7 +382,7 @@ hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws&
 }
 
 hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, const LayerOut& o, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3((c.dim + 255) / 256, m), dim3(256), 0, s, w.plan, w.y, c.dim, c.topk, sd, o);
+  hipLaunchKernelGGL(k_combine, dim3((c.dim + 1023) / 1024, m), dim3(256), 0, s, w.plan, w.y, c.dim, c.topk, sd, o);
   return hipGetLastError();
 }
 
