@@ -239,6 +239,13 @@ def prefill_bench(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     k_ms = {k: np.array([ev.elapsed_ms(evs[k][2 * j], evs[k][2 * j + 1]) for j in range(nt)]) for k, _ in kinds}
+    # the expert stage: its four launches run on two streams (the experts with at most 8 pairs on the caller's,
+    # the others on the library's second stream), so its time is the span from the first launch's start to the
+    # last one's end, each taken against the router's start in the same step
+    def at(k, j, end):
+        return ev.elapsed_ms(evs["router"][2 * j], evs[k][2 * j + end])
+    span_ms = np.array([max(at(k, j, 1) for k in ("gateup", "gateup2", "down", "down2")) -
+                        min(at(k, j, 0) for k in ("gateup", "gateup2")) for j in range(nt)])
     for k, _ in kinds:
         ev.destroy(evs[k])
     wall = t1 - t0
@@ -261,8 +268,8 @@ def prefill_bench(args):
             "shared_down": 2 * m * s.dim * s.inter}
     kern = {k: {"avg_us": us[k], "weight_bytes": kbytes[k], "gbs": kbytes[k] / us[k] / 1e3,
                 "tops": kops[k] / us[k] / 1e6} for k, _ in kinds}
-    launch_bytes = kbytes["gateup"]
-    k_avg = us["gateup"] * 1e-6
+    launch_bytes = kbytes["gateup"] + kbytes["down"]
+    k_avg = float(span_ms.mean()) * 1e-3
     achieved = launch_bytes / k_avg / 1e9
     step_bytes = sum(kbytes.values())
     res = {
@@ -283,18 +290,18 @@ def prefill_bench(args):
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("k_gateup_pf_small+k_gateup_pf", "hbm_traffic_prefill_m512_dim4096.md",
+                     "traffic": measured_traffic("expert stage", "hbm_traffic_prefill_m512_dim4096.md",
                                                  PREFILL_SOURCES) if m == 512 else None,
-                     "kernel": "k_gateup_pf_small+k_gateup_pf",
+                     "kernel": "expert stage (k_gateup_pf_small, k_gateup_pf, k_down_pf_small, k_down_pf on two streams)",
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
-                     "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
-                                           float(np.percentile(k_ms["gateup"], 90) * 1e3)],
-                     "int8_mfma_tops": kops["gateup"] / k_avg / 1e12, "int8_mfma_peak_tops": 5000.0},
+                     "launch_p10_p90_us": [float(np.percentile(span_ms, 10) * 1e3),
+                                           float(np.percentile(span_ms, 90) * 1e3)],
+                     "int8_mfma_tops": (kops["gateup"] + kops["down"]) / k_avg / 1e12, "int8_mfma_peak_tops": 5000.0},
         "detail": {"kernels": kern, "split_launch_us": split, "union_experts_mean": nu,
                    "largest_group": int(counts.max()),
                    "step_weight_bytes": step_bytes, "step_gbs": step_bytes / (wall / K) / 1e9,
-                   "timed_kernels_us": sum(us.values()), "expert_kernels_gbs":
-                       (kbytes["gateup"] + kbytes["down"]) / (us["gateup"] + us["down"]) / 1e3},
+                   "kernel_us_sum": sum(us.values()), "expert_stage_us": k_avg * 1e6,
+                   "note": "kernels on the two streams overlap: the per-kernel times include the sharing"},
     }
     if not args.no_cpu:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)

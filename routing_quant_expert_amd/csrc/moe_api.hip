@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -31,6 +32,47 @@ int fail(int code, const char* fmt, const char* a = "", long long b = 0) {
 }
 
 bool pow2_upto16(int v) { return v >= 1 && v <= 16 && (v & (v - 1)) == 0; }
+
+// Prefill runs its independent launches on a second stream of the device
+// (created on first use, default priority, never destroyed): the shared
+// expert's two GEMMs from the start of the call (they need only x), the
+// expert kernels of the experts with more than 8 pairs once the grouping is
+// done; the caller's stream waits for them before the combine. The fork and
+// join are event record/wait pairs, so a graph capture of the caller's
+// stream takes the second stream's work in as well. Concurrent prefill calls
+// on one device from several host threads share this stream and its events
+// and are then ordered by them.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t start = nullptr, plan = nullptr, done = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+const SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&n.start, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.plan, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.done, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    ss = n;
+  }
+  return &ss;
+}
+
+// `after` (on stream `from`) happens before what is launched next on `to`.
+hipError_t fork_join(hipEvent_t after, hipStream_t from, hipStream_t to) {
+  hipError_t e = hipEventRecord(after, from);
+  if (e != hipSuccess) return e;
+  return hipStreamWaitEvent(to, after, 0);
+}
 
 // The single-token kernels: up to 6 picks (a wave each) and down rows of at
 // most 8 Q3_K super-blocks (each pick's 16-row tile is staged whole in LDS);
@@ -168,12 +210,21 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
   hipError_t e;
   FrontSelect sel{layer.bias, hdr};
   if (m > kMaxDecodeTokens) {   // prefill
+    const SideStream* ss = side_stream();
+    if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
+    if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
+    if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
     if ((e = launch_router_pf(x, m, layer.gate_w, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router_pf");
     if ((e = launch_select(layer.bias, m, c, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
     if ((e = launch_group(hdr, m, c, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
-    if ((e = launch_gateup_pf(layer.experts, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(layer.experts, m, c, w, s)) != hipSuccess) return hip_fail(e, "down_pf");
-    if ((e = launch_shared_pf(x, m, layer, c, w, s)) != hipSuccess) return hip_fail(e, "shared_pf");
+    // (inter = 256: one down kernel takes every expert, so both gate/up parts stay on the caller's stream)
+    const hipStream_t big = c.inter / 256 > 1 ? ss->s : s;
+    if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
+    if ((e = launch_gateup_pf(layer.experts, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(layer.experts, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
+    if ((e = launch_gateup_pf(layer.experts, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(layer.experts, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
+    if ((e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
     if ((e = launch_combine(m, c, w, w.sd, o, s)) != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
   }
@@ -283,10 +334,18 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
   int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  const SideStream* ss = side_stream();
+  if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
   if ((e = launch_router_pf(x, m, nullptr, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
   if ((e = launch_group(header, m, *cfg, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
-  if ((e = launch_gateup_pf(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-  if ((e = launch_down_pf(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "down_pf");
+  // (inter = 256: one down kernel takes every expert, so both gate/up parts stay on the caller's stream)
+  const hipStream_t big = cfg->inter / 256 > 1 ? ss->s : s;
+  if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
+  if ((e = launch_gateup_pf(*experts, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
+  if ((e = launch_down_pf(*experts, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
+  if ((e = launch_gateup_pf(*experts, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+  if ((e = launch_down_pf(*experts, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
+  if (big != s && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
   if ((e = launch_combine(m, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) != hipSuccess)
     return hip_fail(e, "combine");
   return MOE_OK;

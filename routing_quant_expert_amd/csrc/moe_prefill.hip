@@ -846,7 +846,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 }
 
 template <int NSB>
-hipError_t launch_gateup_pf_t(const GateUpPfArgs& a, int max_u, hipStream_t s) {
+hipError_t launch_gateup_pf_t(const GateUpPfArgs& a, int max_u, int part, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k_gateup_pf<NSB>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -857,15 +857,17 @@ hipError_t launch_gateup_pf_t(const GateUpPfArgs& a, int max_u, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(MOE_K_GATEUP, k_gateup_pf_small<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLdsSmall, s, a);
-  MOE_LAUNCH(MOE_K_GATEUP2, k_gateup_pf<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLds, s, a);
+  if (part == 0)
+    MOE_LAUNCH(MOE_K_GATEUP, k_gateup_pf_small<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLdsSmall, s, a);
+  else
+    MOE_LAUNCH(MOE_K_GATEUP2, k_gateup_pf<NSB>, dim3(max_u * (a.inter / 64)), dim3(256), kGuLds, s, a);
   return hipGetLastError();
 }
 
 template <int NSB>
-hipError_t launch_down_pf_t(const DownPfArgs& a, int max_u, hipStream_t s) {
-  if constexpr (NSB == 1) {   // one super-block of k: the kernel without the ring
-    MOE_LAUNCH(MOE_K_DOWN, k_down_pf_direct<NSB>, dim3(max_u * (a.dim / 128)), dim3(256), 0, s, a);
+hipError_t launch_down_pf_t(const DownPfArgs& a, int max_u, int part, hipStream_t s) {
+  if constexpr (NSB == 1) {   // one super-block of k: one kernel without the ring for every expert
+    if (part == 0) MOE_LAUNCH(MOE_K_DOWN, k_down_pf_direct<NSB>, dim3(max_u * (a.dim / 128)), dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
   static bool attr_set = false;
@@ -878,8 +880,10 @@ hipError_t launch_down_pf_t(const DownPfArgs& a, int max_u, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(MOE_K_DOWN, k_down_pf_small<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), dn_lds<2>(), s, a);
-  MOE_LAUNCH(MOE_K_DOWN2, k_down_pf<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), dn_lds<4>(), s, a);
+  if (part == 0)
+    MOE_LAUNCH(MOE_K_DOWN, k_down_pf_small<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), dn_lds<2>(), s, a);
+  else
+    MOE_LAUNCH(MOE_K_DOWN2, k_down_pf<NSB>, dim3(max_u * (a.dim / kDnRows)), dim3(256), dn_lds<4>(), s, a);
   return hipGetLastError();
   }
 }
@@ -905,28 +909,28 @@ hipError_t launch_group(const int32_t* header, int m, const moe_cfg& c, const Ws
   return hipGetLastError();
 }
 
-hipError_t launch_gateup_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
+hipError_t launch_gateup_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
   const int max_u = min(c.n_routed, m * c.topk);
   GateUpPfArgs a{ex, w.plan, w.xq, w.xd64, m, c.inter, c.swiglu_limit, w.g, w.u, w.h, w.hq, w.hd, w.hd64, w.hs};
   switch (c.dim / 256) {
-    case 1: return launch_gateup_pf_t<1>(a, max_u, s);
-    case 2: return launch_gateup_pf_t<2>(a, max_u, s);
-    case 4: return launch_gateup_pf_t<4>(a, max_u, s);
-    case 8: return launch_gateup_pf_t<8>(a, max_u, s);
-    case 16: return launch_gateup_pf_t<16>(a, max_u, s);
+    case 1: return launch_gateup_pf_t<1>(a, max_u, part, s);
+    case 2: return launch_gateup_pf_t<2>(a, max_u, part, s);
+    case 4: return launch_gateup_pf_t<4>(a, max_u, part, s);
+    case 8: return launch_gateup_pf_t<8>(a, max_u, part, s);
+    case 16: return launch_gateup_pf_t<16>(a, max_u, part, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_down_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
+hipError_t launch_down_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
   const int max_u = min(c.n_routed, m * c.topk);
   DownPfArgs a{ex, w.plan, w.hq, w.hd, w.hd64, m * c.topk, c.dim, w.y};
   switch (c.inter / 256) {
-    case 1: return launch_down_pf_t<1>(a, max_u, s);
-    case 2: return launch_down_pf_t<2>(a, max_u, s);
-    case 4: return launch_down_pf_t<4>(a, max_u, s);
-    case 8: return launch_down_pf_t<8>(a, max_u, s);
-    case 16: return launch_down_pf_t<16>(a, max_u, s);
+    case 1: return launch_down_pf_t<1>(a, max_u, part, s);
+    case 2: return launch_down_pf_t<2>(a, max_u, part, s);
+    case 4: return launch_down_pf_t<4>(a, max_u, part, s);
+    case 8: return launch_down_pf_t<8>(a, max_u, part, s);
+    case 16: return launch_down_pf_t<16>(a, max_u, part, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -329,3 +329,40 @@ def test_prefill_group_sizes_at_the_kernel_split(shape):
             f32_accept(v["y"][p], ex["y"], ex["near_y"], f"y row {r} e {e}")
         want = ref["out_f32"][r]
         assert rel_l2(out32[t0], want) <= 1e-3 and np.abs(out32[t0] - want).max() <= 1e-2, r
+
+
+def test_prefill_graph_capture_replays_equal_eager():
+    """Prefill forks work onto the library's second stream (the shared expert
+    from the start, the experts with more than 8 pairs after the grouping) and
+    joins before the combine. Captured in a graph on the caller's stream, the
+    fork and join come along: three replays, with eager work and
+    synchronisation between them, each give the eager output bit for bit."""
+    shape = synth.Shape(dim=1024, inter=512)
+    dl = dev_layer(shape, seed=3)
+    c = dl.cfg
+    m = 40
+    x = torch.from_numpy(synth.tokens(dl.spec, 300, m)).cuda()
+    ws = workspace(c, m)
+    out = torch.empty((m, shape.dim), dtype=torch.uint16, device="cuda")
+    out32 = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr)
+    torch.cuda.synchronize()
+    ref32, refh = out32.clone(), hdr.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr, stream=s.cuda_stream)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out32.fill_(0.0)
+        hdr.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out32.view(torch.int32), ref32.view(torch.int32)), rep
+        assert torch.equal(hdr, refh), rep
