@@ -35,13 +35,23 @@ PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_front.h", "moe_kquan
                    "../../include/moe.h")
 
 
+def source_text_key(text: bytes) -> bytes:
+    """A source file's code with its comments dropped and whitespace runs
+    collapsed: edits to comments leave a kernel's key unchanged."""
+    import re
+    tok = re.compile(rb'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+    code = tok.sub(lambda mt: mt.group(0) if mt.group(0)[:1] in (b'"', b"'") else b" ", text)
+    return re.sub(rb"\s+", b" ", code).strip()
+
+
 def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
-    """Hash of a kernel's sources (ties measured counters to a kernel version)."""
+    """Hash of a kernel's sources without their comments (ties measured
+    counters to a kernel version)."""
     import hashlib
     h = hashlib.sha256()
     for f in sources:
         with open(os.path.join(ROOT, "routing_quant_expert_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            h.update(source_text_key(fh.read()))
     return h.hexdigest()[:16]
 
 

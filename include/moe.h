@@ -16,11 +16,17 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller. The
- *     library allocates nothing on these paths and keeps no state between
- *     calls beyond what the caller's workspace holds.
+ *     library allocates no memory on these paths and keeps no state between
+ *     calls beyond what the caller's workspace holds. The prefill calls
+ *     (m > 8) create, on their first use on a device, one non-blocking
+ *     stream and three events of the library's own, kept until the process
+ *     ends: part of their work runs there, forked from and joined back into
+ *     `stream` by event record/wait pairs before the call's last launch, so
+ *     to the caller all of it is ordered on `stream` (a graph capture of
+ *     `stream` takes it in). The enqueue holds a per-device lock.
  *   - bf16 and fp16 values are passed as their uint16_t bit patterns.
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
- *     enqueues work on it and returns; nothing synchronises. Errors found on
+ *     enqueues work and returns; nothing synchronises. Errors found on
  *     the device (non-finite ranking keys, invalid picks) are reported in the
  *     header's status word and in the workspace status word, visible once
  *     the caller synchronises.

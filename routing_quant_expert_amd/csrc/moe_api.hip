@@ -39,21 +39,25 @@ bool pow2_upto16(int v) { return v >= 1 && v <= 16 && (v & (v - 1)) == 0; }
 // expert kernels of the experts with more than 8 pairs once the grouping is
 // done; the caller's stream waits for them before the combine. The fork and
 // join are event record/wait pairs, so a graph capture of the caller's
-// stream takes the second stream's work in as well. Concurrent prefill calls
-// on one device from several host threads share this stream and its events
-// and are then ordered by them.
+// stream takes the second stream's work in as well. A call holds the
+// device's lock while it enqueues (the launches are asynchronous, so only
+// for the enqueue), so that calls from several host threads cannot
+// interleave their record/wait pairs on the shared events; their side work
+// runs in the order the calls took the lock.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t start = nullptr, plan = nullptr, done = nullptr;
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;
+std::mutex g_side_mu[kMaxDevices];
 
-const SideStream* side_stream() {
+// The current device's side stream, created on first use, with its lock
+// taken into `hold`; nullptr (lock not taken) on failure.
+const SideStream* side_stream(std::unique_lock<std::mutex>& hold) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mu);
+  std::unique_lock<std::mutex> lock(g_side_mu[dev]);
   SideStream& ss = g_side[dev];
   if (!ss.s) {
     SideStream n;
@@ -64,6 +68,7 @@ const SideStream* side_stream() {
       return nullptr;
     ss = n;
   }
+  hold = std::move(lock);
   return &ss;
 }
 
@@ -210,7 +215,8 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
   hipError_t e;
   FrontSelect sel{layer.bias, hdr};
   if (m > kMaxDecodeTokens) {   // prefill
-    const SideStream* ss = side_stream();
+    std::unique_lock<std::mutex> hold;
+    const SideStream* ss = side_stream(hold);
     if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
     if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
     if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
@@ -334,7 +340,8 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
   int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  const SideStream* ss = side_stream();
+  std::unique_lock<std::mutex> hold;
+  const SideStream* ss = side_stream(hold);
   if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
   if ((e = launch_router_pf(x, m, nullptr, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
   if ((e = launch_group(header, m, *cfg, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
