@@ -158,6 +158,36 @@ def stack_bench(args):
     def step(i):
         R.stack_forward(cfg, layers, xs_all[i % nt_tok], ws, headers=hdrs)
 
+    if args.graph:
+        # one captured step per distinct input; before timing, each graph's
+        # first replay must give the eager step's residual stream and headers
+        ref = []
+        for t in range(nt_tok):
+            step(t)
+            torch.cuda.synchronize()
+            ref.append((xs_all[t].clone(), hdrs.clone()))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(side):
+            for t in range(nt_tok):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    R.stack_forward(cfg, layers, xs_all[t], ws, headers=hdrs, stream=side.cuda_stream)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        for t in range(nt_tok):
+            xs_all[t, 1:].fill_(0)
+            hdrs.fill_(0)
+            graphs[t].replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(xs_all[t], ref[t][0]) and torch.equal(hdrs, ref[t][1])):
+                sys.exit(f"bench: graph replay of input {t} differs from the eager step")
+        del ref
+
+        def step(i):   # noqa: F811
+            graphs[i % nt_tok].replay()
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -184,6 +214,7 @@ def stack_bench(args):
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": f"moe_stack{n}_decode_m{m}_dim4096_inter2048_e384_top6", "layers": n, "m": m,
+                   "launch": "graph replay" if args.graph else "eager",
                    "dim": s.dim, "inter": s.inter, "n_routed": s.n_routed, "topk": s.topk,
                    "resident_weight_bytes": n * (s.n_routed * s.expert_stride + 3 * s.inter * s.dim * 2 +
                                                  s.n_routed * s.dim * 2), "seed": args.seed},
@@ -334,6 +365,8 @@ def main():
                                                      "prefill path, Zipf-skewed bias)")
     ap.add_argument("--layers", type=int, default=1,
                     help="decode through a stack of this many layers per step (each its own seeded weights)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --layers: replay each step from a captured graph (checked against eager first)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the HBM byte counters)")
     args = ap.parse_args()

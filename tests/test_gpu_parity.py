@@ -385,6 +385,49 @@ def test_stack_forward_40_small_layers(m):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_stack_graph_capture_replays_equal_eager(m):
+    """The decode step through a stack, captured in a graph on a side stream:
+    three replays, with eager work and synchronisation between them, each
+    give the eager residual stream, outputs and headers bit for bit (the
+    kernels reset their own counters, so nothing needs a memset node)."""
+    n = 4
+    specs = [synth.LayerSpec(TINY, seed=9, layer=l) for l in range(n)]
+    say(f"graph of a {n}-layer stack dim={TINY.dim} m={m}")
+    dls = [DeviceLayer(sp) for sp in specs]
+    c = dls[0].cfg
+    layers = [d.layer for d in dls]
+    xs = torch.empty((n + 1, m, TINY.dim), dtype=torch.uint16, device="cuda")
+    xs[0] = torch.from_numpy(synth.tokens(specs[0], 11, m)).cuda()
+    out = torch.empty((n, m, TINY.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((n, m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    ws = workspace(c, m)
+    R.stack_forward(c, layers, xs, ws, out_f32=out, headers=hdr)
+    torch.cuda.synchronize()
+    ref_xs, ref_out, ref_hdr = xs.clone(), out.clone(), hdr.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            R.stack_forward(c, layers, xs, ws, out_f32=out, headers=hdr, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xs[1:].fill_(0)
+        out.fill_(0.0)
+        hdr.fill_(0)
+        R.stack_forward(c, layers[:1], xs[:2], ws)   # eager work between replays
+        torch.cuda.synchronize()
+        xs[1:].fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xs, ref_xs), rep
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), rep
+        assert torch.equal(hdr, ref_hdr), rep
+    del dls
+
+
 def test_stack_forward_40_full_size_layers():
     """Forty dim-4096 layers resident at once (~142 GB), one token; the
     oracle checks a sample of the layers, the residual stream every layer."""
