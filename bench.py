@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # a kernel's source file and every header it includes (the counters are tied to these)
 KERNEL_SOURCES = ("moe_decode1.hip", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h", "moe_select.h",
                   "../../include/moe.h")
+UNION_SOURCES = ("moe_experts.hip", "moe_kquant.h", "moe_math.h", "moe_internal.h", "../../include/moe.h")
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h",
                    "../../include/moe.h")
 
@@ -504,7 +505,9 @@ def main():
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(kernel) if m == 1 else None, "kernel": kernel,
+                     "traffic": (measured_traffic(kernel) if m == 1 else
+                                 measured_traffic(kernel, "hbm_traffic_decode_m8_dim4096.md", UNION_SOURCES) if m == 8
+                                 else None), "kernel": kernel,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
                      "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
                                            float(np.percentile(k_ms["gateup"], 90) * 1e3)]},
