@@ -36,6 +36,10 @@
  *     multiples of 256 with dim/256 and inter/256 powers of two <= 16 (the
  *     K-quant kernels give each 256-weight super-block of a row to one lane
  *     and stage whole row tiles in LDS). Anything else: MOE_EUNSUPPORTED.
+ *   - Tokens per call: 1 <= m <= 65535 with m * topk * max(dim, inter) < 2^31
+ *     (the kernels index the per-pair activations with 32-bit offsets); m < 1
+ *     is MOE_EINVAL, more is MOE_EUNSUPPORTED (also for the workspace calls,
+ *     where moe_workspace_bytes then returns 0).
  *   - Calls that share one workspace on one stream run in order; calls that
  *     overlap on different streams must use different workspaces.
  */
@@ -109,8 +113,11 @@ typedef struct moe_layer {
  *                        an expert's slot is its id) */
 int32_t moe_header_words(const moe_cfg* cfg);
 
-/* Bytes of workspace the calls below need for up to max_m tokens (>= 1).
- * Returns 0 for an invalid or unsupported cfg. The workspace must be
+/* Bytes of workspace the calls below need for up to max_m tokens (>= 1):
+ * the caller-owned counterpart of the pages' per-layer device buffers
+ * (logits, the group's q8_1 rows, gate/up/h/down outputs, the shared
+ * expert's sg/su/sh/sd, the routing header and plan tables) [moe_v41.rs,
+ * struct MoeV41]. Returns 0 for an invalid or unsupported cfg. The workspace must be
  * 256-byte aligned device memory. Its control region (the first 256 bytes,
  * for every m: the counter through which the last router workgroup of
  * moe_layer_forward learns that it is last) must be zero before the first
@@ -189,8 +196,10 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
  * as at m = 1), computed with the (token, expert) pairs grouped by expert
  * and each expert's blocks read once per 16 of its tokens: gate/up on Q2_K
  * and down on Q3_K as int8 MFMA tiles with exact integer block sums and a
- * float64 epilogue [moe_v41.rs, module doc; Kernels: prefill "group by
- * expert" with int8 MFMA K-quant tiles]. Arguments and error behaviour as
+ * float64 epilogue [moe_v41.rs, module doc; struct Kernels: gather,
+ * scatter_add, mmq_q2k_* / mmq_q3k_*; struct MoeV41: one expert group's
+ * gathered rows and q8_1 activations, group-major token rows and weights];
+ * the int8 MFMA tiling is this library's own. Arguments and error behaviour as
  * moe_experts_decode (x bf16 [m][dim], header int32 [m][moe_header_words],
  * y_routed f32 [m][dim]); the workspace is sized for m. */
 int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const int32_t* header,

@@ -96,6 +96,19 @@ int check_cfg(const moe_cfg* c) {
   return MOE_OK;
 }
 
+// Token counts the kernels index with 32-bit offsets and grid dimensions: at
+// most kMaxTokens tokens (the combine's grid rows), and every per-pair
+// activation buffer (m * topk rows of max(dim, inter) bytes) under 2^31 bytes
+// (the prefill kernels' buffer descriptors and offsets are 32-bit).
+int check_m(const moe_cfg& c, int64_t m) {
+  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  const int64_t width = c.dim > c.inter ? c.dim : c.inter;
+  if (m > kMaxTokens || m * c.topk * width >= ((int64_t)1 << 31))
+    return fail(MOE_EUNSUPPORTED, "too many tokens for one call%s (m %lld; at most 65535 and m*topk*max(dim,inter) < 2^31)",
+                "", m);
+  return MOE_OK;
+}
+
 uint64_t take(uint64_t& total, uint64_t bytes) {
   uint64_t off = total;
   total = (total + bytes + 255) & ~(uint64_t)255;
@@ -259,7 +272,7 @@ extern "C" {
 int32_t moe_header_words(const moe_cfg* cfg) { return cfg ? 1 + 3 * cfg->topk : 0; }
 
 size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m) {
-  if (check_cfg(cfg) != MOE_OK || max_m < 1) return 0;
+  if (check_cfg(cfg) != MOE_OK || check_m(*cfg, max_m) != MOE_OK) return 0;
   moe_ws_layout L;
   layout_of(*cfg, max_m, &L);
   return L.total;
@@ -267,7 +280,7 @@ size_t moe_workspace_bytes(const moe_cfg* cfg, int32_t max_m) {
 
 int moe_workspace_init(const moe_cfg* cfg, int32_t max_m, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
-  if (max_m < 1) return fail(MOE_EINVAL, "max_m must be >= 1%s (max_m %lld)", "", max_m);
+  if (int r = check_m(*cfg, max_m)) return r;
   moe_ws_layout L;
   if (int r = check_ws(*cfg, max_m, ws, ws_bytes, &L)) return r;
   hipError_t e = launch_zero(static_cast<uint8_t*>(ws) + L.ctl, 256, (hipStream_t)stream);
@@ -276,7 +289,8 @@ int moe_workspace_init(const moe_cfg* cfg, int32_t max_m, void* ws, size_t ws_by
 
 int moe_workspace_layout(const moe_cfg* cfg, int32_t max_m, moe_ws_layout* out) {
   if (int r = check_cfg(cfg)) return r;
-  if (!out || max_m < 1) return fail(MOE_EINVAL, "layout output NULL or max_m < 1%s%lld");
+  if (!out) return fail(MOE_EINVAL, "layout output is NULL%s%lld");
+  if (int r = check_m(*cfg, max_m)) return r;
   layout_of(*cfg, max_m, out);
   return MOE_OK;
 }
@@ -285,7 +299,7 @@ int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uin
                      float* logits, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
   if (!x || !gate_w || !bias || !header) return fail(MOE_EINVAL, "x, gate_w, bias and header must be non-NULL%s%lld");
-  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  if (int r = check_m(*cfg, m)) return r;
   if (!a16(x) || !a16(gate_w)) return fail(MOE_EINVAL, "x and gate_w must be 16-byte aligned%s%lld");
   moe_ws_layout L;
   if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
@@ -331,7 +345,7 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
                         const moe_experts* experts, float* y_routed, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
   if (!x || !header || !y_routed) return fail(MOE_EINVAL, "x, header and y_routed must be non-NULL%s%lld");
-  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  if (int r = check_m(*cfg, m)) return r;
   if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
   if (int r = check_experts(experts)) return r;
   moe_ws_layout L;
@@ -363,7 +377,7 @@ int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t
   if (int r = check_cfg(cfg)) return r;
   if (!x || !out_bf16) return fail(MOE_EINVAL, "x and out_bf16 must be non-NULL%s%lld");
   if (int r = check_layer(layer)) return r;
-  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  if (int r = check_m(*cfg, m)) return r;
   if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
   moe_ws_layout L;
   if (int r = check_ws(*cfg, m, ws, ws_bytes, &L)) return r;
@@ -378,7 +392,7 @@ int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_lay
   if (int r = check_cfg(cfg)) return r;
   if (!layers || !xs) return fail(MOE_EINVAL, "layers and xs must be non-NULL%s%lld");
   if (n_layers < 1) return fail(MOE_EINVAL, "n_layers must be >= 1%s (n_layers %lld)", "", n_layers);
-  if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
+  if (int r = check_m(*cfg, m)) return r;
   if (!a16(xs) || ((int64_t)m * cfg->dim * 2) % 16) return fail(MOE_EINVAL, "xs must be 16-byte aligned%s%lld");
   for (int l = 0; l < n_layers; ++l)
     if (int r = check_layer(&layers[l])) return r;

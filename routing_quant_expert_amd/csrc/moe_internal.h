@@ -12,6 +12,7 @@
 namespace moe {
 
 constexpr int kMaxDecodeTokens = 8;   // the union-of-experts decode path
+constexpr int kMaxTokens = 65535;      // tokens of one call (see check_m)
 constexpr int kMaxTopk = 8;
 constexpr int kMaxTopkM1 = 6;   // the single-token kernels: one wave per pick + two shared-expert waves in 512 threads
 constexpr int kMaxRouted = 1024;

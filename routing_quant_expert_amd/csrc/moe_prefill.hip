@@ -1,5 +1,8 @@
 // Prefill: the layer for many tokens at once (A9) [moe_v41.rs, module doc;
-// Kernels: the batched MoE path, "group by expert, int8 MFMA K-quant tiles"].
+// struct Kernels: gather, scatter_add and the mmq_q2k_* / mmq_q3k_* handles;
+// struct MoeV41: the gathered rows and q8_1 activations of one expert group,
+// the group-major token rows and weights]. The int8 MFMA tiles below are this
+// library's own design for CDNA4.
 //
 //  * k_router_pf: the router GEMV and scores with every (row, 8-token group)
 //    pair as its own wave (the per-row summation order of the decode router,

@@ -88,3 +88,24 @@ def oracle_header(spec, x_np, bias=None):
     lg = oracle.router_logits(x_np, synth.gate_w(spec))
     hdr, sc = oracle.select(spec.shape, lg, synth.bias(spec) if bias is None else bias)
     return lg, hdr, sc
+
+
+def check_combine_bits(ws, layout: dict, tab: dict, m: int, topk: int, out_f32: np.ndarray, with_shared: bool,
+                       tokens=None):
+    """The combine order, bit for bit at any size: each token's f32 output
+    must equal the oracle's combine applied to the device's own per-pair
+    expert outputs y (in plan order, ascending expert id) with the plan
+    weights, and then the device's own shared-expert output sd added after
+    the routed sum [moe_v41.rs, fn shared_side]. The inputs are the device's,
+    so no rounding of the GEMVs can blur a wrong summation order."""
+    P, dim = layout["max_pairs"], out_f32.shape[1]
+    y = ws_array(ws, layout, "y", np.float32, P * dim).reshape(P, dim)
+    sd = ws_array(ws, layout, "sd", np.float32, m * dim).reshape(m, dim) if with_shared else None
+    for t in (range(m) if tokens is None else tokens):
+        pairs = [int(p) for p in tab["tok_pairs"][t][:topk] if p >= 0]
+        ys = np.stack([y[p] for p in pairs])
+        w = np.array([tab["pair_w"][p] for p in pairs], np.float32)
+        want, _ = oracle.combine(ys, w, None if sd is None else sd[t])
+        got = np.ascontiguousarray(out_f32[t], np.float32)
+        bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+        assert bad.size == 0, f"combine of token {t}: {bad.size} outputs differ, first at {bad[:4]}"

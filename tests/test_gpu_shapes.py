@@ -57,3 +57,56 @@ def test_layer_forward_other_widths(shape):
     finally:
         del dl
         torch.cuda.empty_cache()
+
+
+ROUTING = [dict(n_routed=100, topk=1, norm_topk_prob=False), dict(n_routed=100, topk=8, norm_topk_prob=True),
+           dict(n_routed=1024, topk=8, norm_topk_prob=False), dict(n_routed=1024, topk=5, norm_topk_prob=True),
+           dict(n_routed=64, topk=2, norm_topk_prob=True)]
+
+
+@pytest.mark.parametrize("routing", ROUTING, ids=lambda r: f"e{r['n_routed']}_k{r['topk']}_n{int(r['norm_topk_prob'])}")
+def test_layer_forward_other_routing_configs(routing):
+    """The rest of the supported routing set at dim 512: n_routed not a
+    multiple of 64 and up to 1024 (the 16-key-per-lane selection), topk 1
+    and 8 (topk above 6 takes the multi-token kernels at m = 1, with 64 pairs
+    at m = 8), unnormalised weights; m = 1, 8 and 40, every token against the
+    oracle."""
+    import dataclasses
+    shape = dataclasses.replace(synth.SHAPE_TINY, **routing)
+    spec = synth.LayerSpec(shape, seed=8)
+    say(f"generating layer e{shape.n_routed} k{shape.topk} norm {shape.norm_topk_prob}")
+    dl = DeviceLayer(spec)
+    c = dl.cfg
+    try:
+        for m in (1, 8, 40):
+            x_np = synth.tokens(spec, 10 * m, m)
+            x = torch.from_numpy(x_np).cuda()
+            ws = workspace(c, m)
+            out = torch.empty((m, shape.dim), dtype=torch.uint16, device="cuda")
+            out32 = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+            hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+            say(f"  layer_forward m={m}")
+            R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr)
+            torch.cuda.synchronize()
+            ref = olayer.layer_forward(spec, x_np)
+            assert np.array_equal(hdr.cpu().numpy(), ref["header"]), m
+            o = out32.cpu().numpy()
+            for t in range(m):
+                err = np.abs(o[t] - ref["out_f32"][t])
+                assert rel_l2(o[t], ref["out_f32"][t]) <= 1e-3 and err.max() <= 1e-2, (m, t)
+            L = R.workspace_layout(c, m)
+            tab = plan_tables(ws, L, m, shape.topk)
+            P = L["max_pairs"]
+            y = ws_array(ws, L, "y", np.float32, P * shape.dim).reshape(P, shape.dim)
+            for t in range(m):
+                for k, e in enumerate(ref["tok"][t]["ids"]):
+                    ex = ref["tok"][t]["experts"][k]
+                    f32_accept(y[int(tab["tok_pairs"][t][k])], ex["y"], ex["near_y"], f"y m={m} tok {t} e {e}")
+            # the routing call alone gives the same headers
+            hdr2 = torch.empty_like(hdr)
+            R.route_select(c, x, dl.gate_w, dl.bias, hdr2, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(hdr2.cpu().numpy(), ref["header"]), m
+    finally:
+        del dl
+        torch.cuda.empty_cache()

@@ -142,3 +142,31 @@ def test_empty_batch_is_rejected_by_every_entry_point():
             call()
         assert ei.value.code == -1, i
     assert R.workspace_bytes(c, 0) == 0
+
+
+def test_token_count_bound_is_enforced_before_any_launch():
+    """The kernels index per-pair activations with 32-bit offsets and put
+    tokens on a grid dimension: m above 65535, or with m * topk *
+    max(dim, inter) >= 2^31, is MOE_EUNSUPPORTED for every entry point, and
+    the workspace size query returns 0 there."""
+    ex = R.Experts(1 << 20, 0, 0, 0, 0)
+    layer = R.Layer(8192, 16384, ex, 1 << 21, 1 << 22, 1 << 23)
+    ws = _FakePtr(1 << 24, n=1 << 40)
+    for shape, m in ((synth.SHAPE_TINY, 65536), (synth.SHAPE_DS41, 87382)):
+        c = R.cfg_from_shape(shape)
+        assert R.workspace_bytes(c, m) == 0
+        x = _FakePtr(4096, shape=(m, shape.dim))
+        calls = [
+            lambda: R.workspace_layout(c, m),
+            lambda: R.route_select(c, x, _FakePtr(8192), _FakePtr(16384), _FakePtr(32768), ws, stream=0),
+            lambda: R.experts_prefill(c, x, _FakePtr(8192), ex, _FakePtr(16384), ws, stream=0),
+            lambda: R.layer_forward(c, layer, x, _FakePtr(16384), ws, stream=0),
+            lambda: R.stack_forward(c, [layer], _FakePtr(4096, shape=(2, m, shape.dim)), ws, stream=0),
+        ]
+        for i, call in enumerate(calls):
+            with pytest.raises(R.MoeError) as ei:
+                call()
+            assert ei.value.code == -2, (shape.dim, i)
+    # the largest accepted counts still size a workspace
+    assert R.workspace_bytes(R.cfg_from_shape(synth.SHAPE_TINY), 65535) > 0
+    assert R.workspace_bytes(R.cfg_from_shape(synth.SHAPE_DS41), 65535) > 0
