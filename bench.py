@@ -9,10 +9,12 @@ whole layer forward (route, select, routed experts, shared expert, combine)
 for one token; steps cycle through `--tokens` distinct input rows so that
 consecutive tokens pick mostly different experts (the 256 MB last-level
 cache cannot hold a token's 54.7 MB of expert blocks from one step to the
-next). A sample of the steps has its three kernels (front, routed gate/up,
-routed + shared down with the combine) timed with HIP events recorded by the
-dispatches themselves, inside the timed region; the roofline line is the
-routed gate/up kernel's.
+next). Every second step's routed gate/up dispatch (the layer's largest
+kernel) records HIP start/end events of its own, in the warm-up and in the
+timed loop alike, so the tokens/s of a short run and a long one agree; the
+roofline line is that kernel's. The three kernels (front, gate/up, down with
+the combine) are timed once more in 64 steps after the timed region, and a
+read-only streaming kernel gives the box's achievable HBM read rate.
 
 --m 2..8 runs the multi-token path instead (correlated token rows, the
 union of their picks read once); its gate/up kernel is the one timed.
@@ -101,32 +103,88 @@ class HipEvents:
             self.h.hipEventDestroy(e)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, seconds: float, note: str = ""):
     """The oracle (plain C, as it stands) on host cores: whole-layer forward of
-    successive tokens of the same workload until `seconds` have passed."""
-    import numpy as np  # noqa: F401
+    successive tokens of the same workload, at all host threads for about 60%
+    of `seconds`, then at one thread for the rest."""
     import oracle
     import synth
     from oracle import layer as olayer
     gw, b = synth.gate_w(spec), synth.bias(spec)
     sw = tuple(synth.shared_w(spec, w) for w in ("w1", "w3", "w2"))
     cache = olayer.ExpertCache(spec)
-    # generate inputs outside the timed part: the experts of the sampled tokens
-    ntok = 0
-    t_total = 0.0
-    while t_total < seconds and ntok < 256:
-        x = synth.tokens(spec, ntok, 1)
-        r = olayer.route(spec, x, gw, b)
-        for e in r["header"][0, 1:1 + spec.shape.topk]:
-            cache(int(e))
-        t0 = time.perf_counter()
-        olayer.layer_forward(spec, x, experts=cache, gate_w=gw, bias=b, shared_w=sw, keep_experts=False)
-        t_total += time.perf_counter() - t0
-        ntok += 1
-        cache._c.clear()
-    return {"value": ntok / t_total, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{ntok} tokens of the same layer (m=1), whole-layer forward, {t_total:.1f} s of CPU time; "
-                      f"input generation excluded{note}"}
+
+    def sample(budget, t_first):
+        ntok, t_total = 0, 0.0
+        while t_total < budget and ntok < 256:
+            x = synth.tokens(spec, t_first + ntok, 1)
+            r = olayer.route(spec, x, gw, b)
+            for e in r["header"][0, 1:1 + spec.shape.topk]:
+                cache(int(e))                      # input generation stays outside the timed part
+            t0 = time.perf_counter()
+            olayer.layer_forward(spec, x, experts=cache, gate_w=gw, bias=b, shared_w=sw, keep_experts=False)
+            t_total += time.perf_counter() - t0
+            ntok += 1
+            cache._c.clear()
+        return ntok, t_total
+
+    threads = oracle.num_threads()
+    n_all, t_all = sample(0.6 * seconds, 0)
+    oracle.set_num_threads(1)
+    try:
+        n_one, t_one = sample(0.4 * seconds, 1000)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": n_all / t_all, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_all} tokens of the same layer (m=1), whole-layer forward, {t_all:.1f} s at {threads} "
+                      f"threads; input generation excluded{note}",
+            "single_thread": {"value": n_one / t_one, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{n_one} further tokens, {t_one:.1f} s at one thread"},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def hbm_ceiling(blocks: int = 16384):
+    """The box's achievable HBM read rate: the library's plain read-only
+    streaming kernel (16-byte loads, a contiguous share per workgroup) over windows that the
+    256 MB last-level cache cannot hold, each launch timed by the events of
+    its own dispatch. 1 GiB windows alternate over 2 GiB; 64 MiB windows (the
+    size of the m = 1 gate/up kernel's weights) rotate over 32 places."""
+    import numpy as np
+    import torch
+
+    import routing_quant_expert_amd as R
+    GiB = 1 << 30
+    buf = torch.zeros(2 * GiB, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ev = HipEvents()
+    L = R.lib()
+    res = {}
+    for name, size, nwin, reps in (("1GiB", GiB, 2, 12), ("64MiB", 64 << 20, 32, 64)):
+        evs = ev.create(2 * reps)
+        for i in range(4):                      # warm-up, hook included
+            L.moe_time_next_launch(R.MOE_K_READ_PROBE, evs[0], evs[1])
+            R.read_probe(buf[(i % nwin) * size:], size, sink, blocks)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            L.moe_time_next_launch(R.MOE_K_READ_PROBE, evs[2 * i], evs[2 * i + 1])
+            R.read_probe(buf[(i % nwin) * size:], size, sink, blocks)
+        torch.cuda.synchronize()
+        us = np.array([ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(reps)]) * 1e3
+        ev.destroy(evs)
+        res[name] = {"GBs": size / float(np.median(us)) / 1e3, "median_us": float(np.median(us)), "launches": reps}
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def stack_bench(args):
@@ -258,9 +316,6 @@ def prefill_bench(args):
         b = i % nb
         R.layer_forward(dl.cfg, dl.layer, xs[b * m:(b + 1) * m], out, ws, header=hdrs[b])
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     ev = HipEvents()
     K = args.steps
     every = max(1, min(args.time_every, 2))
@@ -269,7 +324,13 @@ def prefill_bench(args):
              ("down", R.MOE_K_DOWN), ("down2", R.MOE_K_DOWN2), ("shared_gu", R.MOE_K_SHARED_GU),
              ("shared_down", R.MOE_K_SHARED_DOWN))
     evs = {k: ev.create(2 * nt) for k, _ in kinds}
+    scratch = {k: ev.create(2) for k, _ in kinds}
     L = R.lib()
+    for i in range(args.warmup):   # the same event-bracketed dispatches as the timed loop
+        if i % every == 0:
+            for k, which in kinds:
+                L.moe_time_next_launch(which, scratch[k][0], scratch[k][1])
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -290,6 +351,7 @@ def prefill_bench(args):
                         min(at(k, j, 0) for k in ("gateup", "gateup2")) for j in range(nt)])
     for k, _ in kinds:
         ev.destroy(evs[k])
+        ev.destroy(scratch[k])
     wall = t1 - t0
     picks = hdrs[:, :, 1:1 + s.topk].cpu().numpy()
     n_u = np.array([len(np.unique(p)) for p in picks])
@@ -358,9 +420,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--tokens", type=int, default=64, help="distinct input rows cycled through")
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--time-every", type=int, default=32, help="bracket every n-th step's timed kernel")
+    ap.add_argument("--time-every", type=int, default=2,
+                    help="bracket every n-th step's gate/up dispatch with events (the same in warm-up and timed loop)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-only HBM streaming measurement")
     ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernels; 2..8: the "
                                                      "multi-token decode path on correlated rows; > 8: the "
                                                      "prefill path, Zipf-skewed bias)")
@@ -418,38 +482,62 @@ def main():
     R.workspace_init(dl.cfg, m, ws)
     out = torch.empty((m, s.dim), dtype=torch.uint16, device="cuda")
     hw = R.header_words(dl.cfg)
-    hdrs = torch.empty((args.steps, m, hw), dtype=torch.int32, device="cuda")
+    K = args.steps
+    hdrs = torch.empty((K, m, hw), dtype=torch.int32, device="cuda")
     hdr_w = torch.empty((m, hw), dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
-    def step(i, hdr):
-        t = (i % args.tokens) * m
-        R.layer_forward(dl.cfg, dl.layer, xs[t:t + m], out, ws, header=hdr)
+    # a step is one moe_layer_forward call through the C ABI; its arguments are marshalled once per cycled input
+    L = R.lib()
+    cfg_p, layer_p = ctypes.byref(dl.cfg), ctypes.byref(dl.layer)
+    x_p = [ctypes.c_void_p(xs[t * m].data_ptr()) for t in range(args.tokens)]
+    out_p, ws_p = ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr())
+    ws_n = ctypes.c_size_t(ws.numel())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hdr_p = [ctypes.c_void_p(hdrs[i].data_ptr()) for i in range(K)]
+    hdr_wp = ctypes.c_void_p(hdr_w.data_ptr())
 
-    for i in range(args.warmup):
-        step(i, hdr_w)
-    torch.cuda.synchronize()
+    def step(i, hdr):
+        rc = L.moe_layer_forward(cfg_p, layer_p, x_p[i % args.tokens], m, out_p, None, hdr, ws_p, ws_n, stream)
+        if rc:
+            raise R.MoeError(rc, L.moe_last_error().decode())
 
     ev = HipEvents()
-    K = args.steps
     every = max(1, args.time_every)
     nt = (K + every - 1) // every
-    kinds = (("front", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("down", R.MOE_K_DOWN))
-    evs = {k: ev.create(2 * nt) for k, _ in kinds}
-    L = R.lib()
+    evs = ev.create(2 * nt)
+    scratch = ev.create(2)
+    # warm-up: the same launches and the same event-bracketed dispatches as the timed loop
+    for i in range(args.warmup):
+        if i % every == 0:
+            L.moe_time_next_launch(R.MOE_K_GATEUP, scratch[0], scratch[1])
+        step(i, hdr_wp)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if i % every == 0:          # a sample of the steps brackets its kernels with events
+        if i % every == 0:          # every `every`-th step's gate/up dispatch records its own start and end
             j = i // every
-            for k, which in kinds:
-                L.moe_time_next_launch(which, evs[k][2 * j], evs[k][2 * j + 1])
-        step(args.warmup + i, hdrs[i])
+            L.moe_time_next_launch(R.MOE_K_GATEUP, evs[2 * j], evs[2 * j + 1])
+        step(args.warmup + i, hdr_p[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k_ms = {k: np.array([ev.elapsed_ms(evs[k][2 * j], evs[k][2 * j + 1]) for j in range(nt)]) for k, _ in kinds}
+    gu_ms = np.array([ev.elapsed_ms(evs[2 * j], evs[2 * j + 1]) for j in range(nt)])
+    ev.destroy(evs)
+
+    # after the timed region: the three kernels of a further 64 steps, each bracketed on every second step
+    kinds = (("front", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("down", R.MOE_K_DOWN))
+    n_pass = 64
+    kev = {k: ev.create(n_pass) for k, _ in kinds}
+    for i in range(n_pass):
+        if i % 2 == 0:
+            for k, which in kinds:
+                L.moe_time_next_launch(which, kev[k][i], kev[k][i + 1])
+        step(args.warmup + K + i, hdr_wp)
+    torch.cuda.synchronize()
+    k_ms = {k: np.array([ev.elapsed_ms(kev[k][i], kev[k][i + 1]) for i in range(0, n_pass, 2)]) for k, _ in kinds}
     for k, _ in kinds:
-        ev.destroy(evs[k])
+        ev.destroy(kev[k])
+    ev.destroy(scratch)
 
     wall = t1 - t0
     ms_per_step = wall * 1e3 / K
@@ -476,17 +564,20 @@ def main():
                   "gateup": float(n_u.mean()) * 2 * s.gate_bytes,
                   "down": float(n_u.mean()) * s.down_bytes + shared_down_bytes}
     launch_bytes = kbytes["gateup"]
-    k_avg = us["gateup"] * 1e-6
-    routed_bytes = float(n_u.mean()) * expert_bytes
-    extra = {"kernels": {k: {"avg_us": us[k], "weight_bytes": kbytes[k], "gbs": kbytes[k] / us[k] / 1e3}
-                         for k, _ in kinds},
+    k_avg = float(gu_ms.mean()) * 1e-3
+    extra = {"kernels_after_timed_region": {k: {"avg_us": us[k], "weight_bytes": kbytes[k],
+                                                "gbs": kbytes[k] / us[k] / 1e3} for k, _ in kinds},
              "layer_weight_bytes": sum(kbytes.values()),
              "layer_kernels_us": sum(us.values()),
              "layer_kernels_gbs": sum(kbytes.values()) / sum(us.values()) / 1e3,
-             "expert_kernels_gbs": (kbytes["gateup"] + kbytes["down"]) / (us["gateup"] + us["down"]) / 1e3}
+             "expert_kernels_gbs": (kbytes["gateup"] + kbytes["down"]) / (us["gateup"] + us["down"]) / 1e3,
+             "step_gbs": sum(kbytes.values()) / (wall / K) / 1e9,
+             "timing_note": f"every {every}-th step's gate/up dispatch carries start/end events, in the warm-up "
+                            "and the timed loop alike; the per-kernel figures come from 64 further steps"}
     if m > 1:
         extra["union_experts_mean"] = float(n_u.mean())
     achieved = launch_bytes / k_avg / 1e9
+    ceiling = None if args.no_ceiling else hbm_ceiling()
     res = {
         "metric": "MoE-layer decode tokens/s at m=1 and % of HBM peak on expert-weight bytes",
         "value": K * m / wall,
@@ -509,10 +600,13 @@ def main():
                                  measured_traffic(kernel, "hbm_traffic_decode_m8_dim4096.md", UNION_SOURCES) if m == 8
                                  else None), "kernel": kernel,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
-                     "launch_p10_p90_us": [float(np.percentile(k_ms["gateup"], 10) * 1e3),
-                                           float(np.percentile(k_ms["gateup"], 90) * 1e3)]},
+                     "launch_p10_p90_us": [float(np.percentile(gu_ms, 10) * 1e3),
+                                           float(np.percentile(gu_ms, 90) * 1e3)]},
         "detail": extra,
     }
+    if ceiling:
+        res["roofline"]["hbm_read_probe"] = ceiling
+        res["roofline"]["frac_of_read_probe_64MiB"] = achieved / ceiling["64MiB"]["GBs"]
     if not args.no_cpu and m == 1:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)

@@ -268,7 +268,16 @@ int moe_swiglu_host(const float* g, const float* u, int64_t n, float limit, floa
                                 (MOE_K_GATEUP is then the one of the experts with at most 8) */
 #define MOE_K_DOWN2 7        /* prefill: the down kernel of the experts with more than 8 pairs
                                 (MOE_K_DOWN is then the one of the experts with at most 8)   */
+#define MOE_K_READ_PROBE 8   /* moe_read_probe's streaming kernel                         */
 int moe_time_next_launch(int32_t which, void* ev_begin, void* ev_end);
+
+/* Measurement only: a plain read-only stream over `bytes` bytes of device
+ * memory at `buf` (16-byte aligned, bytes a multiple of 16) with `blocks`
+ * workgroups of 256 threads (each a contiguous share), 16-byte loads, nothing written
+ * (sink: one device word, written only if the data XOR to a fixed value).
+ * Timed through moe_time_next_launch(MOE_K_READ_PROBE, ...), it gives the
+ * achievable HBM read rate that the kernels' rates are set beside. */
+int moe_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
 
 const char* moe_last_error(void);

@@ -519,6 +519,16 @@ EXPORT int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the OpenMP loops above use from now on (n >= 1); the CPU baseline
+ * times the oracle at one thread and at all host threads. */
+EXPORT void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Array forms of the scalar functions above (for the Python tests).         */
 /* ------------------------------------------------------------------------ */

@@ -17,6 +17,7 @@ MOE_STATUS_NAN_KEY = 2
 MOE_STATUS_BAD_PICK = 4
 MOE_K_GATEUP, MOE_K_DOWN, MOE_K_ROUTER, MOE_K_SHARED_GU, MOE_K_SHARED_DOWN, MOE_K_GATEUP2, MOE_K_DOWN2 = (
     1, 2, 3, 4, 5, 6, 7)
+MOE_K_READ_PROBE = 8
 
 
 class MoeError(RuntimeError):
@@ -78,6 +79,7 @@ def lib():
         L.moe_scores_host.argtypes = [_VP, ctypes.c_int64, ctypes.c_float, _VP, ctypes.c_int32]
         L.moe_swiglu_host.argtypes = [_VP, _VP, ctypes.c_int64, ctypes.c_float, _VP]
         L.moe_time_next_launch.argtypes = [ctypes.c_int32, _VP, _VP]
+        L.moe_read_probe.argtypes = [_VP, ctypes.c_uint64, _VP, ctypes.c_int32, _VP]
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -181,3 +183,8 @@ def time_next_launch(which: int, ev_begin, ev_end):
     b = None if ev_begin is None else ctypes.c_void_p(ev_begin.cuda_event)
     e = None if ev_end is None else ctypes.c_void_p(ev_end.cuda_event)
     _check(lib().moe_time_next_launch(which, b, e))
+
+
+def read_probe(buf, nbytes: int, sink, blocks: int, stream=None):
+    """Stream `nbytes` of the device tensor `buf` through the library's read-only probe kernel."""
+    _check(lib().moe_read_probe(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)))
