@@ -220,6 +220,21 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
 int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
                       float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_layer_forward
+ * for 1 <= m <= 8 tokens with no workspace argument. Its workspace is a
+ * fixed 6 MiB array of the library's own on each GPU, held from the
+ * library's load until the process ends; a shape whose workspace would not
+ * fit returns MOE_EWORKSPACE, m outside 1..8 MOE_EINVAL. The first call on a
+ * device looks the array's device address up and zeroes its control words
+ * with a kernel on `stream`; no call allocates or frees anything. Every call
+ * on one GPU shares the array: calls that overlap on one GPU (different
+ * streams, or host threads) race and must not be issued. The intermediate
+ * results stay in that array and are not exposed. Arguments, outputs and
+ * the other errors as moe_layer_forward. */
+int moe_layer_forward_noalloc(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m,
+                              uint16_t* out_bf16, float* out_f32, int32_t* header, void* stream);
+
 /* One step through a stack of n_layers MoE layers for m >= 1 tokens:
  * for l = 0 .. n_layers-1, out_l = layer l applied to x_l exactly as
  * moe_layer_forward computes it, and x_{l+1} = bf16(f32(x_l) + out_l), the

@@ -73,6 +73,8 @@ def lib():
                                           _VP, _VP, ctypes.c_size_t, _VP]
         L.moe_layer_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), _VP, ctypes.c_int32, _VP, _VP,
                                         _VP, _VP, ctypes.c_size_t, _VP]
+        L.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), _VP, ctypes.c_int32,
+                                                _VP, _VP, _VP, _VP]
         L.moe_stack_forward.argtypes = [ctypes.POINTER(Cfg), ctypes.POINTER(Layer), ctypes.c_int32, _VP,
                                          ctypes.c_int32, _VP, _VP, _VP, ctypes.c_size_t, _VP]
         L.moe_scores.argtypes = [_VP, ctypes.c_int64, ctypes.c_float, _VP, ctypes.c_int32, _VP]
@@ -148,6 +150,13 @@ def layer_forward(cfg: Cfg, layer: Layer, x, out_bf16, ws, out_f32=None, header=
     _check(lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(layer), _ptr(x), m, _ptr(out_bf16),
                                    _ptr(out_f32), _ptr(header), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
+
+
+def layer_forward_noalloc(cfg: Cfg, layer: Layer, x, out_bf16, out_f32=None, header=None, stream=None):
+    """The layer for m <= 8 tokens on the library's fixed scratch (no workspace argument)."""
+    m = x.shape[0]
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(layer), _ptr(x), m, _ptr(out_bf16),
+                                           _ptr(out_f32), _ptr(header), _stream(stream)))
 
 
 def stack_forward(cfg: Cfg, layers, xs, ws, out_f32=None, headers=None, stream=None):

@@ -286,6 +286,44 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The fixed scratch of moe_layer_forward_noalloc: one workspace-sized array
+// per GPU, held from the library's load until the process ends, so that the
+// entry point needs no allocation. Its name is a host-side stand-in, not a
+// device address: the address each device's copy has is looked up once per
+// device (with that device current) and kept; only that pointer is passed to
+// kernels. Every call on a GPU shares the array, so calls that overlap on one
+// GPU race.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)6 << 20;   // every supported shape at m <= 8 needs at most 5.1 MiB
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu[kMaxDevices];
+}  // namespace
+
+// This device's copy of `scratch`. On the first use on a device: look its
+// address up and zero its control words (offset 0 in every workspace layout)
+// with a fill kernel on `s`, ahead of the call's own launches; every call
+// leaves them zero again. The rest of a workspace needs no initialisation.
+int scratch_of_device(hipStream_t s, uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device index out of range%s (%lld)", "", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu[dev]);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    if ((e = launch_zero(p, 256, s)) != hipSuccess) return hip_fail(e, "scratch control words");
+    g_scratch[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch[dev]);
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -466,6 +504,28 @@ int moe_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int32_t bloc
              static_cast<const uint4*>(buf), bytes / 16, sink);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "read_probe");
+}
+
+int moe_layer_forward_noalloc(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m,
+                              uint16_t* out_bf16, float* out_f32, int32_t* header, void* stream) {
+  if (int r = check_cfg(cfg)) return r;
+  if (!x || !out_bf16) return fail(MOE_EINVAL, "x and out_bf16 must be non-NULL%s%lld");
+  if (int r = check_layer(layer)) return r;
+  if (m < 1 || m > kMaxDecodeTokens)
+    return fail(MOE_EINVAL, "the no-allocation entry point takes 1 <= m <= 8 tokens%s (m %lld)", "", m);
+  if (!a16(x)) return fail(MOE_EINVAL, "x must be 16-byte aligned%s%lld");
+  moe_ws_layout L;
+  layout_of(*cfg, m, &L);
+  if (L.total > kScratchBytes)
+    return fail(MOE_EWORKSPACE, "this shape needs %s%lld bytes of workspace, more than the library's fixed scratch",
+                "", (long long)L.total);
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = nullptr;
+  if (int r = scratch_of_device(s, &ws)) return r;
+  Ws w = ws_view(ws, L, *cfg, m);
+  LayerOut o{out_f32, out_bf16, nullptr, nullptr};
+  int32_t* grp = reinterpret_cast<int32_t*>(ws + L.grp);
+  return layer_launches(*cfg, *layer, x, m, o, header ? header : w.status + 4, w, grp, s);
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
