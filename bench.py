@@ -298,8 +298,9 @@ def prefill_bench(args):
     from synth.device import DeviceLayer
 
     m = args.m
-    spec = synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed, zipf_bias=True)
+    spec = synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed, zipf_bias=True, shared_quant=args.shared_quant)
     s = spec.shape
+    shq = 1 if args.shared_quant else 0
     print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts, Zipf bias)",
           file=sys.stderr, flush=True)
     dl = DeviceLayer(spec)
@@ -323,6 +324,8 @@ def prefill_bench(args):
     kinds = (("router", R.MOE_K_ROUTER), ("gateup", R.MOE_K_GATEUP), ("gateup2", R.MOE_K_GATEUP2),
              ("down", R.MOE_K_DOWN), ("down2", R.MOE_K_DOWN2), ("shared_gu", R.MOE_K_SHARED_GU),
              ("shared_down", R.MOE_K_SHARED_DOWN))
+    if shq:   # the K-quant shared expert runs inside the expert launches: no bf16 shared GEMMs
+        kinds = tuple(kv for kv in kinds if not kv[0].startswith("shared"))
     evs = {k: ev.create(2 * nt) for k, _ in kinds}
     scratch = {k: ev.create(2) for k, _ in kinds}
     L = R.lib()
@@ -365,17 +368,19 @@ def prefill_bench(args):
     us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
     nu = float(n_u.mean())
     pairs = m * s.topk
-    kbytes = {"router": s.n_routed * s.dim * 2, "gateup": nu * 2 * s.gate_bytes, "down": nu * s.down_bytes,
+    nx = nu + shq        # expert groups the stage reads (the K-quant shared one included)
+    px = pairs + shq * m  # (token, expert) pairs of the stage
+    kbytes = {"router": s.n_routed * s.dim * 2, "gateup": nx * 2 * s.gate_bytes, "down": nx * s.down_bytes,
               "shared_gu": 2 * s.inter * s.dim * 2, "shared_down": s.inter * s.dim * 2}
-    kops = {"router": 2 * m * s.n_routed * s.dim, "gateup": 2 * pairs * 2 * s.inter * s.dim,
-            "down": 2 * pairs * s.dim * s.inter, "shared_gu": 2 * m * 2 * s.inter * s.dim,
+    kops = {"router": 2 * m * s.n_routed * s.dim, "gateup": 2 * px * 2 * s.inter * s.dim,
+            "down": 2 * px * s.dim * s.inter, "shared_gu": 2 * m * 2 * s.inter * s.dim,
             "shared_down": 2 * m * s.dim * s.inter}
     kern = {k: {"avg_us": us[k], "weight_bytes": kbytes[k], "gbs": kbytes[k] / us[k] / 1e3,
                 "tops": kops[k] / us[k] / 1e6} for k, _ in kinds}
     launch_bytes = kbytes["gateup"] + kbytes["down"]
     k_avg = float(span_ms.mean()) * 1e-3
     achieved = launch_bytes / k_avg / 1e9
-    step_bytes = sum(kbytes.values())
+    step_bytes = sum(v for k, v in kbytes.items() if not (shq and k.startswith("shared")))
     res = {
         "metric": "MoE-layer prefill tokens/s at m=512 and % of HBM peak on expert-weight bytes",
         "value": K * m / wall,
@@ -389,13 +394,15 @@ def prefill_bench(args):
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": f"moe_layer_prefill_m{m}_zipf_dim4096_inter2048_e384_top6", "dim": s.dim,
+        "config": {"workload": f"moe_layer_prefill_m{m}_zipf_dim4096_inter2048_e384_top6" +
+                               ("_shared_q2k_q3k" if shq else ""), "dim": s.dim,
+                   "shared_expert": "Q2_K/Q3_K blocks" if shq else "bf16",
                    "inter": s.inter, "n_routed": s.n_routed, "topk": s.topk, "m": m, "batches_cycled": nb,
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("expert stage", "hbm_traffic_prefill_m512_dim4096.md",
-                                                 PREFILL_SOURCES) if m == 512 else None,
+                                                 PREFILL_SOURCES) if m == 512 and not shq else None,
                      "kernel": "expert stage (k_gateup_pf_small, k_gateup_pf, k_down_pf_small, k_down_pf on two streams)",
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
                      "launch_p10_p90_us": [float(np.percentile(span_ms, 10) * 1e3),
@@ -425,6 +432,8 @@ def main():
     ap.add_argument("--time-every", type=int, default=2,
                     help="bracket every n-th step's gate/up dispatch with events (the same in warm-up and timed loop)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-only HBM streaming measurement")
+    ap.add_argument("--shared-quant", action="store_true",
+                    help="the layer's shared expert as Q2_K/Q3_K blocks (run as one more expert) instead of bf16")
     ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernels; 2..8: the "
                                                      "multi-token decode path on correlated rows; > 8: the "
                                                      "prefill path, Zipf-skewed bias)")
@@ -465,9 +474,10 @@ def main():
     from synth.device import DeviceLayer
 
     torch.cuda.set_device(0)
-    spec = synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed)
+    spec = synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed, shared_quant=args.shared_quant)
     s = spec.shape
     m = args.m
+    shq = 1 if args.shared_quant else 0
     print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts) on the device",
           file=sys.stderr, flush=True)
     if args.layers > 1:
@@ -542,27 +552,30 @@ def main():
     wall = t1 - t0
     ms_per_step = wall * 1e3 / K
     router_bytes = s.n_routed * s.dim * 2
-    shared_gu_bytes = 2 * s.inter * s.dim * 2
-    shared_down_bytes = s.inter * s.dim * 2
+    # the shared expert: bf16 matrices, or (--shared-quant) K-quant blocks read as one more expert of the step
+    shared_gu_bytes = 0 if shq else 2 * s.inter * s.dim * 2
+    shared_down_bytes = 0 if shq else s.inter * s.dim * 2
     expert_bytes = 2 * s.gate_bytes + s.down_bytes
     us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
+    sfx = "_shared_q2k_q3k" if shq else ""
     if m == 1:
         kernel = "k_gateup_m1"
         n_u = np.full(1, s.topk)
-        workload = "moe_layer_decode_m1_dim4096_inter2048_e384_top6"
+        workload = f"moe_layer_decode_m1_dim4096_inter2048_e384_top6{sfx}"
     else:
         picks = hdrs[:, :, 1:1 + s.topk].cpu().numpy()
         n_u = np.array([len(np.unique(p)) for p in picks[::every]])   # the timed steps' unions
         kernel = "k_gateup"
-        workload = f"moe_layer_decode_m{m}_correlated_dim4096_inter2048_e384_top6"
+        workload = f"moe_layer_decode_m{m}_correlated_dim4096_inter2048_e384_top6{sfx}"
+    n_x = n_u.astype(np.float64) + shq   # experts whose blocks the step reads (the K-quant shared one included)
     if m == 1:   # the single-token launches: router | selection, routed + shared gate/up | down + combine
         kbytes = {"front": router_bytes,
-                  "gateup": s.topk * 2 * s.gate_bytes + shared_gu_bytes,
-                  "down": s.topk * s.down_bytes + shared_down_bytes}
+                  "gateup": float(n_x.mean()) * 2 * s.gate_bytes + shared_gu_bytes,
+                  "down": float(n_x.mean()) * s.down_bytes + shared_down_bytes}
     else:
         kbytes = {"front": router_bytes + shared_gu_bytes,
-                  "gateup": float(n_u.mean()) * 2 * s.gate_bytes,
-                  "down": float(n_u.mean()) * s.down_bytes + shared_down_bytes}
+                  "gateup": float(n_x.mean()) * 2 * s.gate_bytes,
+                  "down": float(n_x.mean()) * s.down_bytes + shared_down_bytes}
     launch_bytes = kbytes["gateup"]
     k_avg = float(gu_ms.mean()) * 1e-3
     extra = {"kernels_after_timed_region": {k: {"avg_us": us[k], "weight_bytes": kbytes[k],
@@ -576,6 +589,8 @@ def main():
                             "and the timed loop alike; the per-kernel figures come from 64 further steps"}
     if m > 1:
         extra["union_experts_mean"] = float(n_u.mean())
+    routed_bytes = float(n_u.mean()) * expert_bytes
+    extra["routed_expert_bytes"] = routed_bytes
     achieved = launch_bytes / k_avg / 1e9
     ceiling = None if args.no_ceiling else hbm_ceiling()
     res = {
@@ -593,10 +608,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload, "dim": s.dim, "inter": s.inter,
                    "n_routed": s.n_routed, "topk": s.topk, "m": m, "tokens_cycled": args.tokens,
+                   "shared_expert": "Q2_K/Q3_K blocks" if shq else "bf16",
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (measured_traffic(kernel) if m == 1 else
+                     "traffic": (None if shq else measured_traffic(kernel) if m == 1 else
                                  measured_traffic(kernel, "hbm_traffic_decode_m8_dim4096.md", UNION_SOURCES) if m == 8
                                  else None), "kernel": kernel,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),

@@ -36,7 +36,7 @@
  *     multiples of 256 with dim/256 and inter/256 powers of two <= 16 (the
  *     K-quant kernels give each 256-weight super-block of a row to one lane
  *     and stage whole row tiles in LDS). Anything else: MOE_EUNSUPPORTED.
- *   - Tokens per call: 1 <= m <= 65535 with m * topk * max(dim, inter) < 2^31
+ *   - Tokens per call: 1 <= m <= 65535 with m * (topk + 1) * max(dim, inter) < 2^31
  *     (the kernels index the per-pair activations with 32-bit offsets); m < 1
  *     is MOE_EINVAL, more is MOE_EUNSUPPORTED (also for the workspace calls,
  *     where moe_workspace_bytes then returns 0).
@@ -92,15 +92,30 @@ typedef struct moe_experts {
 } moe_experts;
 
 /* One layer's resident weights [moe_v41.rs, struct MoeV41LayerWeights]:
- * gate_w bf16 [n_routed][dim]; bias f32 [n_routed] (correction bias);
- * shared expert bf16 sh_w1 [inter][dim], sh_w3 [inter][dim], sh_w2 [dim][inter]. */
+ * gate_w bf16 [n_routed][dim]; bias f32 [n_routed] (correction bias); the
+ * shared expert either as bf16 matrices (shared_kind MOE_SHARED_BF16) sh_w1
+ * [inter][dim], sh_w3 [inter][dim], sh_w2 [dim][inter], or as K-quant blocks
+ * (MOE_SHARED_KQUANT) in shared_q laid out like one routed expert: Q2_K gate
+ * (w1) and up (w3) [inter][dim/256] at base + gate_off / up_off, Q3_K down
+ * (w2) [dim][inter/256] at base + down_off (stride unused), 16-byte aligned
+ * [moe_v41.rs, struct MoeV41LayerWeights: the shared matrices resident as
+ * bf16 or as the GGUF's Q2_K (w1, w3) / Q3_K (w2) blocks on the routed
+ * experts' kernels]. The K-quant shared expert runs exactly as one more
+ * routed expert of every token with weight 1 (q8_1 of x, gate/up GEMVs,
+ * clamped SwiGLU, q8_1 of h, down GEMV), and is added after the routed sum
+ * like the bf16 one [moe_v41.rs, fn shared_side]. A struct whose trailing
+ * fields are zero is a bf16-shared layer. */
+#define MOE_SHARED_BF16 0
+#define MOE_SHARED_KQUANT 1
 typedef struct moe_layer {
   const uint16_t* gate_w;
   const float* bias;
   moe_experts experts;
-  const uint16_t* sh_w1;
+  const uint16_t* sh_w1;     /* bf16 shared expert (MOE_SHARED_BF16); may be NULL otherwise */
   const uint16_t* sh_w3;
   const uint16_t* sh_w2;
+  int32_t shared_kind;       /* MOE_SHARED_BF16 or MOE_SHARED_KQUANT */
+  moe_experts shared_q;      /* the K-quant shared expert's blocks (MOE_SHARED_KQUANT) */
 } moe_layer;
 
 /* Words of one token's routing header: 1 + 3*topk int32
@@ -134,7 +149,12 @@ int moe_workspace_init(const moe_cfg* cfg, int32_t max_m, void* ws, size_t ws_by
 /* Offsets (bytes from the workspace start) of the intermediate results, for
  * inspection after a call has completed [the pages' workspace buffers,
  * moe_v41.rs, struct MoeV41]. Pair p = one (expert, token) of the plan, in
- * ascending expert id, then ascending token. */
+ * ascending expert id, then ascending token; a K-quant shared expert is the
+ * plan's expert id n_routed (weight 1), so its pairs come last. The plan
+ * words hold n_u, n_pairs, then max_pairs entries each of u_expert, u_first,
+ * u_npairs, pair_tok, pair_expert, pair_w (f32 bits), then tok_pairs
+ * [max_m][topk + 1]: each token's pairs in plan order, the last entry its
+ * K-quant shared expert's pair (-1 = none). */
 typedef struct moe_ws_layout {
   uint64_t total;
   uint64_t xq;       /* int8  [max_m][dim]        q8_1 codes of x                  */
@@ -157,10 +177,10 @@ typedef struct moe_ws_layout {
   uint64_t yr;       /* f32   [max_m][dim]        routed sum (layer forward)       */
   uint64_t status;   /* int32 [4] device status words (word 0: OR of MOE_STATUS_*) */
   uint64_t ctl;      /* 256 B control words (zero between calls); always offset 0  */
-  uint64_t grp;      /* int32 [max_m + 2*n_routed] grouping scratch (prefill)       */
+  uint64_t grp;      /* int32 [max_m + 2*(n_routed+1)] grouping scratch (prefill)   */
   uint64_t xd64;     /* f64   [max_m][dim/32]     q8_1 scales of x (prefill)       */
   uint64_t hd64;     /* f64   [pairs][inter/32]   q8_1 scales of h (prefill)       */
-  int32_t max_pairs; /* max_m * topk                                              */
+  int32_t max_pairs; /* max_m * (topk + 1)                                        */
   int32_t plan_words;
 } moe_ws_layout;
 

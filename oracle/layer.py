@@ -8,6 +8,11 @@ prefill are defined exactly as m = 1 repeated):
      Q2_K gate/up GEMV, clamped SwiGLU, q8_1, Q3_K down GEMV
   4. acc = sum over the plan of w*y (f32, in plan order), then + shared expert
      output, out = bf16(acc)                           [moe_v41.rs, fn shared_side]
+The shared expert is either resident bf16 (a dense MLP whose SwiGLU output is
+rounded to bf16) or K-quant blocks run exactly as one more routed expert
+(q8_1 of x, Q2_K gate/up, clamped SwiGLU, q8_1 of h, Q3_K down) whose output
+is added after the routed sum [moe_v41.rs, struct MoeV41LayerWeights: the
+shared matrices as bf16 or the GGUF's Q2_K/Q3_K blocks].
 A stack of layers (one decode step through them, [step_seg.rs, module doc])
 adds each layer's output to its input in f32 and rounds to bf16.
 """
@@ -41,15 +46,20 @@ def route(spec: synth.LayerSpec, x_bf16: np.ndarray, gate_w=None, bias=None) -> 
 
 
 def layer_forward(spec: synth.LayerSpec, x_bf16: np.ndarray, *, with_shared: bool = True, experts=None,
-                  gate_w=None, bias=None, shared_w=None, keep_experts: bool = True) -> dict:
-    """Full layer for the bf16 rows x [m, dim]. Returns per-token results."""
+                  gate_w=None, bias=None, shared_w=None, shared_q=None, keep_experts: bool = True) -> dict:
+    """Full layer for the bf16 rows x [m, dim]. Returns per-token results.
+    The shared expert is K-quant when spec.shared_quant or shared_q (its
+    (gate, up, down) raw blocks) is given, else bf16 (shared_w = (w1, w3, w2))."""
     s = spec.shape
     x_bf16 = np.ascontiguousarray(x_bf16, np.uint16).reshape(-1, s.dim)
     m = x_bf16.shape[0]
     experts = experts or ExpertCache(spec)
     r = route(spec, x_bf16, gate_w, bias)
     status, picks, wts, plan = header_fields(r["header"], s.topk)
-    if with_shared:
+    quant_shared = with_shared and (shared_q is not None or spec.shared_quant)
+    if quant_shared:
+        shared_q = shared_q or tuple(synth.shared_q_blocks(spec, w) for w in ("gate", "up", "down"))
+    elif with_shared:
         shared_w = shared_w or tuple(synth.shared_w(spec, w) for w in ("w1", "w3", "w2"))
     out = dict(r)
     out.update(xq=[], xd16=[], tok=[], y_routed=np.empty((m, s.dim), np.float32),
@@ -69,7 +79,11 @@ def layer_forward(spec: synth.LayerSpec, x_bf16: np.ndarray, *, with_shared: boo
         ys = np.stack([p["y"] for p in per])
         out["y_routed"][t], _ = combine(ys, w_plan)
         sd = None
-        if with_shared:
+        if quant_shared:   # one more expert on the same q8_1(x), output added after the routed sum
+            sh = expert(s, xq, xd, *shared_q)
+            out["shared"].append(sh)
+            sd = sh["y"]
+        elif with_shared:
             sh = shared(s, x_bf16[t], *shared_w)
             out["shared"].append(sh)
             sd = sh["sd"]

@@ -39,7 +39,11 @@ class Experts(ctypes.Structure):
 
 class Layer(ctypes.Structure):
     _fields_ = [("gate_w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("experts", Experts),
-                ("sh_w1", ctypes.c_void_p), ("sh_w3", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p)]
+                ("sh_w1", ctypes.c_void_p), ("sh_w3", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p),
+                ("shared_kind", ctypes.c_int32), ("shared_q", Experts)]
+
+
+MOE_SHARED_BF16, MOE_SHARED_KQUANT = 0, 1
 
 
 class WsLayout(ctypes.Structure):

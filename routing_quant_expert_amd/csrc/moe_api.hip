@@ -105,7 +105,11 @@ hipError_t fork_join(hipEvent_t after, hipStream_t from, hipStream_t to) {
 // The single-token kernels: up to 6 picks (a wave each) and down rows of at
 // most 8 Q3_K super-blocks (each pick's 16-row tile is staged whole in LDS);
 // other shapes take the union path, which is correct for every m <= 8.
-bool single_token_fits(const moe_cfg& c) { return c.topk <= kMaxTopkM1 && c.inter / 256 <= 8; }
+// With a K-quant shared expert (shq = 1) its blocks take one more pick's wave
+// in place of the two bf16 shared-expert waves.
+bool single_token_fits(const moe_cfg& c, int shq = 0) {
+  return (shq ? c.topk + 1 <= kMaxTopk : c.topk <= kMaxTopkM1) && c.inter / 256 <= 8;
+}
 
 int check_cfg(const moe_cfg* c) {
   if (!c) return fail(MOE_EINVAL, "cfg is NULL%s%lld");
@@ -126,9 +130,9 @@ int check_cfg(const moe_cfg* c) {
 int check_m(const moe_cfg& c, int64_t m) {
   if (m < 1) return fail(MOE_EINVAL, "m must be >= 1%s (m %lld)", "", m);
   const int64_t width = c.dim > c.inter ? c.dim : c.inter;
-  if (m > kMaxTokens || m * c.topk * width >= ((int64_t)1 << 31))
-    return fail(MOE_EUNSUPPORTED, "too many tokens for one call%s (m %lld; at most 65535 and m*topk*max(dim,inter) < 2^31)",
-                "", m);
+  if (m > kMaxTokens || m * (c.topk + 1) * width >= ((int64_t)1 << 31))
+    return fail(MOE_EUNSUPPORTED,
+                "too many tokens for one call%s (m %lld; at most 65535 and m*(topk+1)*max(dim,inter) < 2^31)", "", m);
   return MOE_OK;
 }
 
@@ -157,13 +161,34 @@ int check_experts(const moe_experts* ex) {
   if (!ex || !ex->base) return fail(MOE_EINVAL, "experts / experts->base is NULL%s%lld");
   if (!a16(ex->base) || (ex->stride & 15) || (ex->gate_off & 15) || (ex->up_off & 15) || (ex->down_off & 15))
     return fail(MOE_EINVAL, "expert arena: base, stride and offsets must be multiples of 16 bytes%s%lld");
+  // the prefill kernels address a matrix inside an expert with 32-bit offsets
+  const uint64_t lim = (uint64_t)1 << 31;
+  if (ex->gate_off >= lim || ex->up_off >= lim || ex->down_off >= lim)
+    return fail(MOE_EUNSUPPORTED, "expert arena: matrix offsets must be below 2^31 bytes%s%lld");
   return MOE_OK;
 }
 
 }  // namespace
 
+XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q) {
+  XArena a;
+  a.base = static_cast<const uint8_t*>(ex.base);
+  a.stride = ex.stride;
+  a.gate_off = ex.gate_off;
+  a.up_off = ex.up_off;
+  a.down_off = ex.down_off;
+  a.sbase = shared_q ? static_cast<const uint8_t*>(shared_q->base) : nullptr;
+  a.sgate_off = shared_q ? shared_q->gate_off : 0;
+  a.sup_off = shared_q ? shared_q->up_off : 0;
+  a.sdown_off = shared_q ? shared_q->down_off : 0;
+  a.n_routed = n_routed;
+  return a;
+}
+
+// Every token has at most topk + 1 plan entries (its picks and a K-quant
+// shared expert), so the pair tables hold max_m * (topk + 1) pairs.
 bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
-  const uint64_t m = max_m, P = (uint64_t)max_m * c.topk;
+  const uint64_t m = max_m, P = (uint64_t)max_m * (c.topk + 1);
   uint64_t t = 0;
   L->ctl = take(t, 256);   // first, so that its place does not depend on m
   L->xq = take(t, m * c.dim);
@@ -186,7 +211,7 @@ bool layout_of(const moe_cfg& c, int max_m, moe_ws_layout* L) {
   L->sd = take(t, m * c.dim * 4);
   L->yr = take(t, m * c.dim * 4);
   L->status = take(t, 16 + m * (1 + 3 * c.topk) * 4);   // status words, then a header scratch
-  L->grp = take(t, (m + 2 * (uint64_t)c.n_routed) * 4);
+  L->grp = take(t, (m + 2 * ((uint64_t)c.n_routed + 1)) * 4);
   L->xd64 = take(t, m * (c.dim / 32) * 8);
   L->hd64 = take(t, P * (c.inter / 32) * 8);
   L->total = t;
@@ -238,51 +263,72 @@ bool take_timed(int which, hipEvent_t* begin, hipEvent_t* end) {
 }
 
 int check_layer(const moe_layer* layer) {
-  if (!layer || !layer->gate_w || !layer->bias || !layer->sh_w1 || !layer->sh_w2 || !layer->sh_w3)
-    return fail(MOE_EINVAL, "layer weights must be non-NULL%s%lld");
-  if (!a16(layer->gate_w) || !a16(layer->sh_w1) || !a16(layer->sh_w2) || !a16(layer->sh_w3))
-    return fail(MOE_EINVAL, "the bf16 weights must be 16-byte aligned%s%lld");
+  if (!layer || !layer->gate_w || !layer->bias) return fail(MOE_EINVAL, "layer weights must be non-NULL%s%lld");
+  if (layer->shared_kind == MOE_SHARED_BF16) {
+    if (!layer->sh_w1 || !layer->sh_w2 || !layer->sh_w3)
+      return fail(MOE_EINVAL, "the bf16 shared expert's matrices must be non-NULL%s%lld");
+    if (!a16(layer->sh_w1) || !a16(layer->sh_w2) || !a16(layer->sh_w3))
+      return fail(MOE_EINVAL, "the bf16 weights must be 16-byte aligned%s%lld");
+  } else if (layer->shared_kind == MOE_SHARED_KQUANT) {
+    if (int r = check_experts(&layer->shared_q)) return r;
+  } else {
+    return fail(MOE_EINVAL, "unknown shared_kind%s %lld", "", layer->shared_kind);
+  }
+  if (!a16(layer->gate_w)) return fail(MOE_EINVAL, "gate_w must be 16-byte aligned%s%lld");
   return check_experts(&layer->experts);
+}
+
+bool shared_bf16(const moe_layer& layer) { return layer.shared_kind == MOE_SHARED_BF16; }
+
+XArena layer_arena(const moe_cfg& c, const moe_layer& layer) {
+  return arena_of(layer.experts, c.n_routed, shared_bf16(layer) ? nullptr : &layer.shared_q);
 }
 
 // One layer's launches on `s` (A1-A7), the result to `o`.
 int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, int m, const LayerOut& o,
                    int32_t* hdr, const Ws& w, int32_t* grp, hipStream_t s) {
   hipError_t e;
-  FrontSelect sel{layer.bias, hdr};
+  const bool bf16 = shared_bf16(layer);
+  const XArena ar = layer_arena(c, layer);
+  const int shq = ar.has_shared();
+  FrontSelect sel{layer.bias, hdr, shq};
   if (m > kMaxDecodeTokens) {   // prefill
     std::unique_lock<std::mutex> hold;
     const SideStream* ss = side_stream(hold);
     if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
-    if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
-    if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
-    if ((e = launch_router_pf(x, m, layer.gate_w, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router_pf");
-    if ((e = launch_select(layer.bias, m, c, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
-    if ((e = launch_group(hdr, m, c, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
     // (inter = 256: one down kernel takes every expert, so both gate/up parts stay on the caller's stream)
     const hipStream_t big = c.inter / 256 > 1 ? ss->s : s;
+    const bool side_used = bf16 || big != s;
+    if (bf16) {
+      if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
+      if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
+    }
+    if ((e = launch_router_pf(x, m, layer.gate_w, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router_pf");
+    if ((e = launch_select(layer.bias, m, c, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
+    if ((e = launch_group(hdr, m, c, w, grp, shq, s)) != hipSuccess) return hip_fail(e, "group");
     if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
-    if ((e = launch_gateup_pf(layer.experts, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(layer.experts, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
-    if ((e = launch_gateup_pf(layer.experts, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(layer.experts, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
-    if ((e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
-    if ((e = launch_combine(m, c, w, w.sd, o, s)) != hipSuccess) return hip_fail(e, "combine");
+    if ((e = launch_gateup_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
+    if ((e = launch_gateup_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
+    if (side_used && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
+    if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
   }
-  if (m == 1 && single_token_fits(c)) {   // router + q8_1; selection, routed and shared gate/up; down + combine
+  if (m == 1 && single_token_fits(c, shq)) {   // router + q8_1; selection, routed and shared gate/up; down + combine
     if ((e = launch_front(x, 1, layer.gate_w, nullptr, nullptr, nullptr, c, w, nullptr, s)) != hipSuccess)
       return hip_fail(e, "front");
-    if ((e = launch_gateup_m1(layer.experts, &sel, nullptr, x, &layer, c, w, s)) != hipSuccess)
+    if ((e = launch_gateup_m1(ar, &sel, nullptr, x, bf16 ? &layer : nullptr, c, w, s)) != hipSuccess)
       return hip_fail(e, "gateup_m1");
-    if ((e = launch_down_m1(layer.experts, c, w, layer.sh_w2, o, s)) != hipSuccess) return hip_fail(e, "down_m1");
+    if ((e = launch_down_m1(ar, c, w, bf16 ? layer.sh_w2 : nullptr, o, s)) != hipSuccess) return hip_fail(e, "down_m1");
     return MOE_OK;
   }
-  if ((e = launch_front(x, m, layer.gate_w, &sel, layer.sh_w1, layer.sh_w3, c, w, nullptr, s)) != hipSuccess)
+  if ((e = launch_front(x, m, layer.gate_w, &sel, bf16 ? layer.sh_w1 : nullptr, bf16 ? layer.sh_w3 : nullptr, c, w,
+                        nullptr, s)) != hipSuccess)
     return hip_fail(e, "front");
-  if ((e = launch_gateup(layer.experts, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup");
-  if ((e = launch_down(layer.experts, m, c, w, layer.sh_w2, s)) != hipSuccess) return hip_fail(e, "down");
-  if ((e = launch_combine(m, c, w, w.sd, o, s)) != hipSuccess) return hip_fail(e, "combine");
+  if ((e = launch_gateup(ar, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup");
+  if ((e = launch_down(ar, m, c, w, bf16 ? layer.sh_w2 : nullptr, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");
   return MOE_OK;
 }
 
@@ -295,7 +341,7 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
 // kernels. Every call on a GPU shares the array, so calls that overlap on one
 // GPU race.
 // ---------------------------------------------------------------------------
-constexpr size_t kScratchBytes = (size_t)6 << 20;   // every supported shape at m <= 8 needs at most 5.1 MiB
+constexpr size_t kScratchBytes = (size_t)6 << 20;   // every supported shape at m <= 8 needs at most 5.7 MiB
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
@@ -386,17 +432,18 @@ int moe_experts_decode(const moe_cfg* cfg, const uint16_t* x, int32_t m, const i
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = launch_quant_x(x, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+  const XArena ar = arena_of(*experts, cfg->n_routed, nullptr);
   if (m == 1 && single_token_fits(*cfg)) {
-    if ((e = launch_gateup_m1(*experts, nullptr, header, x, nullptr, *cfg, w, s)) != hipSuccess)
+    if ((e = launch_gateup_m1(ar, nullptr, header, x, nullptr, *cfg, w, s)) != hipSuccess)
       return hip_fail(e, "gateup_m1");
-    if ((e = launch_down_m1(*experts, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) !=
+    if ((e = launch_down_m1(ar, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) !=
         hipSuccess)
       return hip_fail(e, "down_m1");
     return MOE_OK;
   }
   if ((e = launch_plan(header, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "plan");
-  if ((e = launch_gateup(*experts, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
-  if ((e = launch_down(*experts, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_gateup(ar, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "gateup");
+  if ((e = launch_down(ar, m, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "down");
   if ((e = launch_combine(m, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) != hipSuccess)
     return hip_fail(e, "combine");
   return MOE_OK;
@@ -419,14 +466,15 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
   const SideStream* ss = side_stream(hold);
   if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
   if ((e = launch_router_pf(x, m, nullptr, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
-  if ((e = launch_group(header, m, *cfg, w, grp, s)) != hipSuccess) return hip_fail(e, "group");
+  if ((e = launch_group(header, m, *cfg, w, grp, 0, s)) != hipSuccess) return hip_fail(e, "group");
   // (inter = 256: one down kernel takes every expert, so both gate/up parts stay on the caller's stream)
   const hipStream_t big = cfg->inter / 256 > 1 ? ss->s : s;
+  const XArena ar = arena_of(*experts, cfg->n_routed, nullptr);
   if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
-  if ((e = launch_gateup_pf(*experts, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
-  if ((e = launch_down_pf(*experts, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
-  if ((e = launch_gateup_pf(*experts, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-  if ((e = launch_down_pf(*experts, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
+  if ((e = launch_gateup_pf(ar, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
+  if ((e = launch_down_pf(ar, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
+  if ((e = launch_gateup_pf(ar, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+  if ((e = launch_down_pf(ar, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
   if (big != s && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
   if ((e = launch_combine(m, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) != hipSuccess)
     return hip_fail(e, "combine");

@@ -26,7 +26,7 @@ namespace moe {
 namespace {
 
 struct M1Plan {
-  int e[kMaxTopk];     // plan order (ascending id); -1 = dropped
+  int e[kMaxTopk];     // plan order (ascending id; a quantised shared expert last); -1 = dropped
   float w[kMaxTopk];
   int n_u;
 };
@@ -34,10 +34,13 @@ struct M1Plan {
 // Wave 0 fills the block's plan (LDS) from the scores (mode 0) or from the
 // caller's header (mode 1, checked: ids in range, no repeats); the `writer`
 // workgroup also writes the header (mode 0), the plan tables and the status.
+// shq = 1: the layer's quantised shared expert (id n_routed, weight 1) is the
+// plan's last entry.
 template <int KPER>
 __device__ void plan_m1(int mode, bool writer, const float* __restrict__ scores, const float* __restrict__ bias,
                         const int32_t* __restrict__ header_in, int n_routed, int topk, int norm, float route_scale,
-                        int32_t* __restrict__ header_out, PlanView plan, int32_t* __restrict__ status, M1Plan& P) {
+                        int32_t* __restrict__ header_out, PlanView plan, int32_t* __restrict__ status, M1Plan& P,
+                        int shq) {
   const int lane = threadIdx.x & 63;
   int pick = 0;
   float wv = 0.0f;
@@ -69,29 +72,37 @@ __device__ void plan_m1(int mode, bool writer, const float* __restrict__ scores,
     P.e[rank] = pick;
     P.w[rank] = wv;
   }
-  if (lane == 0) P.n_u = ok ? topk : 0;
+  if (lane == topk && shq && ok) {
+    P.e[topk] = n_routed;
+    P.w[topk] = 1.0f;
+  }
+  if (lane == 0) P.n_u = ok ? topk + shq : 0;
   if (writer) {
     if (mode == 0 && lane < topk) {
       header_out[1 + lane] = pick;
       header_out[1 + topk + lane] = (int32_t)__builtin_bit_cast(uint32_t, wv);
       header_out[1 + 2 * topk + rank] = pick;
     }
-    if (lane < topk) {
+    if (lane < topk || (lane == topk && shq)) {
+      const int slot = lane < topk ? rank : topk;
+      const int ex_id = lane < topk ? pick : n_routed;
       if (ok) {
-        plan.u_expert()[rank] = pick;
-        plan.u_first()[rank] = rank;
-        plan.u_npairs()[rank] = 1;
-        plan.pair_tok()[rank] = 0;
-        plan.pair_expert()[rank] = pick;
-        plan.pair_w()[rank] = wv;
-        plan.tok_pairs()[rank] = rank;
+        plan.u_expert()[slot] = ex_id;
+        plan.u_first()[slot] = slot;
+        plan.u_npairs()[slot] = 1;
+        plan.pair_tok()[slot] = 0;
+        plan.pair_expert()[slot] = ex_id;
+        plan.pair_w()[slot] = lane < topk ? wv : 1.0f;
+        plan.tok_pairs()[slot] = slot;
       } else {
         plan.tok_pairs()[lane] = -1;
       }
+    } else if (lane == topk) {
+      plan.tok_pairs()[topk] = -1;   // no shared entry
     }
     if (lane == 0) {
-      *plan.n_u() = ok ? topk : 0;
-      *plan.n_pairs() = ok ? topk : 0;
+      *plan.n_u() = ok ? topk + shq : 0;
+      *plan.n_pairs() = ok ? topk + shq : 0;
       if (mode == 0) header_out[0] = nan_any ? MOE_STATUS_NAN_KEY : 0;
       const int st = (nan_any ? MOE_STATUS_NAN_KEY : 0) | (ok ? 0 : MOE_STATUS_BAD_PICK);
       if (st) atomicOr(status, st);
@@ -102,8 +113,9 @@ __device__ void plan_m1(int mode, bool writer, const float* __restrict__ scores,
 struct GateUp1Args {
   int mode;                 // 0: select from the scores; 1: the caller's header
   int shared_blocks;        // leading workgroups that only run shared-expert units (mode 0 with the layer)
-  int shared_units;         // hidden units of the shared expert done here (0: none)
-  moe_experts ex;
+  int shared_units;         // hidden units of the bf16 shared expert done here (0: none)
+  XArena ex;                // the routed experts, and a quantised shared expert as id n_routed
+  int slots;                // plan entries with a gate/up row group each: topk, + 1 for a quantised shared expert
   const float* bias;
   const int32_t* hdr_in;
   int32_t* hdr_out;
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
     const int sb = threadIdx.x % NSB;
     if (wave == 0) {
       plan_m1<KPER>(a.mode, blk == 0, w.scores, a.bias, a.hdr_in, a.n_routed, a.topk, a.norm, a.route_scale,
-                    a.hdr_out, w.plan, w.status, P);
+                    a.hdr_out, w.plan, w.status, P, a.slots - a.topk);
     } else {   // meanwhile the other waves stage the token's q8_1 activation and run a shared unit each;
                // the unit's loads and the activation's are in flight together
       const bool unit = wave - 1 < nu;
@@ -202,10 +214,10 @@ __global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
     if (e >= 0) {
       Act A;
       load_act_lds<NSB>(A, act_lds, sb);
-      const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
+      const uint8_t* gbase = a.ex.gate(e);
+      const uint8_t* ubase = a.ex.up(e);
       auto tile_src = [&](int c) -> const uint8_t* {
-        const uint64_t off = (c & 1) ? a.ex.up_off : a.ex.gate_off;
-        return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
+        return ((c & 1) ? ubase : gbase) + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
       };
 #pragma unroll
       for (int c = 0; c < SLOTS && c < 4; ++c)
@@ -303,8 +315,10 @@ struct DownM1Geom {
 
 constexpr int kDownRows = 16;
 
+// slots: one wave per plan entry (the picks, and a quantised shared expert as
+// the last, weight 1); SHARED: two more waves for the bf16 shared expert's rows.
 template <int NSB, bool SHARED>
-__global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, int inter, int topk,
+__global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int inter, int slots,
                                                  const uint16_t* __restrict__ w2, LayerOut o) {
   using G = DownM1Geom<NSB, kDownRows>;
   extern __shared__ __align__(16) uint8_t lds[];
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = blockIdx.x * kDownRows;
   const int n_u = *w.plan.n_u();
-  if (wave < topk) {
+  if (wave < slots) {
     const int e_slot = w.plan.u_expert()[wave];   // (loaded together with n_u: no dependent round trip)
     const int e = wave < n_u ? e_slot : -1;
     if (e >= 0) {
@@ -322,8 +336,7 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
       uint8_t* mine = lds + wave * G::kWaveBytes;
       // the rows, then this expert's q8_1(h) into registers: every load is in
       // flight at once, and one wait covers them all
-      dma_wave<G::kChunks>((const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off +
-                               (uint64_t)row0 * G::kRowBytes, mine);
+      dma_wave<G::kChunks>(ex.down(e) + (uint64_t)row0 * G::kRowBytes, mine);
       constexpr int kAP = (ActLds<NSB>::kChunks + 63) / 64;
       u32x4 piece[kAP];
 #pragma unroll
@@ -356,11 +369,11 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
     } else if (lane < kDownRows) {
       ys[wave][lane] = 0.0f;
     }
-  } else if (SHARED && wave < topk + 2) {
+  } else if (SHARED && wave < slots + 2) {
     // shared expert down rows: half of the block's rows per wave, f32
     constexpr int kR = kDownRows / 2;
     constexpr int kCh = NSB >= 2 ? NSB / 2 : 1;   // 16-byte chunks of a row per lane (inter = 256*NSB)
-    const int rbase = row0 + kR * (wave - topk);
+    const int rbase = row0 + kR * (wave - slots);
     float p[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) p[r] = 0.0f;
@@ -396,7 +409,7 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
 #pragma unroll
       for (int r = 0; r < kR; ++r)
         if (r == lane) v = p[r];
-      sds[kR * (wave - topk) + lane] = v;
+      sds[kR * (wave - slots) + lane] = v;
       w.sd[rbase + lane] = v;
     }
   }
@@ -404,8 +417,8 @@ __global__ __launch_bounds__(512) void k_down_m1(moe_experts ex, Ws w, int dim, 
   if (threadIdx.x < kDownRows) {
     const int r = threadIdx.x;
     float acc = 0.0f;
-    for (int i = 0; i < topk; ++i)
-      if (i < n_u) acc = fadd(acc, fmul(w.plan.pair_w()[i], ys[i][r]));
+    for (int i = 0; i < slots; ++i)
+      if (i < n_u) acc = fadd(acc, fmul(w.plan.pair_w()[i], ys[i][r]));   // a quantised shared expert last, weight 1
     if (SHARED) acc = fadd(acc, sds[r]);
     if (o.f32) o.f32[row0 + r] = acc;
     if (o.bf16) o.bf16[row0 + r] = bf16_rne(acc);
@@ -429,16 +442,17 @@ hipError_t launch_gateup_m1_t(const GateUp1Args& a, const moe_cfg& c, const Ws& 
     if (e != hipSuccess) return e;
     attr_set[ai] = true;
   }
-  MOE_LAUNCH(MOE_K_GATEUP, kern, dim3(a.shared_blocks + c.topk * (c.inter / 32)), dim3(256), shm, s, a, w);
+  MOE_LAUNCH(MOE_K_GATEUP, kern, dim3(a.shared_blocks + a.slots * (c.inter / 32)), dim3(256), shm, s, a, w);
   return hipGetLastError();
 }
 
 template <int NSB>
-hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
+hipError_t launch_down_m1_t(const XArena& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
                             hipStream_t s) {
   using G = DownM1Geom<NSB, kDownRows>;
-  size_t shm = (size_t)c.topk * G::kWaveBytes;
-  const int threads = 64 * (c.topk + (w2 ? 2 : 0));
+  const int slots = c.topk + ex.has_shared();
+  size_t shm = (size_t)slots * G::kWaveBytes;
+  const int threads = 64 * (slots + (w2 ? 2 : 0));
   auto kern = w2 ? k_down_m1<NSB, true> : k_down_m1<NSB, false>;
   static bool attr_set[2] = {false, false};
   const int ai = w2 ? 1 : 0;
@@ -448,18 +462,19 @@ hipError_t launch_down_m1_t(const moe_experts& ex, const moe_cfg& c, const Ws& w
     if (e != hipSuccess) return e;
     attr_set[ai] = true;
   }
-  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, c.topk, w2,
+  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, slots, w2,
              o);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const int32_t* hdr_in,
+hipError_t launch_gateup_m1(const XArena& ex, const FrontSelect* sel, const int32_t* hdr_in,
                             const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s) {
   GateUp1Args a;
   a.mode = sel ? 0 : 1;
-  const int routed_blocks = c.topk * (c.inter / 32);
+  a.slots = c.topk + ex.has_shared();
+  const int routed_blocks = a.slots * (c.inter / 32);
   a.shared_units = (sel && layer) ? c.inter : 0;
   const int rest = a.shared_units - kUnitsRouted * routed_blocks;
   a.shared_blocks = rest > 0 ? (rest + kUnitsShared - 1) / kUnitsShared : 0;
@@ -487,7 +502,7 @@ hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const
   }
 }
 
-hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
+hipError_t launch_down_m1(const XArena& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
                           hipStream_t s) {
   hipError_t err;
   switch (c.inter / 256) {

@@ -33,7 +33,7 @@ namespace {
 // thus loads its token's activation once and keeps it for every tile.
 // ---------------------------------------------------------------------------
 template <int NSB, int SLOTS>
-__global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, const int8_t* __restrict__ xq,
+__global__ __launch_bounds__(256) void k_gateup(XArena ex, PlanView plan, const int8_t* __restrict__ xq,
                                                 const uint16_t* __restrict__ xd, const int32_t* __restrict__ xs,
                                                 int dim, int inter, float* __restrict__ g_out,
                                                 float* __restrict__ u_out, float* __restrict__ h_out,
@@ -52,10 +52,10 @@ __global__ __launch_bounds__(256) void k_gateup(moe_experts ex, PlanView plan, c
   const int sb = threadIdx.x % NSB, g = threadIdx.x / NSB;
   const int j = g % np_pad, rg = g / np_pad, RG = kGroups / np_pad;
   const bool has = j < np;
-  const uint8_t* ebase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride;
+  const uint8_t* gbase = ex.gate(e);
+  const uint8_t* ubase = ex.up(e);
   auto tile_src = [&](int c) -> const uint8_t* {
-    const uint64_t off = (c & 1) ? ex.up_off : ex.gate_off;
-    return ebase + off + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
+    return ((c & 1) ? ubase : gbase) + (uint64_t)(32 * grp + 16 * (c >> 1)) * G::kRowBytes;
   };
   Act A;
   {
@@ -221,7 +221,7 @@ __device__ void shared_down_rows(int blk, int m, int dim, int inter, const uint1
 }
 
 template <int NSB>
-__global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, const int8_t* __restrict__ hq,
+__global__ __launch_bounds__(256) void k_down(XArena ex, PlanView plan, const int8_t* __restrict__ hq,
                                               const uint16_t* __restrict__ hd, const int32_t* __restrict__ hs,
                                               int dim, int inter, float* __restrict__ y, int shared_blocks, int m,
                                               const uint16_t* __restrict__ w2, const uint16_t* __restrict__ sh,
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void k_down(moe_experts ex, PlanView plan, con
   const int j = g % np_pad, rg = g / np_pad, RG = kGroups / np_pad;
   const bool has = j < np;
   const int pair = first + (has ? j : 0);
-  const uint8_t* mbase = (const uint8_t*)ex.base + (uint64_t)e * ex.stride + ex.down_off;
+  const uint8_t* mbase = ex.down(e);
   Act A;
   load_act(A, hq + (int64_t)pair * inter, hd + (int64_t)pair * (inter / 32), hs + (int64_t)pair * (inter / 16), sb);
 #pragma unroll
@@ -273,20 +273,21 @@ __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __r
   const int t = blockIdx.y;
   const int r = 4 * (blockIdx.x * 256 + threadIdx.x);   // dim is a multiple of 256
   if (r >= dim) return;
-  int pp[kMaxTopk];
-  float pw[kMaxTopk];
+  // the token's plan entries (its picks, then a quantised shared expert of weight 1: RN(1 * y) = y)
+  int pp[kMaxSlots];
+  float pw[kMaxSlots];
 #pragma unroll
-  for (int i = 0; i < kMaxTopk; ++i) {
-    pp[i] = i < topk ? plan.tok_pairs()[t * topk + i] : -1;
+  for (int i = 0; i < kMaxSlots; ++i) {
+    pp[i] = i <= topk ? plan.tok_pairs()[t * plan.slots() + i] : -1;
     pw[i] = pp[i] >= 0 ? plan.pair_w()[pp[i]] : 0.0f;
   }
-  float4 yv[kMaxTopk];
+  float4 yv[kMaxSlots];
 #pragma unroll
-  for (int i = 0; i < kMaxTopk; ++i)
+  for (int i = 0; i < kMaxSlots; ++i)
     yv[i] = pp[i] >= 0 ? *reinterpret_cast<const float4*>(y + (int64_t)pp[i] * dim + r) : make_float4(0, 0, 0, 0);
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < kMaxTopk; ++i) {
+  for (int i = 0; i < kMaxSlots; ++i) {
     if (pp[i] >= 0) {
       const float v[4] = {yv[i].x, yv[i].y, yv[i].z, yv[i].w};
 #pragma unroll
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void k_combine(PlanView plan, const float* __r
 constexpr int kGateUpSlots = 2;
 
 template <int NSB>
-hipError_t launch_gateup_t(const moe_experts& ex, int max_u, const moe_cfg& c, const Ws& w, hipStream_t s) {
+hipError_t launch_gateup_t(const XArena& ex, int max_u, const moe_cfg& c, const Ws& w, hipStream_t s) {
   using G = GateUpGeom<NSB>;
   auto kern = k_gateup<NSB, kGateUpSlots>;
   const size_t shm = (size_t)kGateUpSlots * G::kTileBytes;
@@ -329,7 +330,7 @@ hipError_t launch_gateup_t(const moe_experts& ex, int max_u, const moe_cfg& c, c
 }
 
 template <int NSB>
-hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg& c, const Ws& w, const uint16_t* w2,
+hipError_t launch_down_t(const XArena& ex, int m, int max_u, const moe_cfg& c, const Ws& w, const uint16_t* w2,
                          hipStream_t s) {
   using G = DownGeom<NSB>;
   auto kern = k_down<NSB>;
@@ -352,8 +353,8 @@ hipError_t launch_down_t(const moe_experts& ex, int m, int max_u, const moe_cfg&
 
 }  // namespace
 
-hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
-  const int max_u = min(c.n_routed, m * c.topk);
+hipError_t launch_gateup(const XArena& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  const int max_u = min(c.n_routed, m * c.topk) + ex.has_shared();
   hipError_t err;
   switch (c.dim / 256) {
     case 1: err = launch_gateup_t<1>(ex, max_u, c, w, s); break;
@@ -366,9 +367,9 @@ hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const W
   return err;
 }
 
-hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
+hipError_t launch_down(const XArena& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
                        hipStream_t s) {
-  const int max_u = min(c.n_routed, m * c.topk);
+  const int max_u = min(c.n_routed, m * c.topk) + ex.has_shared();
   hipError_t err;
   switch (c.inter / 256) {
     case 1: err = launch_down_t<1>(ex, m, max_u, c, w, w2, s); break;

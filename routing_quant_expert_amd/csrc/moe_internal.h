@@ -15,6 +15,7 @@ constexpr int kMaxDecodeTokens = 8;   // the union-of-experts decode path
 constexpr int kMaxTokens = 65535;      // tokens of one call (see check_m)
 constexpr int kMaxTopk = 8;
 constexpr int kMaxTopkM1 = 6;   // the single-token kernels: one wave per pick + two shared-expert waves in 512 threads
+constexpr int kMaxSlots = kMaxTopk + 1;   // a token's plan entries: its picks and the quantised shared expert
 constexpr int kMaxRouted = 1024;
 constexpr int kQ2KBytes = 84;
 constexpr int kQ3KBytes = 110;
@@ -22,8 +23,10 @@ constexpr int kQ3KBytes = 110;
 // Plan tables inside the workspace (int32 words):
 //   [0] n_u (distinct experts), [1] n_pairs,
 //   then max_pairs entries each of u_expert, u_first, u_npairs, pair_tok,
-//   pair_expert, pair_w (f32 bits), then tok_pairs [max_m][topk] (pair index
-//   of each of a token's picks in ascending expert id; -1 = none).
+//   pair_expert, pair_w (f32 bits), then tok_pairs [max_m][topk + 1] (pair
+//   index of each of a token's plan entries in ascending expert id: its
+//   picks, then, for a layer whose shared expert is quantised, that expert as
+//   id n_routed with weight 1; -1 = none).
 struct PlanView {
   int32_t* base;
   int max_pairs, max_m, topk;
@@ -36,8 +39,35 @@ struct PlanView {
   __host__ __device__ int32_t* pair_expert() const { return base + 2 + 4 * max_pairs; }
   __host__ __device__ float* pair_w() const { return reinterpret_cast<float*>(base + 2 + 5 * max_pairs); }
   __host__ __device__ int32_t* tok_pairs() const { return base + 2 + 6 * max_pairs; }
-  static int words(int max_pairs, int max_m, int topk) { return 2 + 6 * max_pairs + max_m * topk; }
+  __host__ __device__ int slots() const { return topk + 1; }   // tok_pairs entries per token
+  static int words(int max_pairs, int max_m, int topk) { return 2 + 6 * max_pairs + max_m * (topk + 1); }
 };
+
+// The expert blocks as the kernels address them: routed expert e < n_routed
+// at base + e * stride, each matrix at its offset inside; id n_routed is the
+// layer's shared expert when its matrices are K-quant blocks (Q2_K gate/up,
+// Q3_K down at sbase + the s*_off offsets), run on the same kernels as one
+// more expert of every token [moe_v41.rs, struct MoeV41LayerWeights: the
+// shared matrices as resident bf16 or the GGUF's Q2_K/Q3_K blocks on the
+// routed experts' kernels].
+struct XArena {
+  const uint8_t* base;
+  uint64_t stride, gate_off, up_off, down_off;
+  const uint8_t* sbase;   // nullptr: the layer has no quantised shared expert
+  uint64_t sgate_off, sup_off, sdown_off;
+  int n_routed;
+  __host__ __device__ bool shared(int e) const { return e >= n_routed; }
+  __host__ __device__ const uint8_t* blocks(int e) const { return shared(e) ? sbase : base + (uint64_t)e * stride; }
+  __host__ __device__ uint64_t goff(int e) const { return shared(e) ? sgate_off : gate_off; }
+  __host__ __device__ uint64_t uoff(int e) const { return shared(e) ? sup_off : up_off; }
+  __host__ __device__ uint64_t doff(int e) const { return shared(e) ? sdown_off : down_off; }
+  __host__ __device__ const uint8_t* gate(int e) const { return blocks(e) + goff(e); }
+  __host__ __device__ const uint8_t* up(int e) const { return blocks(e) + uoff(e); }
+  __host__ __device__ const uint8_t* down(int e) const { return blocks(e) + doff(e); }
+  __host__ __device__ int has_shared() const { return sbase ? 1 : 0; }
+};
+// The routed arena alone (shared_q NULL), or with the layer's quantised shared expert.
+XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q);
 
 // Control words (workspace region `ctl`, 256 bytes, zero between calls).
 struct Ctl {
@@ -93,15 +123,16 @@ struct LayerOut {
 struct FrontSelect {
   const float* bias;
   int32_t* header;
+  int shq;   // 1: the plan also gets the layer's quantised shared expert (id n_routed) for every token
 };
 hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const FrontSelect* sel, const uint16_t* w1,
                         const uint16_t* w3, const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s);
 hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
 hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s);
 hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_gateup(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+hipError_t launch_gateup(const XArena& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
 // down: routed Q3_K rows, plus the shared expert's down rows when w2 is given.
-hipError_t launch_down(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
+hipError_t launch_down(const XArena& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
                        hipStream_t s);
 hipError_t launch_combine(int m, const moe_cfg& c, const Ws& w, const float* sd, const LayerOut& o, hipStream_t s);
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s);
@@ -110,9 +141,9 @@ hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out,
 // expert's gate/up rows run in the same launch when `layer` is given too) or
 // from the caller's header (checked here); then the down rows of every pick +
 // the shared expert's down rows + the combine.
-hipError_t launch_gateup_m1(const moe_experts& ex, const FrontSelect* sel, const int32_t* hdr_in,
+hipError_t launch_gateup_m1(const XArena& ex, const FrontSelect* sel, const int32_t* hdr_in,
                             const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_down_m1(const moe_experts& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
+hipError_t launch_down_m1(const XArena& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
                           hipStream_t s);
 // Zero-fill of `bytes` bytes (a multiple of 16) with a kernel (no memset node).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);

@@ -158,17 +158,23 @@ __global__ __launch_bounds__(256) void k_router_pf(const uint16_t* __restrict__ 
 // Grouping by expert. Scratch `grp` (int32): tok_ok [m], e_first [n_routed],
 // e_count [n_routed].
 // ---------------------------------------------------------------------------
+// shq = 1: every token that keeps its picks also gets the layer's quantised
+// shared expert (id n_routed, weight 1): one more group after all routed
+// ones, holding those tokens in ascending order.
 __global__ __launch_bounds__(1024) void k_group_count(const int32_t* __restrict__ header, int m, int topk, int n_routed,
                                                      PlanView plan, int32_t* __restrict__ grp,
-                                                     int32_t* __restrict__ status) {
+                                                     int32_t* __restrict__ status, int shq) {
   __shared__ int cnt[kMaxRouted];
   __shared__ int wtot[2][16];
+  __shared__ int n_ok;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hw = 1 + 3 * topk;
+  const int slots = plan.slots();
   int32_t* tok_ok = grp;
   int32_t* e_first = grp + m;
-  int32_t* e_count = e_first + n_routed;
+  int32_t* e_count = e_first + n_routed + 1;
   for (int e = tid; e < n_routed; e += 1024) cnt[e] = 0;
+  if (tid == 0) n_ok = 0;
   __syncthreads();
   bool bad_any = false;
   for (int t = tid; t < m; t += 1024) {
@@ -188,9 +194,11 @@ __global__ __launch_bounds__(1024) void k_group_count(const int32_t* __restrict_
     for (int r = 0; r < kMaxTopk; ++r) {
       if (r < topk) {
         if (ok) atomicAdd(&cnt[p[r]], 1);
-        else plan.tok_pairs()[(int64_t)t * topk + r] = -1;
+        else plan.tok_pairs()[(int64_t)t * slots + r] = -1;
       }
     }
+    if (ok && shq) atomicAdd(&n_ok, 1);
+    else plan.tok_pairs()[(int64_t)t * slots + topk] = -1;   // no shared entry (k_group_fill writes the others)
     bad_any |= !ok;
   }
   if (bad_any) atomicOr(status, MOE_STATUS_BAD_PICK);
@@ -225,9 +233,17 @@ __global__ __launch_bounds__(1024) void k_group_count(const int32_t* __restrict_
       plan.u_npairs()[uid] = c;
     }
   }
-  if (tid == 1023) {   // totals over all 16 waves (threads past n_routed add 0)
-    *plan.n_pairs() = bv + v;
-    *plan.n_u() = bf + f;
+  if (tid == 1023) {   // totals over all 16 waves (threads past n_routed add 0), then the shared group
+    const int np = bv + v, nu = bf + f;
+    e_first[n_routed] = np;
+    e_count[n_routed] = n_ok;
+    if (n_ok > 0) {
+      plan.u_expert()[nu] = n_routed;
+      plan.u_first()[nu] = np;
+      plan.u_npairs()[nu] = n_ok;
+    }
+    *plan.n_pairs() = np + n_ok;
+    *plan.n_u() = nu + (n_ok > 0 ? 1 : 0);
   }
 }
 
@@ -239,10 +255,27 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
   const int e = blockIdx.x, lane = threadIdx.x;
   const int32_t* tok_ok = grp;
   const int32_t* e_first = grp + m;
-  const int32_t* e_count = e_first + n_routed;
+  const int32_t* e_count = e_first + n_routed + 1;
   if (e_count[e] == 0) return;
   int pos = e_first[e];
   const int hw = 1 + 3 * topk;
+  const int slots = plan.slots();
+  if (e == n_routed) {   // the quantised shared expert: every token that keeps its picks, ascending, weight 1
+    for (int t0 = 0; t0 < m; t0 += 64) {
+      const int t = t0 + lane;
+      const bool hit = t < m && tok_ok[t] != 0;
+      const unsigned long long mask = __ballot(hit);
+      if (hit) {
+        const int p = pos + __popcll(mask & ((1ull << lane) - 1ull));
+        plan.pair_tok()[p] = t;
+        plan.pair_expert()[p] = e;
+        plan.pair_w()[p] = 1.0f;
+        plan.tok_pairs()[(int64_t)t * slots + topk] = p;
+      }
+      pos += __popcll(mask);
+    }
+    return;
+  }
   const int64_t P = (int64_t)m * topk;
   // kB rows of 64 picks at a time: their loads are all issued before any
   // ballot (the plan stores in between would otherwise keep each row's loads
@@ -296,7 +329,7 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
           slot = 0;
           for (int r2 = 0; r2 < topk; ++r2) slot += h[1 + r2] < e ? 1 : 0;
         }
-        plan.tok_pairs()[(int64_t)t * topk + slot] = p;
+        plan.tok_pairs()[(int64_t)t * slots + slot] = p;
       }
       pos += __popcll(mask);
     }
@@ -317,7 +350,7 @@ __global__ __launch_bounds__(64) void k_group_fill(const int32_t* __restrict__ h
 // block scales as float64 ([block][token]).
 // ---------------------------------------------------------------------------
 struct GateUpPfArgs {
-  moe_experts ex;
+  XArena ex;
   PlanView plan;
   const int8_t* xq;
   const double* xd64;
@@ -456,9 +489,9 @@ __device__ __forceinline__ void gateup_pf_body(const GateUpPfArgs& a, uint8_t* l
   if (SMALL ? np > 8 : np <= 8) return;   // the other kernel's expert
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
   if (tid < 16) lut[tid] = ((uint32_t)tid * 0x030201u) << 8;   // bytes {0, sc, 2sc, 3sc}
-  const uint8_t* ebase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride;
-  const uint32_t ebytes = (uint32_t)((a.ex.gate_off > a.ex.up_off ? a.ex.gate_off : a.ex.up_off) +
-                                     (uint64_t)a.inter * NSB * kQ2KBytes);
+  const uint8_t* ebase = a.ex.blocks(e);
+  const uint64_t goff = a.ex.goff(e), uoff = a.ex.uoff(e);
+  const uint32_t ebytes = (uint32_t)((goff > uoff ? goff : uoff) + (uint64_t)a.inter * NSB * kQ2KBytes);
   const __amdgpu_buffer_rsrc_t rw = buf_rsrc(ebase, ebytes);
   const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a.xq, (uint32_t)((uint64_t)a.m * dim));
   const __amdgpu_buffer_rsrc_t rd = buf_rsrc(a.xd64, (uint32_t)((uint64_t)a.m * NB * 8));
@@ -468,7 +501,7 @@ __device__ __forceinline__ void gateup_pf_body(const GateUpPfArgs& a, uint8_t* l
   for (int k = 0; k < 12; ++k) {
     const int i = tid + 256 * k, r = i / 24, dw = i % 24;
     const int wr = r >> 5, row = 64 * grp + 32 * (wr & 1) + (r & 31);
-    woff[k] = (uint32_t)(((wr >> 1) ? a.ex.up_off : a.ex.gate_off) + (uint64_t)row * (NSB * kQ2KBytes)) +
+    woff[k] = (uint32_t)(((wr >> 1) ? uoff : goff) + (uint64_t)row * (NSB * kQ2KBytes)) +
               4u * (uint32_t)(dw < 21 ? dw : 0);
   }
   for (int c0 = 0; c0 < np; c0 += kChunk) {
@@ -556,7 +589,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 // v_perm from an 8-byte table per scale value. The MFMA sum is -S_b.
 // ---------------------------------------------------------------------------
 struct DownPfArgs {
-  moe_experts ex;
+  XArena ex;
   PlanView plan;
   const int8_t* hq;
   const uint16_t* hd;
@@ -650,8 +683,7 @@ __global__ __launch_bounds__(256) void k_down_pf_direct(DownPfArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5;
   q3k_lut_fill(lut);
   const int row = 128 * rt + 32 * wave + (lane & 31);
-  const uint8_t* wrow =
-      (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride + a.ex.down_off + (uint64_t)row * (NSB * kQ3KBytes);
+  const uint8_t* wrow = a.ex.down(e) + (uint64_t)row * (NSB * kQ3KBytes);
   for (int c0 = 0; c0 < np; c0 += kChunk) {
     const int nt = min(kChunk, np - c0);
     const int64_t p0 = first + c0;
@@ -793,7 +825,7 @@ __device__ __forceinline__ void down_pf_body(const DownPfArgs& a, uint8_t* lds) 
   if (SMALL ? np > 8 : np <= 8) return;   // the other kernel's expert
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   q3k_lut_fill(lut);
-  const uint8_t* wbase = (const uint8_t*)a.ex.base + (uint64_t)e * a.ex.stride + a.ex.down_off;
+  const uint8_t* wbase = a.ex.down(e);
   const __amdgpu_buffer_rsrc_t rw = buf_rsrc(wbase, (uint32_t)((uint64_t)a.dim * NSB * kQ3KBytes));
   const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a.hq, (uint32_t)((uint64_t)a.n_pairs_max * inter));
   const __amdgpu_buffer_rsrc_t rd = buf_rsrc(a.hd64, (uint32_t)((uint64_t)a.n_pairs_max * NB * 8));
@@ -904,16 +936,18 @@ hipError_t launch_router_pf(const uint16_t* x, int m, const uint16_t* gate_w, co
   return hipGetLastError();
 }
 
-hipError_t launch_group(const int32_t* header, int m, const moe_cfg& c, const Ws& w, int32_t* grp, hipStream_t s) {
-  hipLaunchKernelGGL(k_group_count, dim3(1), dim3(1024), 0, s, header, m, c.topk, c.n_routed, w.plan, grp, w.status);
+hipError_t launch_group(const int32_t* header, int m, const moe_cfg& c, const Ws& w, int32_t* grp, int shq,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k_group_count, dim3(1), dim3(1024), 0, s, header, m, c.topk, c.n_routed, w.plan, grp, w.status,
+                     shq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_group_fill, dim3(c.n_routed), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, grp);
+  hipLaunchKernelGGL(k_group_fill, dim3(c.n_routed + shq), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, grp);
   return hipGetLastError();
 }
 
-hipError_t launch_gateup_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
-  const int max_u = min(c.n_routed, m * c.topk);
+hipError_t launch_gateup_pf(const XArena& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
+  const int max_u = min(c.n_routed, m * c.topk) + ex.has_shared();
   GateUpPfArgs a{ex, w.plan, w.xq, w.xd64, m, c.inter, c.swiglu_limit, w.g, w.u, w.h, w.hq, w.hd, w.hd64, w.hs};
   switch (c.dim / 256) {
     case 1: return launch_gateup_pf_t<1>(a, max_u, part, s);
@@ -925,9 +959,9 @@ hipError_t launch_gateup_pf(const moe_experts& ex, int m, const moe_cfg& c, cons
   }
 }
 
-hipError_t launch_down_pf(const moe_experts& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
-  const int max_u = min(c.n_routed, m * c.topk);
-  DownPfArgs a{ex, w.plan, w.hq, w.hd, w.hd64, m * c.topk, c.dim, w.y};
+hipError_t launch_down_pf(const XArena& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
+  const int max_u = min(c.n_routed, m * c.topk) + ex.has_shared();
+  DownPfArgs a{ex, w.plan, w.hq, w.hd, w.hd64, m * (c.topk + 1), c.dim, w.y};
   switch (c.inter / 256) {
     case 1: return launch_down_pf_t<1>(a, max_u, part, s);
     case 2: return launch_down_pf_t<2>(a, max_u, part, s);

@@ -81,9 +81,12 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
 // distinct experts with a smaller id. A pair's position is then its expert's
 // pair count plus the tokens below it in the mask.
 // ---------------------------------------------------------------------------
+// With shq = 1 every token that keeps its picks also gets the layer's
+// quantised shared expert (id n_routed, weight 1) as its last plan entry: one
+// more distinct expert whose pairs follow all routed pairs, tokens ascending.
 template <int KPER>
 __device__ void build_plan(const int* picks, const float* wts, const int* tok_ok, int m, int topk, PlanView plan,
-                           uint32_t* emap) {
+                           uint32_t* emap, int shq, int n_routed) {
   static_assert(kMaxDecodeTokens <= 8, "token masks are 8 bits");
   const int lane = threadIdx.x & 63;
   const int P = m * topk;
@@ -127,14 +130,33 @@ __device__ void build_plan(const int* picks, const float* wts, const int* tok_ok
       plan.u_first()[uid] = pos;
       plan.u_npairs()[uid] = __popc(v & 0xffu);
     }
-    plan.tok_pairs()[t * topk + rk] = pos;
+    plan.tok_pairs()[t * plan.slots() + rk] = pos;
   } else if (mine) {
-    plan.tok_pairs()[lane] = -1;
+    plan.tok_pairs()[t * plan.slots() + (lane - t * topk)] = -1;
   }
   const unsigned long long vb = __ballot(valid);
+  const int n_pairs = __popcll(vb);
+  const int n_u = (int)(__builtin_amdgcn_readlane((int)incl, 63) >> 16);
+  const unsigned long long okm = __ballot(lane < m && tok_ok[lane]) & (shq ? ~0ull : 0ull);
+  const int n_ok = __popcll(okm);
+  if (lane < m) {   // the token's last plan entry: the quantised shared expert, or none
+    int q = -1;
+    if ((okm >> lane) & 1ull) {
+      q = n_pairs + __popcll(okm & ((1ull << lane) - 1ull));
+      plan.pair_tok()[q] = lane;
+      plan.pair_expert()[q] = n_routed;
+      plan.pair_w()[q] = 1.0f;
+    }
+    plan.tok_pairs()[lane * plan.slots() + topk] = q;
+  }
   if (lane == 0) {
-    *plan.n_pairs() = __popcll(vb);
-    *plan.n_u() = (int32_t)(__builtin_amdgcn_readlane((int)incl, 63) >> 16);
+    *plan.n_pairs() = n_pairs + n_ok;
+    *plan.n_u() = n_u + (n_ok > 0 ? 1 : 0);
+    if (n_ok > 0) {
+      plan.u_expert()[n_u] = n_routed;
+      plan.u_first()[n_u] = n_pairs;
+      plan.u_npairs()[n_u] = n_ok;
+    }
   }
 }
 
@@ -149,6 +171,7 @@ struct FrontArgs {
   const uint16_t* w3;
   float* logits_out;
   int router_blocks, shared_blocks;
+  int shq;   // the plan gets the layer's quantised shared expert (id n_routed) for every token
 };
 
 // Every token's selection and the plan [moe_v41.rs, fn route_from_logits;
@@ -175,7 +198,7 @@ __device__ void select_all(const FrontArgs& a, const Ws& w) {
                        picks + t1 * a.topk, wts + t1 * a.topk, w.status);
   if (threadIdx.x < a.m) tok_ok[threadIdx.x] = 1;
   __syncthreads();
-  if (wave == 0) build_plan<KPER>(picks, wts, tok_ok, a.m, a.topk, w.plan, emap);
+  if (wave == 0) build_plan<KPER>(picks, wts, tok_ok, a.m, a.topk, w.plan, emap, a.shq, a.n_routed);
 }
 
 __global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ h
     if (!ok) atomicOr(status, MOE_STATUS_BAD_PICK);
   }
   __builtin_amdgcn_wave_barrier();
-  build_plan<KPER>(picks, wts, tok_ok, m, topk, plan, emap);
+  build_plan<KPER>(picks, wts, tok_ok, m, topk, plan, emap, 0, n_routed);
 }
 
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, int64_t n, float temp,
@@ -284,6 +307,7 @@ hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const 
   a.logits_out = logits_out;
   a.router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
   a.shared_blocks = w1 ? (c.inter + 3) / 4 : 0;
+  a.shq = sel ? sel->shq : 0;
   const int quant_blocks = (int)((int64_t)m * c.dim / 256);
   MOE_LAUNCH(MOE_K_ROUTER, k_front, dim3(a.router_blocks + a.shared_blocks + quant_blocks), dim3(256), 0, s, a, w);
   return hipGetLastError();

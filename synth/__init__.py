@@ -277,6 +277,7 @@ class LayerSpec:
     seed: int = 1
     layer: int = 0
     zipf_bias: bool = False
+    shared_quant: bool = False   # the shared expert as K-quant blocks (Q2_K gate/up, Q3_K down) instead of bf16
 
     def tag(self, kind: int, index: int = 0, sub: int = 0) -> int:
         return make_tag(kind, self.layer, index, sub)
@@ -325,6 +326,12 @@ def expert_blocks(spec: LayerSpec, e: int, which: str) -> np.ndarray:
         return q2k_blocks(spec.seed, spec.tag(kind, e), 0, nb).reshape(s.inter, s.nsb_gate * Q2K_BYTES)
     nb = s.dim * s.nsb_down
     return q3k_blocks(spec.seed, spec.tag(K_EXP_DOWN, e), 0, nb).reshape(s.dim, s.nsb_down * Q3K_BYTES)
+
+
+def shared_q_blocks(spec: LayerSpec, which: str) -> np.ndarray:
+    """The K-quant shared expert's raw blocks: drawn exactly like a routed
+    expert's, under the expert index n_routed (no routed expert has it)."""
+    return expert_blocks(spec, spec.shape.n_routed, which)
 
 
 def expert_bytes(spec: LayerSpec, e: int) -> np.ndarray:

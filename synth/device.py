@@ -60,13 +60,25 @@ def normal_bf16_into(t, seed: int, tag: int, sigma: float, i0: int = 0):
     _ok(lib().synth_normal_bf16(t.data_ptr(), seed, tag, i0, t.numel(), sigma, _stream()))
 
 
+def fill_expert(spec: LayerSpec, buf, e: int):
+    """Expert index e's blocks (gate | up | down, one stride) into a uint8
+    device tensor; e = n_routed gives the K-quant shared expert."""
+    s = spec.shape
+    assert buf.numel() >= s.expert_stride and buf.data_ptr() % 16 == 0
+    p, st = buf.data_ptr(), _stream()
+    _ok(lib().synth_q2k_blocks(p + s.gate_off, spec.seed, spec.tag(K_EXP_GATE, e), 0, s.inter * s.nsb_gate, st))
+    _ok(lib().synth_q2k_blocks(p + s.up_off, spec.seed, spec.tag(K_EXP_UP, e), 0, s.inter * s.nsb_gate, st))
+    _ok(lib().synth_q3k_blocks(p + s.down_off, spec.seed, spec.tag(K_EXP_DOWN, e), 0, s.dim * s.nsb_down, st))
+
+
 class DeviceLayer:
     """One synthetic layer resident on the GPU: router, bias, expert arena and
-    shared expert, plus the binding structs that point at them."""
+    shared expert (bf16, or K-quant blocks when spec.shared_quant), plus the
+    binding structs that point at them."""
 
     def __init__(self, spec: LayerSpec, device="cuda", arena=None):
         import torch
-        from routing_quant_expert_amd import Experts, Layer, cfg_from_shape
+        from routing_quant_expert_amd import MOE_SHARED_KQUANT, Experts, Layer, cfg_from_shape
         s = spec.shape
         self.spec = spec
         self.cfg = cfg_from_shape(s)
@@ -76,13 +88,21 @@ class DeviceLayer:
         self.arena = arena if arena is not None else torch.empty(s.n_routed * s.expert_stride, dtype=torch.uint8,
                                                                   device=device)
         fill_arena(spec, self.arena)
+        self.experts = Experts(self.arena.data_ptr(), s.expert_stride, s.gate_off, s.up_off, s.down_off)
+        if spec.shared_quant:
+            self.sh_w1 = self.sh_w3 = self.sh_w2 = None
+            self.shared_q = torch.empty(s.expert_stride, dtype=torch.uint8, device=device)
+            fill_expert(spec, self.shared_q, s.n_routed)
+            sq = Experts(self.shared_q.data_ptr(), 0, s.gate_off, s.up_off, s.down_off)
+            self.layer = Layer(self.gate_w.data_ptr(), self.bias.data_ptr(), self.experts, None, None, None,
+                               MOE_SHARED_KQUANT, sq)
+            return
         self.sh_w1 = torch.empty((s.inter, s.dim), dtype=torch.uint16, device=device)
         self.sh_w3 = torch.empty((s.inter, s.dim), dtype=torch.uint16, device=device)
         self.sh_w2 = torch.empty((s.dim, s.inter), dtype=torch.uint16, device=device)
         normal_bf16_into(self.sh_w1, spec.seed, spec.tag(K_SH_W1), SIGMA_W)
         normal_bf16_into(self.sh_w3, spec.seed, spec.tag(K_SH_W3), SIGMA_W)
         normal_bf16_into(self.sh_w2, spec.seed, spec.tag(K_SH_W2), SIGMA_W)
-        self.experts = Experts(self.arena.data_ptr(), s.expert_stride, s.gate_off, s.up_off, s.down_off)
         self.layer = Layer(self.gate_w.data_ptr(), self.bias.data_ptr(), self.experts, self.sh_w1.data_ptr(),
                            self.sh_w3.data_ptr(), self.sh_w2.data_ptr())
 

@@ -48,7 +48,8 @@ def plan_tables(ws, layout, m, topk):
         tab[name] = words[base:base + P]
         base += P
     tab["pair_w"] = tab["pair_w"].view(np.float32)
-    tab["tok_pairs"] = words[base:base + m * topk].reshape(m, topk)
+    # a token's plan entries: its picks in ascending id, then its K-quant shared expert's pair (-1 = none)
+    tab["tok_pairs"] = words[base:base + m * (topk + 1)].reshape(m, topk + 1)
     tab["n_u"], tab["n_pairs"] = n_u, n_pairs
     return tab
 
@@ -96,13 +97,14 @@ def check_combine_bits(ws, layout: dict, tab: dict, m: int, topk: int, out_f32: 
     must equal the oracle's combine applied to the device's own per-pair
     expert outputs y (in plan order, ascending expert id) with the plan
     weights, and then the device's own shared-expert output sd added after
-    the routed sum [moe_v41.rs, fn shared_side]. The inputs are the device's,
+    the routed sum [moe_v41.rs, fn shared_side] (a K-quant shared expert is
+    the token's last plan entry, weight 1). The inputs are the device's,
     so no rounding of the GEMVs can blur a wrong summation order."""
     P, dim = layout["max_pairs"], out_f32.shape[1]
     y = ws_array(ws, layout, "y", np.float32, P * dim).reshape(P, dim)
     sd = ws_array(ws, layout, "sd", np.float32, m * dim).reshape(m, dim) if with_shared else None
     for t in (range(m) if tokens is None else tokens):
-        pairs = [int(p) for p in tab["tok_pairs"][t][:topk] if p >= 0]
+        pairs = [int(p) for p in tab["tok_pairs"][t] if p >= 0]   # a K-quant shared expert last, weight 1
         ys = np.stack([y[p] for p in pairs])
         w = np.array([tab["pair_w"][p] for p in pairs], np.float32)
         want, _ = oracle.combine(ys, w, None if sd is None else sd[t])

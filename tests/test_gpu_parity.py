@@ -193,15 +193,24 @@ def _check_layer(dl, x_np, m, out_f32, out_bf16, hdr, ws, with_shared=True):
     hd = ws_array(ws, L, "hd", np.uint16, P * inter // 32).reshape(P, -1)
     hs = ws_array(ws, L, "hs", np.int32, P * inter // 16).reshape(P, -1)
     y = ws_array(ws, L, "y", np.float32, P * dim).reshape(P, dim)
-    assert tab["n_pairs"] == m * shape.topk
+    shq = with_shared and spec.shared_quant   # the K-quant shared expert: plan expert n_routed, weight 1, last
+    assert tab["n_pairs"] == m * (shape.topk + (1 if shq else 0))
+    if not shq:
+        assert np.all(tab["tok_pairs"][:, shape.topk] == -1)
     accepted = 0   # over all pairs, for the log line and the whole-output comparison
     for p in range(tab["n_pairs"]):
         t, e = int(tab["pair_tok"][p]), int(tab["pair_expert"][p])
-        ids = list(ref["tok"][t]["ids"])
-        k = ids.index(e)
-        ex = ref["tok"][t]["experts"][k]
-        assert tab["pair_w"][p] == ref["tok"][t]["w_plan"][k]
-        assert tab["tok_pairs"][t][k] == p
+        if e == shape.n_routed:
+            assert shq and tab["pair_w"][p] == 1.0 and tab["tok_pairs"][t][shape.topk] == p
+            ex = ref["shared"][t]
+            down = synth.shared_q_blocks(spec, "down")
+        else:
+            ids = list(ref["tok"][t]["ids"])
+            k = ids.index(e)
+            ex = ref["tok"][t]["experts"][k]
+            assert tab["pair_w"][p] == ref["tok"][t]["w_plan"][k]
+            assert tab["tok_pairs"][t][k] == p
+            down = synth.expert_blocks(spec, e, "down")
         # this pair's g/u: a neighbour accepted at a flagged near-midpoint makes its own h differ legitimately,
         # so only this pair's h checks are skipped then
         gu_acc = f32_accept(g[p], ex["g"], ex["near_g"], f"g pair {p}")
@@ -216,7 +225,7 @@ def _check_layer(dl, x_np, m, out_f32, out_bf16, hdr, ws, with_shared=True):
             assert np.array_equal(h[p].view(np.uint32), hh.view(np.uint32)), f"h pair {p} (own g/u)"
             q, d = oracle.q8_1(hh)
             assert np.array_equal(hq[p], q) and np.array_equal(hd[p], d), f"h q8_1 pair {p} (own g/u)"
-            yy, near = oracle.q3k_gemv(synth.expert_blocks(spec, e, "down"), dim, inter, q, d)
+            yy, near = oracle.q3k_gemv(down, dim, inter, q, d)
             accepted += f32_accept(y[p], yy, near, f"y pair {p} (own h)")
         accepted += gu_acc
     if accepted:
@@ -224,9 +233,9 @@ def _check_layer(dl, x_np, m, out_f32, out_bf16, hdr, ws, with_shared=True):
     want = ref["out_f32"] if with_shared else ref["y_routed"]
     err = np.abs(out_f32 - want)
     assert rel_l2(out_f32, want) <= 1e-3 and err.max() <= 1e-2, (rel_l2(out_f32, want), err.max())
-    if accepted == 0 and not with_shared:
+    if accepted == 0 and (shq or not with_shared):   # no f32 GEMV of unstated order: the output is exact
         assert np.array_equal(out_f32.view(np.uint32), want.view(np.uint32))
-    check_combine_bits(ws, L, tab, m, shape.topk, out_f32, with_shared)
+    check_combine_bits(ws, L, tab, m, shape.topk, out_f32, with_shared and not shq)
     if out_bf16 is not None:
         assert np.array_equal(out_bf16, oracle.f32_to_bf16(out_f32))
     return ref

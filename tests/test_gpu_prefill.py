@@ -74,12 +74,20 @@ def _check_tokens(spec, x_np, toks, v, out_f32, want_key, hdr_dev):
     tab = v["tab"]
     toks = list(toks)
     ref = olayer.layer_forward(spec, x_np[toks], with_shared=(want_key == "out_f32"))
+    shq = spec.shared_quant and want_key == "out_f32"
+    topk = spec.shape.topk
     for i, t in enumerate(toks):
         assert np.array_equal(hdr_dev[t], ref["header"][i]), t
-        for k, e in enumerate(ref["tok"][i]["ids"]):
+        # the token's plan entries: its picks, then (K-quant shared expert) expert n_routed with weight 1
+        entries = [(int(e), ref["tok"][i]["experts"][k], k) for k, e in enumerate(ref["tok"][i]["ids"])]
+        if shq:
+            entries.append((spec.shape.n_routed, ref["shared"][i], topk))
+            assert tab["pair_w"][int(tab["tok_pairs"][t][topk])] == 1.0
+        else:
+            assert tab["tok_pairs"][t][topk] == -1
+        for e, ex, k in entries:
             p = int(tab["tok_pairs"][t][k])
             assert tab["pair_expert"][p] == e and tab["pair_tok"][p] == t
-            ex = ref["tok"][i]["experts"][k]
             acc = f32_accept(v["g"][p], ex["g"], ex["near_g"], f"g tok {t} e {e}")
             acc += f32_accept(v["u"][p], ex["u"], ex["near_u"], f"u tok {t} e {e}")
             if acc == 0:
@@ -93,7 +101,9 @@ def _check_tokens(spec, x_np, toks, v, out_f32, want_key, hdr_dev):
                 assert np.array_equal(v["h"][p].view(np.uint32), hh.view(np.uint32)), (t, e)
                 q, d = oracle.q8_1(hh)
                 assert np.array_equal(v["hq"][p], q) and np.array_equal(v["hd"][p], d), (t, e)
-                yy, near = oracle.q3k_gemv(synth.expert_blocks(spec, int(e), "down"), sh.dim, sh.inter, q, d)
+                down = (synth.shared_q_blocks(spec, "down") if e == sh.n_routed else
+                        synth.expert_blocks(spec, int(e), "down"))
+                yy, near = oracle.q3k_gemv(down, sh.dim, sh.inter, q, d)
                 acc += f32_accept(v["y"][p], yy, near, f"y tok {t} e {e} (own h)")
             accepted += acc
         want = ref[want_key][i]

@@ -37,11 +37,11 @@ def test_workspace_queries():
     offs = [L[k] for k in ("ctl", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u", "h", "hq", "hd", "hs",
                            "y", "sg", "su", "sh", "sd", "yr", "status", "grp", "xd64", "hd64")]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs) and L["total"] == n8
-    assert L["max_pairs"] == 48
+    assert L["max_pairs"] == 56   # 8 tokens x (6 picks + a K-quant shared expert)
     assert R.header_words(c) == 19
     # the control words sit at the start for every m, so a workspace initialised for max_m serves smaller calls
     assert all(R.workspace_layout(c, m)["ctl"] == 0 for m in (1, 3, 8, 512))
-    assert R.workspace_bytes(c, 512) > n8 and R.workspace_layout(c, 512)["max_pairs"] == 3072
+    assert R.workspace_bytes(c, 512) > n8 and R.workspace_layout(c, 512)["max_pairs"] == 3584
 
 
 @pytest.mark.parametrize("field,value", [("dim", 300), ("dim", 256 * 3), ("dim", 256 * 32), ("inter", 0),
@@ -146,13 +146,14 @@ def test_empty_batch_is_rejected_by_every_entry_point():
 
 def test_token_count_bound_is_enforced_before_any_launch():
     """The kernels index per-pair activations with 32-bit offsets and put
-    tokens on a grid dimension: m above 65535, or with m * topk *
-    max(dim, inter) >= 2^31, is MOE_EUNSUPPORTED for every entry point, and
+    tokens on a grid dimension: m above 65535, or with m * (topk + 1) *
+    max(dim, inter) >= 2^31 (topk + 1: a K-quant shared expert is one more
+    entry per token), is MOE_EUNSUPPORTED for every entry point, and
     the workspace size query returns 0 there."""
     ex = R.Experts(1 << 20, 0, 0, 0, 0)
     layer = R.Layer(8192, 16384, ex, 1 << 21, 1 << 22, 1 << 23)
     ws = _FakePtr(1 << 24, n=1 << 40)
-    for shape, m in ((synth.SHAPE_TINY, 65536), (synth.SHAPE_DS41, 87382)):
+    for shape, m in ((synth.SHAPE_TINY, 65536), (synth.SHAPE_DS41, 74899)):
         c = R.cfg_from_shape(shape)
         assert R.workspace_bytes(c, m) == 0
         x = _FakePtr(4096, shape=(m, shape.dim))

@@ -253,3 +253,80 @@ def test_stack_residual_against_exact_sums():
         assert np.array_equal(r["headers"][l], hdr)
     # the layers differ (their own seeds): the step is not one layer repeated
     assert not np.array_equal(r["headers"][0], r["headers"][1])
+
+
+# ------------------------------------------------ K-quant shared expert
+# The shared expert's matrices as K-quant blocks run exactly as one more
+# routed expert of the token, added after the routed sum [moe_v41.rs, struct
+# MoeV41LayerWeights: the shared matrices as bf16 or the GGUF's Q2_K (w1, w3)
+# / Q3_K (w2) blocks on the routed experts' kernels; fn shared_side].
+def _kq_spec(seed):
+    return synth.LayerSpec(synth.SHAPE_TINY, seed=seed, shared_quant=True)
+
+
+def _zero_scales(g, u, d):
+    g, u, d = g.copy(), u.copy(), d.copy()
+    for arr, nbytes, offs in ((g, 84, (80, 81, 82, 83)), (u, 84, (80, 81, 82, 83)), (d, 110, (108, 109))):
+        v = arr.reshape(-1, nbytes)
+        for o in offs:
+            v[:, o] = 0
+    return g, u, d
+
+
+def test_kquant_shared_with_zero_scales_adds_nothing():
+    """All-zero shared scales: its output is +0 everywhere, so the layer
+    output is the routed sum bit for bit (acc + 0 = acc)."""
+    spec = _kq_spec(31)
+    zq = _zero_scales(*(synth.shared_q_blocks(spec, w) for w in ("gate", "up", "down")))
+    x = synth.tokens(spec, 0, 3)
+    out = layer.layer_forward(spec, x, shared_q=zq)
+    assert np.array_equal(out["out_f32"].view(np.uint32), out["y_routed"].view(np.uint32))
+    assert all(np.all(sh["y"] == 0.0) for sh in out["shared"])
+
+
+def test_kquant_shared_equal_to_a_picked_expert_gives_its_output():
+    """Shared blocks equal to the blocks of an expert the token picked: the
+    shared output equals that expert's output bit for bit (same q8_1 of x,
+    same GEMVs, same SwiGLU and q8_1 of h)."""
+    spec = _kq_spec(32)
+    x = synth.tokens(spec, 5, 1)
+    e = int(layer.route(spec, x)["header"][0, 1])
+    same = tuple(synth.expert_blocks(spec, e, w) for w in ("gate", "up", "down"))
+    out = layer.layer_forward(spec, x, shared_q=same)
+    k = list(out["tok"][0]["ids"]).index(e)
+    ye = out["tok"][0]["experts"][k]["y"]
+    assert np.array_equal(out["shared"][0]["y"].view(np.uint32), ye.view(np.uint32))
+
+
+def test_kquant_shared_alone_is_the_dense_quantised_mlp():
+    """Routed scales all zero: the layer output is the shared expert alone,
+    checked against a float64 textbook MLP on the dequantised matrices and
+    the dequantised q8_1 activations (W2 . deq(q8_1(silu(min(g,L)) clamp(u))),
+    g, u = W1 . deq(q8_1(x)), W3 . deq(q8_1(x)))."""
+    spec = _kq_spec(33)
+    s = spec.shape
+
+    def zero_experts(e):
+        return _zero_scales(*(synth.expert_blocks(spec, e, w) for w in ("gate", "up", "down")))
+
+    x = synth.tokens(spec, 0, 2)
+    out = layer.layer_forward(spec, x, experts=zero_experts)
+    assert np.all(out["y_routed"] == 0.0)
+    W1 = oracle.q2k_dequant(synth.shared_q_blocks(spec, "gate")).reshape(s.inter, s.dim)
+    W3 = oracle.q2k_dequant(synth.shared_q_blocks(spec, "up")).reshape(s.inter, s.dim)
+    W2 = oracle.q3k_dequant(synth.shared_q_blocks(spec, "down")).reshape(s.dim, s.inter)
+    L = 7.0
+    for t in range(2):
+        q, d = oracle.q8_1(oracle.bf16_to_f32(x[t]))
+        a = q.astype(np.float64) * np.repeat(oracle.fp16_to_f64(d), 32)
+        g, u = (W1 @ a).astype(np.float32), (W3 @ a).astype(np.float32)
+        gz = np.minimum(g.astype(np.float64), L)
+        h = (gz / (1 + np.exp(-gz)) * np.clip(u.astype(np.float64), -L, L)).astype(np.float32)
+        hq, hd = oracle.q8_1(h)
+        ha = hq.astype(np.float64) * np.repeat(oracle.fp16_to_f64(hd), 32)
+        ref = W2 @ ha
+        got = out["out_f32"][t].astype(np.float64)
+        # (on these inputs the textbook h quantises to the same codes as the f32 chain's: only rounding differs)
+        assert np.array_equal(hq, out["shared"][t]["hq"])
+        assert np.sqrt(((got - ref) ** 2).sum() / (ref ** 2).sum()) < 1e-6
+        assert np.abs(got - ref).max() < 1e-4
