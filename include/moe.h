@@ -60,7 +60,7 @@ extern "C" {
 #define MOE_EHIP (-4)          /* a HIP launch or attribute call failed        */
 
 /* Header status bits (word 0 of a token's header). */
-#define MOE_STATUS_MISS 1        /* an expert was not resident (never set: all experts resident) */
+#define MOE_STATUS_MISS 1        /* a pick was not resident in an expert cache (moe_cache_forward) */
 #define MOE_STATUS_NAN_KEY 2     /* a ranking key score+bias was NaN (the pages' "finite scores") */
 #define MOE_STATUS_BAD_PICK 4    /* moe_experts_decode: a pick outside [0,n_routed) or repeated    */
 
@@ -268,6 +268,69 @@ int moe_layer_forward_noalloc(const moe_cfg* cfg, const moe_layer* layer, const 
  *   headers  int32 [n_layers][m][moe_header_words] per-layer headers, may be NULL */
 int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_layers, uint16_t* xs, int32_t m,
                       float* out_f32, int32_t* headers, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Expert streaming beyond HBM ----------------------------------------
+ * An expert cache holds the routed experts of n_layers layers in host memory
+ * and keeps n_slots of them in a device slot pool, with a device slot table
+ * [n_layers][n_routed] (the slot of each expert, -1 = not resident)
+ * [device_route.rs, module doc, fn route_device_m1, fn slot_table_update;
+ * moe_v41.rs, module doc: the LRU gathers the picked experts' raw blocks into
+ * device slots, misses read from storage]. For each layer the routing runs
+ * against the slot table, its header is read back once, the least recently
+ * used slots take the missing picks (copied from host memory), the changed
+ * table rows are uploaded, and the experts run from the slots; every value
+ * is the same as with the experts resident. The cache owns device memory
+ * (the pool, the table, a predicted-header buffer), pinned host buffers and a
+ * copy stream, from moe_cache_create to moe_cache_destroy; its calls are not
+ * thread-safe and must use the device that was current at its creation. */
+typedef struct moe_cache moe_cache;
+
+typedef struct moe_cache_stats {
+  int64_t hits;           /* picks found resident                                     */
+  int64_t misses;         /* picks copied in on demand                                */
+  int64_t prefetched;     /* experts copied in ahead of need                          */
+  int64_t prefetch_used;  /* picks found resident because a prefetch brought them in   */
+  int64_t bytes_copied;   /* host-to-device expert bytes                              */
+  int64_t reads_back;     /* header read-backs (one per layer call)                   */
+} moe_cache_stats;
+
+/* host_experts: n_layers host pointers, layer l's expert e at
+ * host_experts[l] + e * stride with the moe_experts offsets (pinned memory
+ * makes the copies asynchronous); n_slots device slots of stride bytes;
+ * max_m: the largest m of a later moe_cache_forward. */
+int moe_cache_create(const moe_cfg* cfg, int32_t n_layers, const void* const* host_experts, uint64_t stride,
+                     uint64_t gate_off, uint64_t up_off, uint64_t down_off, int32_t n_slots, int32_t max_m,
+                     moe_cache** out);
+int moe_cache_destroy(moe_cache* cache);
+
+/* Layers first_layer .. first_layer + n_layers - 1 of the cache, one step for
+ * m tokens, as moe_stack_forward (xs [n_layers+1][m][dim], out_f32 and
+ * headers per layer, may be NULL; layers[i] gives layer first_layer+i's
+ * router, bias and shared expert; its `experts` field is not used). Each
+ * layer's header has MOE_STATUS_MISS set when a pick was not resident at
+ * routing time, and its plan words hold the picks' slots then (-1 = absent).
+ * prefetch_k in 0..topk: also run the next layer's router on this layer's
+ * input and copy the first prefetch_k predicted picks of each token into
+ * slots while this layer computes [moe_v41.rs, fn prefetch_k; struct MoeV41:
+ * pred_logits]. Blocks the calling thread once per layer (the header's
+ * read-back). MOE_EUNSUPPORTED when a layer's distinct picks need more slots
+ * than the cache has. */
+int moe_cache_forward(moe_cache* cache, const moe_cfg* cfg, const moe_layer* layers, int32_t first_layer,
+                      int32_t n_layers, uint16_t* xs, int32_t m, float* out_f32, int32_t* headers, int32_t prefetch_k,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Copies the listed experts of a layer into slots ahead of need (on `stream`,
+ * after the work enqueued there), evicting least recently used slots. */
+int moe_cache_prefetch(moe_cache* cache, int32_t layer, const int32_t* experts, int32_t n, void* stream);
+int moe_cache_get_stats(const moe_cache* cache, moe_cache_stats* out);
+/* The cache's slot of each expert of a layer (host int32 [n_routed], -1 = not resident). */
+int moe_cache_resident(const moe_cache* cache, int32_t layer, int32_t* slots);
+
+/* The cache's slot assignment alone, on the host (checking only): keys in
+ * 0..n_keys-1 requested in n_batches batches of batch_len keys; each
+ * request's slot (-1: no slot free of the batch) and whether it missed. */
+int moe_lru_simulate(int32_t n_slots, int64_t n_keys, const int64_t* keys, const int32_t* batch_len,
+                     int32_t n_batches, int32_t* slots_out, int32_t* miss_out);
 
 /* The score chain of A3 alone on device data: out[i] = sqrt(softplus(
  * logits[i] / temp)) with correctly rounded exp, log1p, division and sqrt

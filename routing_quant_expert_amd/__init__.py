@@ -6,14 +6,14 @@ in include/moe.h); this package only marshals arguments to it.
 """
 from .binding import (MOE_K_DOWN, MOE_K_DOWN2, MOE_K_GATEUP, MOE_K_GATEUP2, MOE_K_READ_PROBE, MOE_K_ROUTER, MOE_K_SHARED_DOWN, MOE_K_SHARED_GU,
                       MOE_SHARED_BF16, MOE_SHARED_KQUANT,
-                      MOE_STATUS_BAD_PICK, MOE_STATUS_MISS, MOE_STATUS_NAN_KEY, Cfg, Experts, Layer, MoeError,
+                      MOE_STATUS_BAD_PICK, MOE_STATUS_MISS, MOE_STATUS_NAN_KEY, Cfg, ExpertCache, Experts, Layer, MoeError,
                       cfg_from_shape, experts_decode, experts_prefill, header_words, layer_forward, layer_forward_noalloc, lib, read_probe,
-                      route_select, scores, scores_host, stack_forward, swiglu_host, time_next_launch,
+                      lru_simulate, route_select, scores, scores_host, stack_forward, swiglu_host, time_next_launch,
                       workspace_bytes, workspace_init, workspace_layout)
 
 __all__ = [
-    "Cfg", "Experts", "Layer", "MoeError", "cfg_from_shape", "experts_decode", "experts_prefill", "header_words",
-    "layer_forward", "layer_forward_noalloc", "lib", "read_probe", "route_select", "scores", "scores_host", "stack_forward", "swiglu_host",
+    "Cfg", "ExpertCache", "Experts", "Layer", "MoeError", "cfg_from_shape", "experts_decode", "experts_prefill", "header_words",
+    "layer_forward", "layer_forward_noalloc", "lib", "lru_simulate", "read_probe", "route_select", "scores", "scores_host", "stack_forward", "swiglu_host",
     "time_next_launch", "workspace_bytes", "workspace_init", "workspace_layout", "MOE_K_GATEUP", "MOE_K_DOWN",
     "MOE_K_ROUTER", "MOE_K_READ_PROBE", "MOE_K_SHARED_GU", "MOE_K_SHARED_DOWN", "MOE_K_GATEUP2", "MOE_K_DOWN2",
     "MOE_SHARED_BF16", "MOE_SHARED_KQUANT", "MOE_STATUS_MISS", "MOE_STATUS_NAN_KEY", "MOE_STATUS_BAD_PICK",

@@ -46,6 +46,11 @@ class Layer(ctypes.Structure):
 MOE_SHARED_BF16, MOE_SHARED_KQUANT = 0, 1
 
 
+class CacheStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("hits", "misses", "prefetched", "prefetch_used", "bytes_copied",
+                                               "reads_back")]
+
+
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("total", "xq", "xd", "xs", "logits", "scores", "plan", "g", "u",
                                                  "h", "hq", "hd", "hs", "y", "sg", "su", "sh", "sd", "yr",
@@ -86,6 +91,16 @@ def lib():
         L.moe_swiglu_host.argtypes = [_VP, _VP, ctypes.c_int64, ctypes.c_float, _VP]
         L.moe_time_next_launch.argtypes = [ctypes.c_int32, _VP, _VP]
         L.moe_read_probe.argtypes = [_VP, ctypes.c_uint64, _VP, ctypes.c_int32, _VP]
+        L.moe_cache_create.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32, ctypes.POINTER(_VP), ctypes.c_uint64,
+                                       ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.POINTER(_VP)]
+        L.moe_cache_destroy.argtypes = [_VP]
+        L.moe_cache_forward.argtypes = [_VP, ctypes.POINTER(Cfg), ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_int32,
+                                        _VP, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
+        L.moe_cache_prefetch.argtypes = [_VP, ctypes.c_int32, _VP, ctypes.c_int32, _VP]
+        L.moe_cache_get_stats.argtypes = [_VP, ctypes.POINTER(CacheStats)]
+        L.moe_cache_resident.argtypes = [_VP, ctypes.c_int32, _VP]
+        L.moe_lru_simulate.argtypes = [ctypes.c_int32, ctypes.c_int64, _VP, _VP, ctypes.c_int32, _VP, _VP]
         L.moe_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -201,3 +216,63 @@ def time_next_launch(which: int, ev_begin, ev_end):
 def read_probe(buf, nbytes: int, sink, blocks: int, stream=None):
     """Stream `nbytes` of the device tensor `buf` through the library's read-only probe kernel."""
     _check(lib().moe_read_probe(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)))
+
+
+class ExpertCache:
+    """An expert cache (moe_cache_*): n_slots device slots over the host-resident
+    experts of len(host_arenas) layers (host tensors or addresses)."""
+
+    def __init__(self, cfg: Cfg, host_arenas, stride: int, gate_off: int, up_off: int, down_off: int, n_slots: int,
+                 max_m: int):
+        ptrs = [a if isinstance(a, int) else a.data_ptr() for a in host_arenas]
+        arr = (_VP * len(ptrs))(*ptrs)
+        h = _VP()
+        _check(lib().moe_cache_create(ctypes.byref(cfg), len(ptrs), arr, stride, gate_off, up_off, down_off, n_slots,
+                                      max_m, ctypes.byref(h)))
+        self.h, self.cfg = h, cfg
+
+    def forward(self, layers, xs, ws, first_layer: int = 0, out_f32=None, headers=None, prefetch_k: int = 0,
+                stream=None):
+        """xs: bf16 [n_layers+1, m, dim] (xs[0] the input); layers: the cache's layers first_layer.. (Layer)."""
+        n = len(layers)
+        arr = (Layer * n)(*layers)
+        _check(lib().moe_cache_forward(self.h, ctypes.byref(self.cfg), arr, first_layer, n, _ptr(xs), xs.shape[1],
+                                       _ptr(out_f32), _ptr(headers), prefetch_k, _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+    def prefetch(self, layer: int, experts, stream=None):
+        a = np.ascontiguousarray(experts, np.int32)
+        _check(lib().moe_cache_prefetch(self.h, layer, a.ctypes.data, a.size, _stream(stream)))
+
+    def stats(self) -> dict:
+        st = CacheStats()
+        _check(lib().moe_cache_get_stats(self.h, ctypes.byref(st)))
+        return {n: getattr(st, n) for n, _ in CacheStats._fields_}
+
+    def resident(self, layer: int) -> np.ndarray:
+        out = np.empty(self.cfg.n_routed, np.int32)
+        _check(lib().moe_cache_resident(self.h, layer, out.ctypes.data))
+        return out
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lru_simulate(n_slots: int, n_keys: int, batches):
+    """The cache's slot assignment on the host: each batch a list of keys; returns (slots, misses) per request."""
+    keys = np.ascontiguousarray(np.concatenate([np.asarray(b, np.int64) for b in batches]) if batches else
+                                np.zeros(0, np.int64))
+    lens = np.ascontiguousarray([len(b) for b in batches], np.int32)
+    slots = np.empty(keys.size, np.int32)
+    miss = np.empty(keys.size, np.int32)
+    _check(lib().moe_lru_simulate(n_slots, n_keys, keys.ctypes.data, lens.ctypes.data, len(batches),
+                                  slots.ctypes.data, miss.ctypes.data))
+    return slots, miss

@@ -47,12 +47,16 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
-int fail(int code, const char* fmt, const char* a = "", long long b = 0) {
+}  // namespace
+
+int fail(int code, const char* fmt, const char* a, long long b) {
   char buf[512];
   snprintf(buf, sizeof buf, fmt, a, b);
   g_err = buf;
   return code;
 }
+
+namespace {
 
 bool pow2_upto16(int v) { return v >= 1 && v <= 16 && (v & (v - 1)) == 0; }
 
@@ -102,12 +106,14 @@ hipError_t fork_join(hipEvent_t after, hipStream_t from, hipStream_t to) {
   return hipStreamWaitEvent(to, after, 0);
 }
 
+}  // namespace
+
 // The single-token kernels: up to 6 picks (a wave each) and down rows of at
 // most 8 Q3_K super-blocks (each pick's 16-row tile is staged whole in LDS);
 // other shapes take the union path, which is correct for every m <= 8.
 // With a K-quant shared expert (shq = 1) its blocks take one more pick's wave
 // in place of the two bf16 shared-expert waves.
-bool single_token_fits(const moe_cfg& c, int shq = 0) {
+bool single_token_fits(const moe_cfg& c, int shq) {
   return (shq ? c.topk + 1 <= kMaxTopk : c.topk <= kMaxTopkM1) && c.inter / 256 <= 8;
 }
 
@@ -168,9 +174,7 @@ int check_experts(const moe_experts* ex) {
   return MOE_OK;
 }
 
-}  // namespace
-
-XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q) {
+XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q, const int32_t* slot_of) {
   XArena a;
   a.base = static_cast<const uint8_t*>(ex.base);
   a.stride = ex.stride;
@@ -182,6 +186,7 @@ XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q
   a.sup_off = shared_q ? shared_q->up_off : 0;
   a.sdown_off = shared_q ? shared_q->down_off : 0;
   a.n_routed = n_routed;
+  a.slot_of = slot_of;
   return a;
 }
 
@@ -262,7 +267,7 @@ bool take_timed(int which, hipEvent_t* begin, hipEvent_t* end) {
   return true;
 }
 
-int check_layer(const moe_layer* layer) {
+int check_layer(const moe_layer* layer, bool need_experts) {
   if (!layer || !layer->gate_w || !layer->bias) return fail(MOE_EINVAL, "layer weights must be non-NULL%s%lld");
   if (layer->shared_kind == MOE_SHARED_BF16) {
     if (!layer->sh_w1 || !layer->sh_w2 || !layer->sh_w3)
@@ -275,7 +280,7 @@ int check_layer(const moe_layer* layer) {
     return fail(MOE_EINVAL, "unknown shared_kind%s %lld", "", layer->shared_kind);
   }
   if (!a16(layer->gate_w)) return fail(MOE_EINVAL, "gate_w must be 16-byte aligned%s%lld");
-  return check_experts(&layer->experts);
+  return need_experts ? check_experts(&layer->experts) : MOE_OK;
 }
 
 bool shared_bf16(const moe_layer& layer) { return layer.shared_kind == MOE_SHARED_BF16; }
@@ -326,6 +331,63 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
   if ((e = launch_front(x, m, layer.gate_w, &sel, bf16 ? layer.sh_w1 : nullptr, bf16 ? layer.sh_w3 : nullptr, c, w,
                         nullptr, s)) != hipSuccess)
     return hip_fail(e, "front");
+  if ((e = launch_gateup(ar, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup");
+  if ((e = launch_down(ar, m, c, w, bf16 ? layer.sh_w2 : nullptr, s)) != hipSuccess) return hip_fail(e, "down");
+  if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");
+  return MOE_OK;
+}
+
+// Routing of m tokens on `s`: q8_1 of x, the router and its scores, the top-k
+// and the headers (slot_of: an expert cache's slot-table row, see launch_select).
+hipError_t route_launches(const moe_cfg& c, const uint16_t* x, int m, const uint16_t* gate_w, const float* bias,
+                          int32_t* header, const Ws& w, const int32_t* slot_of, hipStream_t s) {
+  hipError_t e = m > kMaxDecodeTokens ? launch_router_pf(x, m, gate_w, c, w, nullptr, s)
+                                      : launch_front(x, m, gate_w, nullptr, nullptr, nullptr, c, w, nullptr, s);
+  if (e != hipSuccess) return e;
+  return launch_select(bias, m, c, w, header, s, slot_of);
+}
+
+// The layer after its routing, from the picks in `header` (device): the
+// routed experts out of arena `ar`, the shared expert and the combine, each
+// token's values exactly as layer_launches computes them (the same kernels,
+// fed the header instead of selecting).
+int layer_launches_hdr(const moe_cfg& c, const moe_layer& layer, const XArena& ar, const uint16_t* x, int m,
+                       const int32_t* header, const LayerOut& o, const Ws& w, int32_t* grp, hipStream_t s) {
+  hipError_t e;
+  const bool bf16 = shared_bf16(layer);
+  const int shq = ar.has_shared();
+  if (m > kMaxDecodeTokens) {
+    std::unique_lock<std::mutex> hold;
+    const SideStream* ss = side_stream(hold);
+    if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
+    const hipStream_t big = c.inter / 256 > 1 ? ss->s : s;
+    const bool side_used = bf16 || big != s;
+    if (bf16) {
+      if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
+      if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
+    }
+    if ((e = launch_router_pf(x, m, nullptr, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
+    if ((e = launch_group(header, m, c, w, grp, shq, s)) != hipSuccess) return hip_fail(e, "group");
+    if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
+    if ((e = launch_gateup_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
+    if ((e = launch_gateup_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
+    if ((e = launch_down_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
+    if (side_used && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
+    if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");
+    return MOE_OK;
+  }
+  if (m == 1 && single_token_fits(c, shq)) {
+    if ((e = launch_quant_x(x, 1, c, w, s)) != hipSuccess) return hip_fail(e, "quant_x");
+    if ((e = launch_gateup_m1(ar, nullptr, header, x, bf16 ? &layer : nullptr, c, w, s)) != hipSuccess)
+      return hip_fail(e, "gateup_m1");
+    if ((e = launch_down_m1(ar, c, w, bf16 ? layer.sh_w2 : nullptr, o, s)) != hipSuccess) return hip_fail(e, "down_m1");
+    return MOE_OK;
+  }
+  if ((e = launch_front(x, m, nullptr, nullptr, bf16 ? layer.sh_w1 : nullptr, bf16 ? layer.sh_w3 : nullptr, c, w,
+                        nullptr, s)) != hipSuccess)
+    return hip_fail(e, "front");
+  if ((e = launch_plan(header, m, c, w, s, shq)) != hipSuccess) return hip_fail(e, "plan");
   if ((e = launch_gateup(ar, m, c, w, s)) != hipSuccess) return hip_fail(e, "gateup");
   if ((e = launch_down(ar, m, c, w, bf16 ? layer.sh_w2 : nullptr, s)) != hipSuccess) return hip_fail(e, "down");
   if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");

@@ -475,7 +475,7 @@ hipError_t launch_gateup_m1(const XArena& ex, const FrontSelect* sel, const int3
   a.mode = sel ? 0 : 1;
   a.slots = c.topk + ex.has_shared();
   const int routed_blocks = a.slots * (c.inter / 32);
-  a.shared_units = (sel && layer) ? c.inter : 0;
+  a.shared_units = layer ? c.inter : 0;   // (with either plan source)
   const int rest = a.shared_units - kUnitsRouted * routed_blocks;
   a.shared_blocks = rest > 0 ? (rest + kUnitsShared - 1) / kUnitsShared : 0;
   a.ex = ex;

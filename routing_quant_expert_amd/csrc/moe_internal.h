@@ -56,18 +56,26 @@ struct XArena {
   const uint8_t* sbase;   // nullptr: the layer has no quantised shared expert
   uint64_t sgate_off, sup_off, sdown_off;
   int n_routed;
+  // With an expert cache: the layer's row of the device slot table; routed
+  // expert e's blocks then sit in slot slot_of[e] of the cache's pool (base,
+  // stride). An absent expert (-1) reads slot 0, as the pages' selection
+  // points it [device_route.rs, module doc]; the cache makes every pick
+  // resident before the expert kernels run. nullptr: expert e is slot e.
+  const int32_t* slot_of;
   __host__ __device__ bool shared(int e) const { return e >= n_routed; }
-  __host__ __device__ const uint8_t* blocks(int e) const { return shared(e) ? sbase : base + (uint64_t)e * stride; }
+  __device__ int slot(int e) const { return slot_of ? max(slot_of[e], 0) : e; }
+  __device__ const uint8_t* blocks(int e) const { return shared(e) ? sbase : base + (uint64_t)slot(e) * stride; }
   __host__ __device__ uint64_t goff(int e) const { return shared(e) ? sgate_off : gate_off; }
   __host__ __device__ uint64_t uoff(int e) const { return shared(e) ? sup_off : up_off; }
   __host__ __device__ uint64_t doff(int e) const { return shared(e) ? sdown_off : down_off; }
-  __host__ __device__ const uint8_t* gate(int e) const { return blocks(e) + goff(e); }
-  __host__ __device__ const uint8_t* up(int e) const { return blocks(e) + uoff(e); }
-  __host__ __device__ const uint8_t* down(int e) const { return blocks(e) + doff(e); }
+  __device__ const uint8_t* gate(int e) const { return blocks(e) + goff(e); }
+  __device__ const uint8_t* up(int e) const { return blocks(e) + uoff(e); }
+  __device__ const uint8_t* down(int e) const { return blocks(e) + doff(e); }
   __host__ __device__ int has_shared() const { return sbase ? 1 : 0; }
 };
-// The routed arena alone (shared_q NULL), or with the layer's quantised shared expert.
-XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q);
+// The routed arena alone (shared_q NULL), or with the layer's quantised shared
+// expert; slot_of: a slot-table row (the arena is then a cache's slot pool).
+XArena arena_of(const moe_experts& ex, int n_routed, const moe_experts* shared_q, const int32_t* slot_of = nullptr);
 
 // Control words (workspace region `ctl`, 256 bytes, zero between calls).
 struct Ctl {
@@ -128,8 +136,12 @@ struct FrontSelect {
 hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const FrontSelect* sel, const uint16_t* w1,
                         const uint16_t* w3, const moe_cfg& c, const Ws& w, float* logits_out, hipStream_t s);
 hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
-hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s);
-hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
+// slot_of (optional): a slot-table row; the header's plan words then hold the
+// picks' slots (-1 = absent) and status bit MOE_STATUS_MISS flags an absent pick.
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s,
+                         const int32_t* slot_of = nullptr);
+// shq = 1: each token's plan also gets the layer's quantised shared expert.
+hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s, int shq = 0);
 hipError_t launch_gateup(const XArena& ex, int m, const moe_cfg& c, const Ws& w, hipStream_t s);
 // down: routed Q3_K rows, plus the shared expert's down rows when w2 is given.
 hipError_t launch_down(const XArena& ex, int m, const moe_cfg& c, const Ws& w, const uint16_t* w2,
@@ -145,6 +157,24 @@ hipError_t launch_gateup_m1(const XArena& ex, const FrontSelect* sel, const int3
                             const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s);
 hipError_t launch_down_m1(const XArena& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
                           hipStream_t s);
+// ---- argument checks and the error message (moe_api.hip) ----
+int fail(int code, const char* fmt, const char* a = "", long long b = 0);   // fmt takes a %s then a %lld
+int hip_fail(hipError_t e, const char* where);
+int check_cfg(const moe_cfg* c);
+int check_m(const moe_cfg& c, int64_t m);
+int check_ws(const moe_cfg& c, int m, void* ws, size_t ws_bytes, moe_ws_layout* L);
+int check_experts(const moe_experts* ex);
+int check_layer(const moe_layer* layer, bool need_experts = true);
+bool a16(const void* p);
+bool single_token_fits(const moe_cfg& c, int shq = 0);
+bool shared_bf16(const moe_layer& layer);
+// Routing of m tokens (q8_1 of x, router, scores, top-k, headers); slot_of as in launch_select.
+hipError_t route_launches(const moe_cfg& c, const uint16_t* x, int m, const uint16_t* gate_w, const float* bias,
+                          int32_t* header, const Ws& w, const int32_t* slot_of, hipStream_t s);
+// The layer after its routing, from the device headers: routed experts out of `ar`, shared expert, combine.
+int layer_launches_hdr(const moe_cfg& c, const moe_layer& layer, const XArena& ar, const uint16_t* x, int m,
+                       const int32_t* header, const LayerOut& o, const Ws& w, int32_t* grp, hipStream_t s);
+
 // Zero-fill of `bytes` bytes (a multiple of 16) with a kernel (no memset node).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

@@ -237,13 +237,16 @@ __global__ __launch_bounds__(1024) void k_group_count(const int32_t* __restrict_
     const int np = bv + v, nu = bf + f;
     e_first[n_routed] = np;
     e_count[n_routed] = n_ok;
-    if (n_ok > 0) {
-      plan.u_expert()[nu] = n_routed;
-      plan.u_first()[nu] = np;
-      plan.u_npairs()[nu] = n_ok;
+    // the shared group holds every kept token: its plan entries take kChunk tokens each, one MFMA pass,
+    // so that its workgroups spread over the device instead of looping over all the tokens
+    const int nsh = (n_ok + kChunk - 1) / kChunk;
+    for (int j = 0; j < nsh; ++j) {
+      plan.u_expert()[nu + j] = n_routed;
+      plan.u_first()[nu + j] = np + kChunk * j;
+      plan.u_npairs()[nu + j] = min(kChunk, n_ok - kChunk * j);
     }
     *plan.n_pairs() = np + n_ok;
-    *plan.n_u() = nu + (n_ok > 0 ? 1 : 0);
+    *plan.n_u() = nu + nsh;
   }
 }
 
@@ -946,8 +949,14 @@ hipError_t launch_group(const int32_t* header, int m, const moe_cfg& c, const Ws
   return hipGetLastError();
 }
 
+// Plan entries of a prefill plan: the distinct routed experts, then the
+// shared group's entries of kChunk tokens.
+int max_entries(const XArena& ex, int m, const moe_cfg& c) {
+  return min(c.n_routed, m * c.topk) + (ex.has_shared() ? (m + kChunk - 1) / kChunk : 0);
+}
+
 hipError_t launch_gateup_pf(const XArena& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
-  const int max_u = min(c.n_routed, m * c.topk) + ex.has_shared();
+  const int max_u = max_entries(ex, m, c);
   GateUpPfArgs a{ex, w.plan, w.xq, w.xd64, m, c.inter, c.swiglu_limit, w.g, w.u, w.h, w.hq, w.hd, w.hd64, w.hs};
   switch (c.dim / 256) {
     case 1: return launch_gateup_pf_t<1>(a, max_u, part, s);
@@ -960,7 +969,7 @@ hipError_t launch_gateup_pf(const XArena& ex, int m, const moe_cfg& c, const Ws&
 }
 
 hipError_t launch_down_pf(const XArena& ex, int m, const moe_cfg& c, const Ws& w, int part, hipStream_t s) {
-  const int max_u = min(c.n_routed, m * c.topk) + ex.has_shared();
+  const int max_u = max_entries(ex, m, c);
   DownPfArgs a{ex, w.plan, w.hq, w.hd, w.hd64, m * (c.topk + 1), c.dim, w.y};
   switch (c.inter / 256) {
     case 1: return launch_down_pf_t<1>(a, max_u, part, s);

@@ -25,10 +25,14 @@ using front::shared_gu_rows;
 // Selection, one wave per token (moe_select.h): writes the header
 // [device_route.rs, fn parse_header] and, for the plan, the picks/weights.
 // ---------------------------------------------------------------------------
+// slot_of (optional, an expert cache's slot-table row): the plan words hold
+// the picks' slots instead of their ids, -1 for an absent expert, and an
+// absent pick sets MOE_STATUS_MISS [device_route.rs, module doc: the header's
+// miss flag and plan slots].
 template <int KPER>
 __device__ void select_token(const float (&sc)[KPER], const float (&bs)[KPER], int n_routed, int topk, int norm,
                              float route_scale, int32_t* __restrict__ hd, int* picks_out, float* w_out,
-                             int32_t* __restrict__ status) {
+                             int32_t* __restrict__ status, const int32_t* __restrict__ slot_of = nullptr) {
   const int lane = threadIdx.x & 63;
   int picks[kMaxTopk];
   float wv = 0.0f;
@@ -42,18 +46,21 @@ __device__ void select_token(const float (&sc)[KPER], const float (&bs)[KPER], i
 #pragma unroll
   for (int r = 0; r < kMaxTopk; ++r)
     if (r < topk) rank += picks[r] < mypick ? 1 : 0;
+  const int slot = (slot_of && lane < topk) ? slot_of[mypick] : mypick;
+  const bool miss = __any(lane < topk && slot < 0);
   if (lane < topk) {
     hd[1 + lane] = mypick;
     hd[1 + topk + lane] = (int32_t)__builtin_bit_cast(uint32_t, wv);
-    hd[1 + 2 * topk + rank] = mypick;
+    hd[1 + 2 * topk + rank] = slot;
     if (picks_out) {
       picks_out[lane] = mypick;
       w_out[lane] = wv;
     }
   }
   if (lane == 0) {
-    hd[0] = nan_any ? MOE_STATUS_NAN_KEY : 0;
-    if (nan_any) atomicOr(status, MOE_STATUS_NAN_KEY);
+    const int st = (nan_any ? MOE_STATUS_NAN_KEY : 0) | (miss ? MOE_STATUS_MISS : 0);
+    hd[0] = st;
+    if (st) atomicOr(status, st);
   }
 }
 
@@ -238,19 +245,20 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
 template <int KPER>
 __global__ __launch_bounds__(64) void k_select(const float* __restrict__ scores, const float* __restrict__ bias,
                                                int n_routed, int topk, int norm, float route_scale,
-                                               int32_t* __restrict__ header, int32_t* __restrict__ status) {
+                                               int32_t* __restrict__ header, int32_t* __restrict__ status,
+                                               const int32_t* __restrict__ slot_of) {
   const int t = blockIdx.x;
   float sc[KPER], bs[KPER];
   select_load<KPER>(scores + (int64_t)t * n_routed, bias, n_routed, sc, bs);
   select_token<KPER>(sc, bs, n_routed, topk, norm, route_scale, header + (int64_t)t * (1 + 3 * topk), nullptr,
-                     nullptr, status);
+                     nullptr, status, slot_of);
 }
 
 // Plan tables from headers given by the caller (m <= 8): picks outside
 // [0, n_routed) or repeated within a token disable that token.
 template <int KPER>
 __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ header, int m, int topk, int n_routed,
-                                                   PlanView plan, int32_t* __restrict__ status) {
+                                                   PlanView plan, int32_t* __restrict__ status, int shq) {
   __shared__ int picks[64];
   __shared__ float wts[64];
   __shared__ int tok_ok[kMaxDecodeTokens];
@@ -275,7 +283,7 @@ __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ h
     if (!ok) atomicOr(status, MOE_STATUS_BAD_PICK);
   }
   __builtin_amdgcn_wave_barrier();
-  build_plan<KPER>(picks, wts, tok_ok, m, topk, plan, emap, 0, n_routed);
+  build_plan<KPER>(picks, wts, tok_ok, m, topk, plan, emap, shq, n_routed);
 }
 
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, int64_t n, float temp,
@@ -313,22 +321,24 @@ hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const 
   return hipGetLastError();
 }
 
-hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s) {
+hipError_t launch_select(const float* bias, int m, const moe_cfg& c, const Ws& w, int32_t* header, hipStream_t s,
+                         const int32_t* slot_of) {
   const int kper = (c.n_routed + 63) / 64;
   if (kper == 6)
     hipLaunchKernelGGL(k_select<6>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk, c.norm_topk_prob,
-                       c.route_scale, header, w.status);
+                       c.route_scale, header, w.status, slot_of);
   else
     hipLaunchKernelGGL(k_select<16>, dim3(m), dim3(64), 0, s, w.scores, bias, c.n_routed, c.topk, c.norm_topk_prob,
-                       c.route_scale, header, w.status);
+                       c.route_scale, header, w.status, slot_of);
   return hipGetLastError();
 }
 
-hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
+hipError_t launch_plan(const int32_t* header, int m, const moe_cfg& c, const Ws& w, hipStream_t s, int shq) {
   if (c.n_routed <= 384)
-    hipLaunchKernelGGL(k_plan_small<6>, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
+    hipLaunchKernelGGL(k_plan_small<6>, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status, shq);
   else
-    hipLaunchKernelGGL(k_plan_small<16>, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status);
+    hipLaunchKernelGGL(k_plan_small<16>, dim3(1), dim3(64), 0, s, header, m, c.topk, c.n_routed, w.plan, w.status,
+                       shq);
   return hipGetLastError();
 }
 

@@ -121,8 +121,10 @@ def test_kquant_shared_prefill(shape, m, check):
     tab = v["tab"]
     assert tab["n_pairs"] == m * (shape.topk + 1)
     nu = tab["n_u"]
-    assert tab["u_expert"][nu - 1] == shape.n_routed and tab["u_npairs"][nu - 1] == m
-    assert tab["u_first"][nu - 1] == m * shape.topk
+    nsh = (m + 15) // 16   # the shared group's plan entries: 16 tokens each (one MFMA pass), after the routed ones
+    assert np.all(tab["u_expert"][nu - nsh:nu] == shape.n_routed) and tab["u_expert"][nu - nsh - 1] < shape.n_routed
+    assert np.array_equal(tab["u_first"][nu - nsh:nu], m * shape.topk + 16 * np.arange(nsh))
+    assert np.array_equal(tab["u_npairs"][nu - nsh:nu], np.minimum(16, m - 16 * np.arange(nsh)))
     assert np.array_equal(tab["pair_tok"][m * shape.topk:m * (shape.topk + 1)], np.arange(m))
     toks = range(m) if check is None else sorted(set(np.linspace(0, m - 1, check).astype(int)))
     _check_tokens(spec, x_np, toks, v, o, "out_f32", h)
