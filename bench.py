@@ -287,6 +287,76 @@ def stack_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def cache_bench(args):
+    """Decode through `--layers` dim-4096 layers whose routed experts live in
+    pinned host memory, with an expert cache of `--cache-slots` device slots
+    (the experts stream in over the host link on a miss); `--prefetch-k`
+    predicted experts of the next layer are copied in ahead."""
+    import numpy as np
+    import torch
+
+    import routing_quant_expert_amd as R
+    import synth
+    from synth.device import DeviceLayer, host_arena
+
+    n, m = args.layers, args.m
+    specs = [synth.LayerSpec(synth.SHAPE_DS41, seed=args.seed, layer=l) for l in range(n)]
+    s = specs[0].shape
+    print(f"bench: generating {n} layers, experts in pinned host memory ({n * s.n_routed * s.expert_stride / 1e9:.1f} GB)",
+          file=sys.stderr, flush=True)
+    scratch = torch.empty(s.n_routed * s.expert_stride, dtype=torch.uint8, device="cuda")
+    hosts = [host_arena(sp, scratch) for sp in specs]
+    del scratch
+    torch.cuda.empty_cache()
+    dls = [DeviceLayer(sp, experts_on_device=False) for sp in specs]
+    cfg = dls[0].cfg
+    cache = R.ExpertCache(cfg, hosts, s.expert_stride, s.gate_off, s.up_off, s.down_off, args.cache_slots, m)
+    nt_tok = max(1, args.tokens)
+    xs_all = torch.empty((nt_tok, n + 1, m, s.dim), dtype=torch.uint16, device="cuda")
+    for t in range(nt_tok):
+        xs_all[t, 0] = torch.from_numpy(synth.tokens(specs[0], t * m, m)).cuda()
+    ws = torch.empty(R.workspace_bytes(cfg, m), dtype=torch.uint8, device="cuda")
+    R.workspace_init(cfg, m, ws)
+    layers = [d.layer for d in dls]
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        cache.forward(layers, xs_all[i % nt_tok], ws, prefetch_k=args.prefetch_k)
+    torch.cuda.synchronize()
+    st0 = cache.stats()
+    K = args.steps
+    t0 = time.perf_counter()
+    for i in range(K):
+        cache.forward(layers, xs_all[(args.warmup + i) % nt_tok], ws, prefetch_k=args.prefetch_k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = {k: v - st0[k] for k, v in cache.stats().items()}
+    cache.close()
+    picks = st["hits"] + st["misses"]
+    res = {
+        "metric": "MoE-layer decode tokens/s at m=1 with the routed experts streamed from host memory",
+        "value": K * m / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"moe_stack{n}_decode_m{m}_dim4096_inter2048_e384_top6_cache{args.cache_slots}"
+                               f"_prefetch{args.prefetch_k}", "layers": n, "m": m, "cache_slots": args.cache_slots,
+                   "prefetch_k": args.prefetch_k, "tokens_cycled": nt_tok, "host_expert_bytes": n * s.n_routed * s.expert_stride,
+                   "seed": args.seed},
+        "detail": {"stats": st, "hit_rate": st["hits"] / max(picks, 1),
+                   "prefetch_used_rate": st["prefetch_used"] / max(st["prefetched"], 1),
+                   "copied_bytes_per_step": st["bytes_copied"] / K,
+                   "copy_gbs": st["bytes_copied"] / wall / 1e9},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def prefill_bench(args):
     """m > 8 tokens per step through the prefill kernels: the dim-4096 layer
     with the Zipf-skewed correction bias, m independent N(0,1) token rows."""
@@ -432,6 +502,10 @@ def main():
     ap.add_argument("--time-every", type=int, default=2,
                     help="bracket every n-th step's gate/up dispatch with events (the same in warm-up and timed loop)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-only HBM streaming measurement")
+    ap.add_argument("--cache-slots", type=int, default=0,
+                    help="with --layers: stream the routed experts from pinned host memory through an expert cache of "
+                         "this many device slots")
+    ap.add_argument("--prefetch-k", type=int, default=0, help="with --cache-slots: predicted experts prefetched per token")
     ap.add_argument("--shared-quant", action="store_true",
                     help="the layer's shared expert as Q2_K/Q3_K blocks (run as one more expert) instead of bf16")
     ap.add_argument("--m", type=int, default=1, help="tokens per step (1: the single-token kernels; 2..8: the "
@@ -480,6 +554,8 @@ def main():
     shq = 1 if args.shared_quant else 0
     print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts) on the device",
           file=sys.stderr, flush=True)
+    if args.cache_slots > 0:
+        return cache_bench(args)
     if args.layers > 1:
         return stack_bench(args)
     dl = DeviceLayer(spec)

@@ -256,3 +256,73 @@ def num_threads() -> int:
 
 def set_num_threads(n: int) -> None:
     lib().oracle_set_num_threads(ctypes.c_int(int(n)))
+
+
+# ------------------------------------------- the entry points, on host memory
+class OExperts(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("stride", ctypes.c_uint64), ("gate_off", ctypes.c_uint64),
+                ("up_off", ctypes.c_uint64), ("down_off", ctypes.c_uint64)]
+
+
+class OLayer(ctypes.Structure):
+    _fields_ = [("gate_w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("experts", OExperts),
+                ("sh_w1", ctypes.c_void_p), ("sh_w3", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p),
+                ("shared_kind", ctypes.c_int32), ("shared_q", OExperts)]
+
+
+def _rc(code: int, name: str):
+    if code != 0:
+        raise ValueError(f"{name}: invalid arguments ({code})")
+
+
+def ref_route_select(shape, x, gate_w, bias):
+    """moe_ref_route_select: (logits [m, n_routed], header [m, 1+3k])."""
+    x = _c(x, np.uint16)
+    m = x.shape[0]
+    logits = np.empty((m, shape.n_routed), np.float32)
+    hdr = np.empty((m, 1 + 3 * shape.topk), np.int32)
+    c = cfg_of(shape)
+    _rc(lib().moe_ref_route_select(ctypes.byref(c), _p(x), ctypes.c_int32(m), _p(_c(gate_w, np.uint16)),
+                                   _p(_c(bias, np.float32)), _p(logits), _p(hdr)), "moe_ref_route_select")
+    return logits, hdr
+
+
+def ref_experts(shape, x, header, arena, stride, gate_off, up_off, down_off, prefill=False):
+    """moe_ref_experts_decode / _prefill on a host arena (uint8, expert e at e * stride)."""
+    x = _c(x, np.uint16)
+    m = x.shape[0]
+    hdr = _c(header, np.int32)
+    arena = _c(arena, np.uint8)
+    ex = OExperts(arena.ctypes.data, stride, gate_off, up_off, down_off)
+    y = np.empty((m, shape.dim), np.float32)
+    c = cfg_of(shape)
+    f = lib().moe_ref_experts_prefill if prefill else lib().moe_ref_experts_decode
+    _rc(f(ctypes.byref(c), _p(x), ctypes.c_int32(m), _p(hdr), ctypes.byref(ex), _p(y)), "moe_ref_experts")
+    return y
+
+
+def ref_layer_forward(shape, x, gate_w, bias, arena, stride, gate_off, up_off, down_off, shared_bf16=None,
+                      shared_q=None):
+    """moe_ref_layer_forward: (out_bf16, out_f32, header). shared_bf16 = (w1, w3, w2), or shared_q = one
+    expert's raw blocks (gate | up | down at the arena's offsets)."""
+    x = _c(x, np.uint16)
+    m = x.shape[0]
+    keep = [_c(gate_w, np.uint16), _c(bias, np.float32), _c(arena, np.uint8)]
+    ex = OExperts(keep[2].ctypes.data, stride, gate_off, up_off, down_off)
+    if shared_q is not None:
+        sq = _c(shared_q, np.uint8)
+        keep.append(sq)
+        layer = OLayer(keep[0].ctypes.data, keep[1].ctypes.data, ex, None, None, None, 1,
+                       OExperts(sq.ctypes.data, 0, gate_off, up_off, down_off))
+    else:
+        w = [_c(a, np.uint16) for a in shared_bf16]
+        keep += w
+        layer = OLayer(keep[0].ctypes.data, keep[1].ctypes.data, ex, w[0].ctypes.data, w[1].ctypes.data,
+                       w[2].ctypes.data, 0, OExperts())
+    ob = np.empty((m, shape.dim), np.uint16)
+    of = np.empty((m, shape.dim), np.float32)
+    hdr = np.empty((m, 1 + 3 * shape.topk), np.int32)
+    c = cfg_of(shape)
+    _rc(lib().moe_ref_layer_forward(ctypes.byref(c), ctypes.byref(layer), _p(x), ctypes.c_int32(m), _p(ob), _p(of),
+                                    _p(hdr)), "moe_ref_layer_forward")
+    return ob, of, hdr

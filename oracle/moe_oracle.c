@@ -561,3 +561,139 @@ EXPORT void oracle_scores_par(const float* logits, int64_t n, float temp, float*
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_score(logits[i], temp);
 }
+
+/* ------------------------------------------------------------------------ */
+/* The four entry points of the layer library, mirrored on host memory so    */
+/* that one suite can drive both implementations through one interface: the */
+/* same argument order and struct layouts as the library's C ABI (declared   */
+/* here independently), each composed from the functions above with no      */
+/* arithmetic of its own. Return 0, or -1 for a NULL argument or m < 1. A    */
+/* token whose header has a pick outside [0, n_routed) or a repeated pick    */
+/* gets a zero routed output [device_route.rs, fn parse_header: picks in     */
+/* range].                                                                   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const void* base;
+  uint64_t stride, gate_off, up_off, down_off;
+} oexperts;
+
+typedef struct {
+  const uint16_t* gate_w;
+  const float* bias;
+  oexperts experts;
+  const uint16_t *sh_w1, *sh_w3, *sh_w2;
+  int32_t shared_kind; /* 0: bf16 sh_w*, 1: K-quant blocks in shared_q */
+  oexperts shared_q;
+} olayer;
+
+EXPORT int moe_ref_route_select(const ocfg* c, const uint16_t* x, int32_t m, const uint16_t* gate_w,
+                                const float* bias, float* logits, int32_t* header) {
+  if (!c || !x || !gate_w || !bias || !header || m < 1) return -1;
+  float* lg = logits ? logits : (float*)malloc(sizeof(float) * (size_t)m * c->n_routed);
+  oracle_router_logits(x, m, gate_w, c->n_routed, c->dim, lg);
+  oracle_select(c, lg, m, bias, header, NULL);
+  if (!logits) free(lg);
+  return 0;
+}
+
+/* One token's routed experts: their outputs ys [k][dim] and weights w in plan
+ * order (ascending expert id), and the token's q8_1(x); 0 when the header's
+ * picks are out of range or repeated. */
+static int ref_token_experts(const ocfg* c, const uint16_t* xrow, const int32_t* hd, const oexperts* ex,
+                             int8_t* xq, uint16_t* xd16, float* ys, float* w) {
+  int k = c->topk, dim = c->dim, inter = c->inter;
+  float* xf = (float*)malloc(sizeof(float) * dim);
+  for (int i = 0; i < dim; ++i) xf[i] = oracle_bf16_to_f32(xrow[i]);
+  oracle_q8_1(xf, dim, xq, xd16);
+  free(xf);
+  for (int r = 0; r < k; ++r) {
+    if (hd[1 + r] < 0 || hd[1 + r] >= c->n_routed) return 0;
+    for (int r2 = 0; r2 < r; ++r2)
+      if (hd[1 + r2] == hd[1 + r]) return 0;
+  }
+  int ids[64];
+  for (int r = 0; r < k; ++r) {
+    ids[r] = hd[1 + r];
+    uint32_t b = (uint32_t)hd[1 + k + r];
+    memcpy(&w[r], &b, 4);
+  }
+  for (int a = 1; a < k; ++a) /* plan order: ascending expert id, weights with their picks */
+    for (int b = a; b > 0 && ids[b] < ids[b - 1]; --b) {
+      int ti = ids[b]; ids[b] = ids[b - 1]; ids[b - 1] = ti;
+      float tw = w[b]; w[b] = w[b - 1]; w[b - 1] = tw;
+    }
+  float *g = (float*)malloc(sizeof(float) * inter), *u = (float*)malloc(sizeof(float) * inter);
+  float* h = (float*)malloc(sizeof(float) * inter);
+  int8_t* hq = (int8_t*)malloc(inter);
+  uint16_t* hd16 = (uint16_t*)malloc(2 * (inter / 32));
+  for (int r = 0; r < k; ++r) {
+    const uint8_t* e = (const uint8_t*)ex->base + (uint64_t)ids[r] * ex->stride;
+    oracle_expert(c, xq, xd16, e + ex->gate_off, e + ex->up_off, e + ex->down_off, g, u, h, hq, hd16,
+                  ys + (size_t)r * dim, NULL, NULL, NULL);
+  }
+  free(g); free(u); free(h); free(hq); free(hd16);
+  return 1;
+}
+
+EXPORT int moe_ref_experts_decode(const ocfg* c, const uint16_t* x, int32_t m, const int32_t* header,
+                                  const oexperts* experts, float* y_routed) {
+  if (!c || !x || !header || !experts || !experts->base || !y_routed || m < 1) return -1;
+  int k = c->topk, dim = c->dim, hw = 1 + 3 * k;
+  int8_t* xq = (int8_t*)malloc(dim);
+  uint16_t* xd16 = (uint16_t*)malloc(2 * (dim / 32));
+  float* ys = (float*)malloc(sizeof(float) * (size_t)k * dim);
+  float w[64];
+  for (int32_t t = 0; t < m; ++t) {
+    float* yt = y_routed + (int64_t)t * dim;
+    if (ref_token_experts(c, x + (int64_t)t * dim, header + (int64_t)t * hw, experts, xq, xd16, ys, w))
+      oracle_combine(dim, k, ys, w, NULL, yt, NULL);
+    else
+      for (int i = 0; i < dim; ++i) yt[i] = 0.0f;
+  }
+  free(xq); free(xd16); free(ys);
+  return 0;
+}
+
+/* Each token of a prefill batch is defined exactly as at m = 1. */
+EXPORT int moe_ref_experts_prefill(const ocfg* c, const uint16_t* x, int32_t m, const int32_t* header,
+                                   const oexperts* experts, float* y_routed) {
+  return moe_ref_experts_decode(c, x, m, header, experts, y_routed);
+}
+
+EXPORT int moe_ref_layer_forward(const ocfg* c, const olayer* layer, const uint16_t* x, int32_t m,
+                                 uint16_t* out_bf16, float* out_f32, int32_t* header) {
+  if (!c || !layer || !x || !out_bf16 || m < 1) return -1;
+  if (layer->shared_kind == 0 ? (!layer->sh_w1 || !layer->sh_w3 || !layer->sh_w2) : !layer->shared_q.base) return -1;
+  int k = c->topk, dim = c->dim, inter = c->inter, hw = 1 + 3 * k;
+  int32_t* hdr = header ? header : (int32_t*)malloc(sizeof(int32_t) * (size_t)m * hw);
+  moe_ref_route_select(c, x, m, layer->gate_w, layer->bias, NULL, hdr);
+  int8_t* xq = (int8_t*)malloc(dim);
+  uint16_t* xd16 = (uint16_t*)malloc(2 * (dim / 32));
+  float* ys = (float*)malloc(sizeof(float) * (size_t)k * dim);
+  float* sd = (float*)malloc(sizeof(float) * dim);
+  float* o32 = (float*)malloc(sizeof(float) * dim);
+  float *sg = (float*)malloc(sizeof(float) * inter), *su = (float*)malloc(sizeof(float) * inter);
+  float* sh32 = (float*)malloc(sizeof(float) * inter);
+  uint16_t* sh = (uint16_t*)malloc(2 * inter);
+  int8_t* hq = (int8_t*)malloc(inter);
+  uint16_t* hd16 = (uint16_t*)malloc(2 * (inter / 32));
+  float w[64];
+  for (int32_t t = 0; t < m; ++t) {
+    const uint16_t* xrow = x + (int64_t)t * dim;
+    ref_token_experts(c, xrow, hdr + (int64_t)t * hw, &layer->experts, xq, xd16, ys, w);
+    if (layer->shared_kind == 0) {
+      oracle_shared(c, xrow, layer->sh_w1, layer->sh_w3, layer->sh_w2, sg, su, sh, sd);
+    } else {   /* the K-quant shared expert: one more expert on the same q8_1(x) */
+      const uint8_t* b = (const uint8_t*)layer->shared_q.base;
+      oracle_expert(c, xq, xd16, b + layer->shared_q.gate_off, b + layer->shared_q.up_off,
+                    b + layer->shared_q.down_off, sg, su, sh32, hq, hd16, sd, NULL, NULL, NULL);
+    }
+    /* the routed sum in plan order, then the shared output added after it */
+    oracle_combine(dim, k, ys, w, sd, o32, out_bf16 + (int64_t)t * dim);
+    if (out_f32) memcpy(out_f32 + (int64_t)t * dim, o32, sizeof(float) * dim);
+  }
+  free(xq); free(xd16); free(ys); free(sd); free(o32); free(sg); free(su); free(sh32); free(sh); free(hq); free(hd16);
+  if (!header) free(hdr);
+  return 0;
+}

@@ -76,7 +76,7 @@ class DeviceLayer:
     shared expert (bf16, or K-quant blocks when spec.shared_quant), plus the
     binding structs that point at them."""
 
-    def __init__(self, spec: LayerSpec, device="cuda", arena=None):
+    def __init__(self, spec: LayerSpec, device="cuda", arena=None, experts_on_device=True):
         import torch
         from routing_quant_expert_amd import MOE_SHARED_KQUANT, Experts, Layer, cfg_from_shape
         s = spec.shape
@@ -85,9 +85,12 @@ class DeviceLayer:
         self.gate_w = torch.empty((s.n_routed, s.dim), dtype=torch.uint16, device=device)
         normal_bf16_into(self.gate_w, spec.seed, spec.tag(K_GATE_W), SIGMA_W)
         self.bias = torch.from_numpy(bias(spec)).to(device)
-        self.arena = arena if arena is not None else torch.empty(s.n_routed * s.expert_stride, dtype=torch.uint8,
-                                                                  device=device)
-        fill_arena(spec, self.arena)
+        if experts_on_device:
+            self.arena = arena if arena is not None else torch.empty(s.n_routed * s.expert_stride, dtype=torch.uint8,
+                                                                      device=device)
+            fill_arena(spec, self.arena)
+        else:   # the routed experts live elsewhere (an expert cache): a placeholder arena of one expert
+            self.arena = torch.zeros(s.expert_stride, dtype=torch.uint8, device=device)
         self.experts = Experts(self.arena.data_ptr(), s.expert_stride, s.gate_off, s.up_off, s.down_off)
         if spec.shared_quant:
             self.sh_w1 = self.sh_w3 = self.sh_w2 = None
@@ -109,3 +112,19 @@ class DeviceLayer:
     def tokens(self, t0: int, m: int, device="cuda"):
         import torch
         return torch.from_numpy(tokens(self.spec, t0, m)).to(device)
+
+
+def host_arena(spec: LayerSpec, scratch=None):
+    """Every routed expert's raw blocks of the layer in pinned host memory
+    (generated on the device into `scratch`, a uint8 device tensor of at least
+    n_routed * stride bytes, then copied down)."""
+    import torch
+    s = spec.shape
+    nbytes = s.n_routed * s.expert_stride
+    if scratch is None:
+        scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    fill_arena(spec, scratch)
+    out = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    out.copy_(scratch[:nbytes])
+    torch.cuda.synchronize()
+    return out

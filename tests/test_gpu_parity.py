@@ -77,6 +77,54 @@ def test_scores_bit_exact_against_oracle():
         say(f"scores flags={flags}: {x.size} values bit-exact")
 
 
+def _near_f32_midpoint(y64, rel):
+    """Where a float64 value lies within rel * |y| of the midpoint between its
+    f32 rounding and that rounding's neighbour toward it (torch, device)."""
+    f = y64.float()
+    fd = f.double()
+    nb = torch.nextafter(f, torch.where(y64 > fd, torch.full_like(f, float("inf")), torch.full_like(f, float("-inf"))))
+    mid = 0.5 * (fd + nb.double())
+    return (fd != y64) & ((y64 - mid).abs() <= rel * y64.abs())
+
+
+def test_score_chain_on_every_f32_input():
+    """All 2^32 f32 inputs (temp 1): the device's fast score path (double
+    exp/log1p with Ziv's rounding test) equals its extended-precision path on
+    every input, so the test's bound holds everywhere; and on every finite
+    input of [-104, 20] whose exp or log1p step lies within 2^-40 relative of
+    an f32 midpoint (the hard cases of correct rounding, found with float64
+    on the device) the device equals the oracle's correctly rounded chain."""
+    n = 1 << 27
+    hard = []
+    for c in range(32):
+        v = torch.arange(c * n, (c + 1) * n, dtype=torch.int64, device="cuda")
+        x = (((v + (1 << 31)) % (1 << 32)) - (1 << 31)).to(torch.int32).view(torch.float32)
+        a, b = torch.empty_like(x), torch.empty_like(x)
+        R.scores(x, 1.0, a, 0)
+        R.scores(x, 1.0, b, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), c
+        ok = torch.isfinite(x) & (x >= -104.0) & (x <= 20.0)
+        xd = x.double()
+        e64 = torch.exp(xd)
+        l64 = torch.log1p(e64.float().double())
+        h = ok & (_near_f32_midpoint(e64, 2.0 ** -40) | _near_f32_midpoint(l64, 2.0 ** -40))
+        hard.append(x[h].cpu())
+        del v, x, a, b, xd, e64, l64, h
+    hx = torch.cat(hard).numpy()
+    say(f"score chain: 2^32 inputs fast == extended; {hx.size} near-midpoint inputs against the oracle")
+    assert hx.size > 1000
+    want = oracle.scores(hx, 1.0)
+    xd = torch.from_numpy(hx).cuda()
+    out = torch.empty_like(xd)
+    R.scores(xd, 1.0, out, 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, (hx[bad[:5]], got[bad[:5]], want[bad[:5]])
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- routing
 @pytest.mark.parametrize("shape,m", [(TINY, 1), (TINY, 5), (TINY, 37), (DS41, 1), (DS41, 8)])
 def test_route_select_bit_exact(shape, m):
