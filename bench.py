@@ -374,6 +374,7 @@ def prefill_bench(args):
     print(f"bench: generating the layer (dim {s.dim}, inter {s.inter}, {s.n_routed} experts, Zipf bias)",
           file=sys.stderr, flush=True)
     dl = DeviceLayer(spec)
+    glibc = use_score_mode(args, dl)
     nb = max(1, min(args.tokens, 4))   # distinct batches cycled through
     xs = torch.from_numpy(synth.tokens(spec, 0, nb * m)).cuda()
     ws = torch.empty(R.workspace_bytes(dl.cfg, m), dtype=torch.uint8, device="cuda")
@@ -465,8 +466,9 @@ def prefill_bench(args):
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": f"moe_layer_prefill_m{m}_zipf_dim4096_inter2048_e384_top6" +
-                               ("_shared_q2k_q3k" if shq else ""), "dim": s.dim,
+                               ("_shared_q2k_q3k" if shq else "") + ("_glibc_scores" if glibc else ""), "dim": s.dim,
                    "shared_expert": "Q2_K/Q3_K blocks" if shq else "bf16",
+                   "scores": "glibc" if glibc else "correctly rounded",
                    "inter": s.inter, "n_routed": s.n_routed, "topk": s.topk, "m": m, "batches_cycled": nb,
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -488,6 +490,18 @@ def prefill_bench(args):
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds, "; the oracle defines each prefill token's output as its single-token output, so tokens/s of the two compare")
     print(json.dumps(res), flush=True)
+
+
+def use_score_mode(args, dl) -> bool:
+    """--score-mode glibc: register the glibc score table on the device and
+    switch the layer's configuration to it (outside any timed region)."""
+    if args.score_mode != "glibc":
+        return False
+    import routing_quant_expert_amd as R
+    print("bench: building the glibc score table", file=sys.stderr, flush=True)
+    R.enable_glibc_scores()
+    dl.cfg.score_mode = R.MOE_SCORE_GLIBC
+    return True
 
 
 def main():
@@ -515,6 +529,9 @@ def main():
                     help="decode through a stack of this many layers per step (each its own seeded weights)")
     ap.add_argument("--graph", action="store_true",
                     help="with --layers: replay each step from a captured graph (checked against eager first)")
+    ap.add_argument("--score-mode", choices=("cr", "glibc"), default="cr",
+                    help="router scores: correctly rounded (default) or the host glibc's, through the library's "
+                         "exception table")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -529,8 +546,8 @@ def main():
         print(f"copied {src.numel()} bytes x3", flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
-              f"of the layer is a design note, not a measured path.", file=sys.stderr)
+        print(f"bench.py: the layer is measured on one GPU (asked for --gpus {args.gpus}); its sharding across "
+              f"GPUs is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
     if args.m < 1:
         print("bench.py: --m must be >= 1", file=sys.stderr)
@@ -559,6 +576,7 @@ def main():
     if args.layers > 1:
         return stack_bench(args)
     dl = DeviceLayer(spec)
+    glibc = use_score_mode(args, dl)
     if m == 1:
         xs = torch.from_numpy(synth.tokens(spec, 0, args.tokens)).cuda()
     else:
@@ -633,7 +651,7 @@ def main():
     shared_down_bytes = 0 if shq else s.inter * s.dim * 2
     expert_bytes = 2 * s.gate_bytes + s.down_bytes
     us = {k: float(v.mean()) * 1e3 for k, v in k_ms.items()}
-    sfx = "_shared_q2k_q3k" if shq else ""
+    sfx = ("_shared_q2k_q3k" if shq else "") + ("_glibc_scores" if glibc else "")
     if m == 1:
         kernel = "k_gateup_m1"
         n_u = np.full(1, s.topk)
@@ -685,6 +703,7 @@ def main():
         "config": {"workload": workload, "dim": s.dim, "inter": s.inter,
                    "n_routed": s.n_routed, "topk": s.topk, "m": m, "tokens_cycled": args.tokens,
                    "shared_expert": "Q2_K/Q3_K blocks" if shq else "bf16",
+                   "scores": "glibc" if glibc else "correctly rounded",
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

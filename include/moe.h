@@ -75,7 +75,21 @@ typedef struct moe_cfg {
   float gate_temp;        /* logits are divided by this before softplus    */
   float route_scale;      /* weights are multiplied by this                */
   float swiglu_limit;     /* SwiGLU clamp L                                */
+  int32_t score_mode;     /* MOE_SCORE_CR (0) or MOE_SCORE_GLIBC (1)       */
 } moe_cfg;
+
+/* Score modes. MOE_SCORE_CR: every step of sqrt(softplus(logit / temp)) is
+ * correctly rounded to f32 (any libm that rounds correctly gives these bits).
+ * MOE_SCORE_GLIBC: the scores of the host's glibc, bit for bit, as the pages'
+ * host reference computes them with f32 expf / log1pf / sqrtf [device_route.rs,
+ * module doc: glibc-exact softplus; moe_v41.rs, fn softplus]: the device
+ * computes the correctly rounded chain and replaces it, for the inputs where
+ * glibc's differs, by glibc's value from a table the host builds from its own
+ * libm (moe_glibc_score_table) and registers for the device
+ * (moe_set_score_table). A call with MOE_SCORE_GLIBC and no table registered
+ * for the current device fails with MOE_EINVAL. */
+#define MOE_SCORE_CR 0
+#define MOE_SCORE_GLIBC 1
 
 /* The resident routed experts: expert e's blocks start at base + e*stride.
  * Inside: gate (w1) and up (w3) at gate_off / up_off, Q2_K [inter rows]
@@ -332,10 +346,30 @@ int moe_cache_resident(const moe_cache* cache, int32_t layer, int32_t* slots);
 int moe_lru_simulate(int32_t n_slots, int64_t n_keys, const int64_t* keys, const int32_t* batch_len,
                      int32_t n_batches, int32_t* slots_out, int32_t* miss_out);
 
+/* The glibc score table, computed on the host from its libm: every f32 input
+ * z <= 20 (z = logit / temp) where sqrtf(log1pf(expf(z))) differs from the
+ * correctly rounded chain, ascending in its bit pattern: keys[i] = the bits of
+ * z, vals[i] = the bits of glibc's score; index[p] (p < 2^24, plus one end
+ * entry, MOE_SCORE_INDEX_LEN words) = the first i with keys[i] >> 8 >= p.
+ * Pass keys = NULL to get the count in *n (vals and index are then ignored);
+ * otherwise keys and vals hold cap >= *n entries and index
+ * MOE_SCORE_INDEX_LEN, else MOE_EINVAL. The first call sweeps all 2^32 inputs
+ * on the host's cores (seconds); later calls copy its result. Host memory. */
+#define MOE_SCORE_INDEX_LEN ((1 << 24) + 1)
+int moe_glibc_score_table(uint32_t* keys, uint32_t* vals, uint32_t* index, int64_t cap, int64_t* n);
+
+/* Registers the device copies of the glibc score table (keys, vals [n],
+ * index [MOE_SCORE_INDEX_LEN], device pointers owned by the caller and kept
+ * alive while the mode is used) for the current device; NULL keys
+ * unregisters. Calls that route with MOE_SCORE_GLIBC read the registration of
+ * the device current when they are made. */
+int moe_set_score_table(const uint32_t* keys, const uint32_t* vals, const uint32_t* index, int64_t n);
+
 /* The score chain of A3 alone on device data: out[i] = sqrt(softplus(
  * logits[i] / temp)) with correctly rounded exp, log1p, division and sqrt
  * [moe_v41.rs, fn softplus, fn route_from_logits]. flags bit 0 forces the
- * extended-precision path of exp/log1p for every element (checking only). */
+ * extended-precision path of exp/log1p for every element (checking only);
+ * flags bit 1 gives the glibc mode's scores (the registered table). */
 int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream);
 
 /* The same score chain computed on the host CPU by the library's own code

@@ -21,12 +21,12 @@ _lib = None
 class OCfg(ctypes.Structure):
     _fields_ = [("dim", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_routed", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32), ("gate_temp", ctypes.c_float),
-                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float)]
+                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float), ("score_mode", ctypes.c_int32)]
 
 
 def cfg_of(shape) -> OCfg:
     return OCfg(shape.dim, shape.inter, shape.n_routed, shape.topk, int(shape.norm_topk_prob),
-                shape.gate_temp, shape.route_scale, shape.swiglu_limit)
+                shape.gate_temp, shape.route_scale, shape.swiglu_limit, int(shape.score_mode))
 
 
 def lib():
@@ -111,6 +111,14 @@ def scores(logits, temp: float) -> np.ndarray:
     a = _c(logits, np.float32)
     out = np.empty(a.shape, np.float32)
     lib().oracle_scores_par(_p(a), _i64(a.size), ctypes.c_float(temp), _p(out))
+    return out
+
+
+def scores_glibc(logits, temp: float) -> np.ndarray:
+    """The glibc mode's scores: the host C library's f32 expf / log1pf / sqrtf chain."""
+    a = _c(logits, np.float32)
+    out = np.empty(a.shape, np.float32)
+    lib().oracle_scores_glibc(_p(a), _i64(a.size), ctypes.c_float(temp), _p(out))
     return out
 
 

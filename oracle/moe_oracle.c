@@ -39,6 +39,7 @@
 typedef struct {
   int32_t dim, inter, n_routed, topk, norm_topk_prob;
   float gate_temp, route_scale, swiglu_limit;
+  int32_t score_mode; /* 0: correctly rounded chain, 1: the host's glibc chain */
 } ocfg;
 
 static void die(const char* msg) {
@@ -151,6 +152,21 @@ EXPORT float oracle_score(float logit, float temp) {
 
 EXPORT void oracle_scores(const float* logits, int64_t n, float temp, float* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_score(logits[i], temp);
+}
+
+/* The glibc mode: the same chain with the host C library's f32 expf, log1pf  */
+/* and sqrtf, as the pages' host reference evaluates it (f32 exp, ln_1p and   */
+/* sqrt) [moe_v41.rs, fn softplus, fn route_from_logits; device_route.rs,     */
+/* module doc: glibc-exact softplus].                                         */
+EXPORT float oracle_score_glibc(float logit, float temp) {
+  float z = logit / temp;
+  float sp = z > 20.0f ? z : log1pf(expf(z));
+  return sqrtf(sp);
+}
+
+EXPORT void oracle_scores_glibc(const float* logits, int64_t n, float temp, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_score_glibc(logits[i], temp);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -299,7 +315,8 @@ EXPORT void oracle_select(const ocfg* c, const float* logits, int64_t m, const f
   for (int64_t t = 0; t < m; ++t) {
     int nan_key = 0;
     for (int e = 0; e < n; ++e) {
-      scores[e] = oracle_score(logits[t * n + e], c->gate_temp);
+      scores[e] = c->score_mode == 1 ? oracle_score_glibc(logits[t * n + e], c->gate_temp)
+                                     : oracle_score(logits[t * n + e], c->gate_temp);
       key[e] = scores[e] + bias[e];
       if (isnan(key[e])) nan_key = 1;
       if (scores_out) scores_out[t * n + e] = scores[e];

@@ -29,7 +29,7 @@ class MoeError(RuntimeError):
 class Cfg(ctypes.Structure):
     _fields_ = [("dim", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_routed", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32), ("gate_temp", ctypes.c_float),
-                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float)]
+                ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float), ("score_mode", ctypes.c_int32)]
 
 
 class Experts(ctypes.Structure):
@@ -91,6 +91,8 @@ def lib():
         L.moe_swiglu_host.argtypes = [_VP, _VP, ctypes.c_int64, ctypes.c_float, _VP]
         L.moe_time_next_launch.argtypes = [ctypes.c_int32, _VP, _VP]
         L.moe_read_probe.argtypes = [_VP, ctypes.c_uint64, _VP, ctypes.c_int32, _VP]
+        L.moe_glibc_score_table.argtypes = [_VP, _VP, _VP, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+        L.moe_set_score_table.argtypes = [_VP, _VP, _VP, ctypes.c_int64]
         L.moe_cache_create.argtypes = [ctypes.POINTER(Cfg), ctypes.c_int32, ctypes.POINTER(_VP), ctypes.c_uint64,
                                        ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.POINTER(_VP)]
@@ -124,7 +126,7 @@ def _stream(stream):
 
 def cfg_from_shape(shape) -> Cfg:
     return Cfg(shape.dim, shape.inter, shape.n_routed, shape.topk, int(shape.norm_topk_prob), shape.gate_temp,
-               shape.route_scale, shape.swiglu_limit)
+               shape.route_scale, shape.swiglu_limit, int(shape.score_mode))
 
 
 def header_words(cfg: Cfg) -> int:
@@ -196,6 +198,43 @@ def scores_host(logits: np.ndarray, temp: float, flags: int = 0) -> np.ndarray:
     out = np.empty_like(a)
     _check(lib().moe_scores_host(a.ctypes.data, a.size, ctypes.c_float(temp), out.ctypes.data, flags))
     return out
+
+
+MOE_SCORE_CR = 0
+MOE_SCORE_GLIBC = 1
+SCORE_INDEX_LEN = (1 << 24) + 1
+
+
+def glibc_score_table():
+    """(keys, vals, index) of the glibc score mode, as uint32 numpy arrays."""
+    n = ctypes.c_int64(0)
+    _check(lib().moe_glibc_score_table(None, None, None, 0, ctypes.byref(n)))
+    keys = np.empty(n.value, np.uint32)
+    vals = np.empty(n.value, np.uint32)
+    index = np.empty(SCORE_INDEX_LEN, np.uint32)
+    _check(lib().moe_glibc_score_table(keys.ctypes.data, vals.ctypes.data, index.ctypes.data, n.value,
+                                       ctypes.byref(n)))
+    return keys, vals, index
+
+
+_score_tables = {}
+
+
+def enable_glibc_scores(device=None):
+    """Uploads the glibc score table to `device` (default: the current one) and
+    registers it there; the tensors stay referenced here for the process."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    if dev.index in _score_tables:
+        return
+    keys, vals, index = glibc_score_table()
+    with torch.cuda.device(dev):
+        # (a host whose libm agrees everywhere still registers a non-NULL, empty table)
+        t = [torch.from_numpy(a.view(np.int32) if a.size else np.zeros(1, np.int32)).to(dev)
+             for a in (keys, vals, index)]
+        torch.cuda.synchronize(dev)
+        _check(lib().moe_set_score_table(t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), keys.size))
+    _score_tables[dev.index] = t
 
 
 def swiglu_host(g: np.ndarray, u: np.ndarray, limit: float) -> np.ndarray:

@@ -21,7 +21,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-command-line-argument"]
 SOURCES = ["moe_api.hip", "moe_route.hip", "moe_experts.hip", "moe_decode1.hip", "moe_prefill.hip",
-           "moe_shared_pf.hip", "moe_cache.hip"]
+           "moe_shared_pf.hip", "moe_cache.hip", "moe_score_table.hip"]
 # the prefill kernels consume MFMA results in VALU code: keep them in VGPRs (no accvgpr copies)
 EXTRA = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

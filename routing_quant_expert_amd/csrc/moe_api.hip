@@ -126,6 +126,8 @@ int check_cfg(const moe_cfg* c) {
     return fail(MOE_EUNSUPPORTED, "dim and inter must be 256 * a power of two <= 16 %s(dim %lld)", "", c->dim);
   if (c->topk < 1 || c->topk > kMaxTopk || c->n_routed < c->topk || c->n_routed > kMaxRouted)
     return fail(MOE_EUNSUPPORTED, "need 1 <= topk <= 8 and topk <= n_routed <= 1024%s (n_routed %lld)", "", c->n_routed);
+  if (c->score_mode != MOE_SCORE_CR && c->score_mode != MOE_SCORE_GLIBC)
+    return fail(MOE_EINVAL, "score_mode must be MOE_SCORE_CR or MOE_SCORE_GLIBC%s (%lld)", "", c->score_mode);
   return MOE_OK;
 }
 
@@ -467,6 +469,7 @@ int moe_workspace_layout(const moe_cfg* cfg, int32_t max_m, moe_ws_layout* out) 
 int moe_route_select(const moe_cfg* cfg, const uint16_t* x, int32_t m, const uint16_t* gate_w, const float* bias,
                      float* logits, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
+  if (int r = check_score_mode(*cfg)) return r;
   if (!x || !gate_w || !bias || !header) return fail(MOE_EINVAL, "x, gate_w, bias and header must be non-NULL%s%lld");
   if (int r = check_m(*cfg, m)) return r;
   if (!a16(x) || !a16(gate_w)) return fail(MOE_EINVAL, "x and gate_w must be 16-byte aligned%s%lld");
@@ -546,6 +549,7 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
 int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m, uint16_t* out_bf16,
                       float* out_f32, int32_t* header, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
+  if (int r = check_score_mode(*cfg)) return r;
   if (!x || !out_bf16) return fail(MOE_EINVAL, "x and out_bf16 must be non-NULL%s%lld");
   if (int r = check_layer(layer)) return r;
   if (int r = check_m(*cfg, m)) return r;
@@ -561,6 +565,7 @@ int moe_layer_forward(const moe_cfg* cfg, const moe_layer* layer, const uint16_t
 int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_layers, uint16_t* xs, int32_t m,
                       float* out_f32, int32_t* headers, void* ws, size_t ws_bytes, void* stream) {
   if (int r = check_cfg(cfg)) return r;
+  if (int r = check_score_mode(*cfg)) return r;
   if (!layers || !xs) return fail(MOE_EINVAL, "layers and xs must be non-NULL%s%lld");
   if (n_layers < 1) return fail(MOE_EINVAL, "n_layers must be >= 1%s (n_layers %lld)", "", n_layers);
   if (int r = check_m(*cfg, m)) return r;
@@ -589,6 +594,11 @@ int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t f
 
 int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags) {
   if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
+  if (flags & 2) {
+    const ScoreTable t = host_score_table();
+    for (int64_t i = 0; i < n; ++i) out[i] = score_mode_of(logits[i], temp, t);
+    return MOE_OK;
+  }
   for (int64_t i = 0; i < n; ++i) out[i] = score_of(logits[i], temp, (flags & 1) != 0);
   return MOE_OK;
 }
@@ -619,6 +629,7 @@ int moe_read_probe(const void* buf, uint64_t bytes, uint32_t* sink, int32_t bloc
 int moe_layer_forward_noalloc(const moe_cfg* cfg, const moe_layer* layer, const uint16_t* x, int32_t m,
                               uint16_t* out_bf16, float* out_f32, int32_t* header, void* stream) {
   if (int r = check_cfg(cfg)) return r;
+  if (int r = check_score_mode(*cfg)) return r;
   if (!x || !out_bf16) return fail(MOE_EINVAL, "x and out_bf16 must be non-NULL%s%lld");
   if (int r = check_layer(layer)) return r;
   if (m < 1 || m > kMaxDecodeTokens)

@@ -282,6 +282,7 @@ int moe_cache_forward(moe_cache* cache, const moe_cfg* cfg, const moe_layer* lay
                       void* ws, size_t ws_bytes, void* stream) {
   if (!cache) return fail(MOE_EINVAL, "expert cache is NULL%s%lld");
   if (int r = check_cfg(cfg)) return r;
+  if (int r = check_score_mode(*cfg)) return r;
   moe_cache* c = cache;
   if (std::memcmp(cfg, &c->cfg, sizeof(moe_cfg)) != 0)
     return fail(MOE_EINVAL, "expert cache: cfg differs from the one the cache was made for%s%lld");

@@ -56,8 +56,8 @@ constexpr int kLoadAhead = 8;   // 16-byte chunks per lane kept in flight by one
 
 __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int dim,
                             const uint16_t* __restrict__ gate_w, int n_routed, float temp, float* __restrict__ logits,
-                            float* __restrict__ scores, float* __restrict__ logits_out, int t_lo = 0,
-                            int t_hi = -1) {
+                            float* __restrict__ scores, float* __restrict__ logits_out, const ScoreTable& st,
+                            int t_lo = 0, int t_hi = -1) {
   const int e = blk * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (e >= n_routed) return;
@@ -116,7 +116,7 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
       const int64_t o = (int64_t)(t0 + lane) * n_routed + e;
       logits[o] = lg;
       if (logits_out) logits_out[o] = lg;
-      scores[o] = score_of(lg, temp);
+      scores[o] = score_mode_of(lg, temp, st);
     }
   }
 }

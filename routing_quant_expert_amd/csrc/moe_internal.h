@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/moe.h"
+#include "moe_math.h"
 
 namespace moe {
 
@@ -157,6 +158,15 @@ hipError_t launch_gateup_m1(const XArena& ex, const FrontSelect* sel, const int3
                             const uint16_t* x, const moe_layer* layer, const moe_cfg& c, const Ws& w, hipStream_t s);
 hipError_t launch_down_m1(const XArena& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
                           hipStream_t s);
+// The glibc score table registered for the current device when c.score_mode
+// is MOE_SCORE_GLIBC (checked by check_cfg), else the empty table.
+ScoreTable score_table_for(const moe_cfg& c);
+// MOE_OK, or MOE_EINVAL when c asks for the glibc mode and the current device
+// has no table registered (every entry point that computes scores).
+int check_score_mode(const moe_cfg& c);
+// The host's copy of the glibc table (built on first use).
+ScoreTable host_score_table();
+
 // ---- argument checks and the error message (moe_api.hip) ----
 int fail(int code, const char* fmt, const char* a = "", long long b = 0);   // fmt takes a %s then a %lld
 int hip_fail(hipError_t e, const char* where);

@@ -183,6 +183,37 @@ __host__ __device__ inline float score_of(float logit, float temp, bool force_sl
   return (float)sqrt((double)sp);
 }
 
+// The glibc score mode's exceptions (moe_glibc_score_table): keys = the f32
+// bits of the inputs z <= 20 whose glibc chain differs from the correctly
+// rounded one, ascending; vals = glibc's scores; index[p] = the first key with
+// prefix (bits >> kScorePrefixShift) >= p. keys == nullptr: the correctly
+// rounded mode.
+constexpr int kScorePrefixShift = 8;   // 2^24 buckets of 256 inputs
+struct ScoreTable {
+  const uint32_t* keys;
+  const uint32_t* vals;
+  const uint32_t* index;
+};
+
+// score_of, or in the glibc mode glibc's value where it differs: the input's
+// prefix bucket, then a binary search of its keys (about one per bucket).
+__host__ __device__ inline float score_mode_of(float logit, float temp, const ScoreTable& t) {
+  const float s = score_of(logit, temp);
+  if (!t.keys) return s;
+  const float z = (float)((double)logit / (double)temp);
+  if (!(z <= 20.0f)) return s;
+  const uint32_t b = __builtin_bit_cast(uint32_t, z);
+  const uint32_t p = b >> kScorePrefixShift;
+  uint32_t lo = t.index[p], hi = t.index[p + 1];
+  const uint32_t end = hi;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (t.keys[mid] < b) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < end && t.keys[lo] == b) ? __builtin_bit_cast(float, t.vals[lo]) : s;
+}
+
 // Clamped SwiGLU: silu(min(g, L)) * clamp(u, -L, L), silu(z) = z / (1 + exp(-z)).
 __host__ __device__ inline float swiglu(float g, float u, float L) {
   float zg = g > L ? L : g;

@@ -76,7 +76,7 @@ __device__ inline void bf16x8_f32(uint4 v, float (&f)[8]) {
 __device__ void router_rows4(int e0, int t0, const uint16_t* __restrict__ x, int m, int dim,
                              const uint16_t* __restrict__ gate_w, int n_routed, float temp,
                              float* __restrict__ logits, float* __restrict__ scores,
-                             float* __restrict__ logits_out) {
+                             float* __restrict__ logits_out, const ScoreTable& st) {
   const int lane = threadIdx.x & 63;
   const int nt = min(kRpTok, m - t0);
   float p[kRpRows][kRpTok];
@@ -134,20 +134,21 @@ __device__ void router_rows4(int e0, int t0, const uint16_t* __restrict__ x, int
       const int64_t o = (int64_t)(t0 + t) * n_routed + e;
       logits[o] = lg;
       if (logits_out) logits_out[o] = lg;
-      scores[o] = score_of(lg, temp);
+      scores[o] = score_mode_of(lg, temp, st);
     }
   }
 }
 
 __global__ __launch_bounds__(256) void k_router_pf(const uint16_t* __restrict__ x, int m, int dim,
                                                    const uint16_t* __restrict__ gate_w, int n_routed, float temp,
-                                                   int router_blocks, Ws w, float* __restrict__ logits_out) {
+                                                   int router_blocks, Ws w, float* __restrict__ logits_out,
+                                                   ScoreTable st) {
   const int bx = blockIdx.x;
   if (bx == 0 && blockIdx.y == 0 && threadIdx.x < 4) w.status[threadIdx.x] = 0;   // every entry point starts here
   if (bx < router_blocks) {
     const int e0 = (4 * bx + (threadIdx.x >> 6)) * kRpRows;
     if (e0 < n_routed)
-      router_rows4(e0, kRpTok * blockIdx.y, x, m, dim, gate_w, n_routed, temp, w.logits, w.scores, logits_out);
+      router_rows4(e0, kRpTok * blockIdx.y, x, m, dim, gate_w, n_routed, temp, w.logits, w.scores, logits_out, st);
     return;
   }
   const int qb = (bx - router_blocks) * gridDim.y + blockIdx.y;
@@ -935,7 +936,7 @@ hipError_t launch_router_pf(const uint16_t* x, int m, const uint16_t* gate_w, co
   const int64_t quant = (int64_t)m * c.dim / 256;
   const int quant_cols = (int)((quant + tgroups - 1) / tgroups);
   MOE_LAUNCH(MOE_K_ROUTER, k_router_pf, dim3(router_blocks + quant_cols, tgroups), dim3(256), 0, s, x, m, c.dim,
-             gate_w, c.n_routed, c.gate_temp, router_blocks, w, logits_out);
+             gate_w, c.n_routed, c.gate_temp, router_blocks, w, logits_out, score_table_for(c));
   return hipGetLastError();
 }
 

@@ -179,6 +179,7 @@ struct FrontArgs {
   float* logits_out;
   int router_blocks, shared_blocks;
   int shq;   // the plan gets the layer's quantised shared expert (id n_routed) for every token
+  ScoreTable st;   // the glibc score mode's table (keys nullptr: correctly rounded scores)
 };
 
 // Every token's selection and the plan [moe_v41.rs, fn route_from_logits;
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a, Ws w) {
   int blk = blockIdx.x;
   if (blk == 0 && threadIdx.x < 4) w.status[threadIdx.x] = 0;   // every entry point starts here
   if (blk < a.router_blocks) {
-    router_rows(blk, a.x, a.m, a.dim, a.gate_w, a.n_routed, a.temp, w.logits, w.scores, a.logits_out);
+    router_rows(blk, a.x, a.m, a.dim, a.gate_w, a.n_routed, a.temp, w.logits, w.scores, a.logits_out, a.st);
     if (!a.bias) return;
     // Count this workgroup's rows as done; the last of the router workgroups
     // selects. Each wave completes its stores, then one release (one L2
@@ -287,9 +288,9 @@ __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ h
 }
 
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, int64_t n, float temp,
-                                                float* __restrict__ out, int force_slow) {
+                                                float* __restrict__ out, int force_slow, ScoreTable st) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = score_of(lg[i], temp, force_slow != 0);
+  if (i < n) out[i] = st.keys ? score_mode_of(lg[i], temp, st) : score_of(lg[i], temp, force_slow != 0);
 }
 
 }  // namespace
@@ -316,6 +317,7 @@ hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const 
   a.router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
   a.shared_blocks = w1 ? (c.inter + 3) / 4 : 0;
   a.shq = sel ? sel->shq : 0;
+  a.st = score_table_for(c);
   const int quant_blocks = (int)((int64_t)m * c.dim / 256);
   MOE_LAUNCH(MOE_K_ROUTER, k_front, dim3(a.router_blocks + a.shared_blocks + quant_blocks), dim3(256), 0, s, a, w);
   return hipGetLastError();
@@ -348,7 +350,11 @@ hipError_t launch_quant_x(const uint16_t* x, int m, const moe_cfg& c, const Ws& 
 
 hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out, int flags, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_scores, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, logits, n, temp, out, flags & 1);
+  moe_cfg glibc{};
+  glibc.score_mode = MOE_SCORE_GLIBC;
+  const ScoreTable st = (flags & 2) ? score_table_for(glibc) : ScoreTable{nullptr, nullptr, nullptr};
+  hipLaunchKernelGGL(k_scores, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, logits, n, temp, out, flags & 1,
+                     st);
   return hipGetLastError();
 }
 

@@ -223,6 +223,7 @@ class Shape:
     route_scale: float = 2.5
     swiglu_limit: float = 7.0
     norm_topk_prob: bool = True
+    score_mode: int = 0          # 0: correctly rounded scores, 1: the host glibc's
 
     @property
     def gate_rows(self) -> int:
