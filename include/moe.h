@@ -17,13 +17,16 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller. The
  *     library allocates no memory on these paths and keeps no state between
- *     calls beyond what the caller's workspace holds. The prefill calls
- *     (m > 8) create, on their first use on a device, one non-blocking
- *     stream and three events of the library's own, kept until the process
- *     ends: part of their work runs there, forked from and joined back into
- *     `stream` by event record/wait pairs before the call's last launch, so
- *     to the caller all of it is ordered on `stream` (a graph capture of
- *     `stream` takes it in). The enqueue holds a per-device lock.
+ *     calls beyond what the caller's workspace holds, with two exceptions:
+ *     the glibc score mode's registered table (moe_set_score_table), and
+ *     the prefill of a layer with a bf16 shared expert (moe_layer_forward
+ *     and moe_stack_forward at m > 8), which creates, on its first use on a
+ *     device, one non-blocking stream and two events of the library's own,
+ *     kept until the process ends: the shared expert's GEMMs run there,
+ *     forked from and joined back into `stream` by event record/wait pairs
+ *     before the call's last launch, so to the caller all of it is ordered
+ *     on `stream` (a graph capture of `stream` takes it in). That enqueue
+ *     holds a per-device lock. Every other call runs on `stream` alone.
  *   - bf16 and fp16 values are passed as their uint16_t bit patterns.
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *     enqueues work and returns; nothing synchronises. Errors found on

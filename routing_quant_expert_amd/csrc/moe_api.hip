@@ -60,20 +60,24 @@ namespace {
 
 bool pow2_upto16(int v) { return v >= 1 && v <= 16 && (v & (v - 1)) == 0; }
 
-// Prefill runs its independent launches on a second stream of the device
-// (created on first use, default priority, never destroyed): the shared
-// expert's two GEMMs from the start of the call (they need only x), the
-// expert kernels of the experts with more than 8 pairs once the grouping is
-// done; the caller's stream waits for them before the combine. The fork and
-// join are event record/wait pairs, so a graph capture of the caller's
-// stream takes the second stream's work in as well. A call holds the
-// device's lock while it enqueues (the launches are asynchronous, so only
-// for the enqueue), so that calls from several host threads cannot
-// interleave their record/wait pairs on the shared events; their side work
-// runs in the order the calls took the lock.
+// A prefill layer with a bf16 shared expert runs that expert's two GEMMs on
+// a second stream of the device (created on first use, default priority,
+// never destroyed), from the start of the call (they need only x), beside
+// the router and the routed experts; the caller's stream waits for them
+// before the combine. The fork and join are event record/wait pairs, so a
+// graph capture of the caller's stream takes the second stream's work in as
+// well. A call holds the device's lock while it enqueues (the launches are
+// asynchronous, so only for the enqueue), so that calls from several host
+// threads cannot interleave their record/wait pairs on the shared events;
+// their side work runs in the order the calls took the lock. Everything else
+// runs on the caller's stream alone (moe_experts_prefill and layers with a
+// K-quant shared expert use no library stream): putting the routed experts
+// with more than 8 pairs on the second stream as well gained nothing
+// measurable, while the shared GEMMs' overlap with the router saves 2 to 5%
+// of a prefill step.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t start = nullptr, plan = nullptr, done = nullptr;
+  hipEvent_t start = nullptr, done = nullptr;
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
@@ -90,7 +94,6 @@ const SideStream* side_stream(std::unique_lock<std::mutex>& hold) {
     SideStream n;
     if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
     if (hipEventCreateWithFlags(&n.start, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.plan, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&n.done, hipEventDisableTiming) != hipSuccess)
       return nullptr;
     ss = n;
@@ -287,6 +290,17 @@ int check_layer(const moe_layer* layer, bool need_experts) {
 
 bool shared_bf16(const moe_layer& layer) { return layer.shared_kind == MOE_SHARED_BF16; }
 
+// The prefill expert stage on `s`: gate/up and down of the experts with more
+// than 8 pairs, then of the others.
+hipError_t prefill_expert_launches(const XArena& ar, int m, const moe_cfg& c, const Ws& w, hipStream_t s) {
+  hipError_t e;
+  for (int part = 1; part >= 0; --part) {
+    if ((e = launch_gateup_pf(ar, m, c, w, part, s)) != hipSuccess) return e;
+    if ((e = launch_down_pf(ar, m, c, w, part, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 XArena layer_arena(const moe_cfg& c, const moe_layer& layer) {
   return arena_of(layer.experts, c.n_routed, shared_bf16(layer) ? nullptr : &layer.shared_q);
 }
@@ -301,24 +315,17 @@ int layer_launches(const moe_cfg& c, const moe_layer& layer, const uint16_t* x, 
   FrontSelect sel{layer.bias, hdr, shq};
   if (m > kMaxDecodeTokens) {   // prefill
     std::unique_lock<std::mutex> hold;
-    const SideStream* ss = side_stream(hold);
-    if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
-    // (inter = 256: one down kernel takes every expert, so both gate/up parts stay on the caller's stream)
-    const hipStream_t big = c.inter / 256 > 1 ? ss->s : s;
-    const bool side_used = bf16 || big != s;
+    const SideStream* ss = nullptr;
     if (bf16) {
+      if (!(ss = side_stream(hold))) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
       if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
       if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
     }
     if ((e = launch_router_pf(x, m, layer.gate_w, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "router_pf");
     if ((e = launch_select(layer.bias, m, c, w, hdr, s)) != hipSuccess) return hip_fail(e, "select");
     if ((e = launch_group(hdr, m, c, w, grp, shq, s)) != hipSuccess) return hip_fail(e, "group");
-    if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
-    if ((e = launch_gateup_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
-    if ((e = launch_gateup_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
-    if (side_used && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
+    if ((e = prefill_expert_launches(ar, m, c, w, s)) != hipSuccess) return hip_fail(e, "experts_pf");
+    if (ss && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
     if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
   }
@@ -360,22 +367,16 @@ int layer_launches_hdr(const moe_cfg& c, const moe_layer& layer, const XArena& a
   const int shq = ar.has_shared();
   if (m > kMaxDecodeTokens) {
     std::unique_lock<std::mutex> hold;
-    const SideStream* ss = side_stream(hold);
-    if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
-    const hipStream_t big = c.inter / 256 > 1 ? ss->s : s;
-    const bool side_used = bf16 || big != s;
+    const SideStream* ss = nullptr;
     if (bf16) {
+      if (!(ss = side_stream(hold))) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
       if ((e = fork_join(ss->start, s, ss->s)) != hipSuccess) return hip_fail(e, "fork");
       if ((e = launch_shared_pf(x, m, layer, c, w, ss->s)) != hipSuccess) return hip_fail(e, "shared_pf");
     }
     if ((e = launch_router_pf(x, m, nullptr, c, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
     if ((e = launch_group(header, m, c, w, grp, shq, s)) != hipSuccess) return hip_fail(e, "group");
-    if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
-    if ((e = launch_gateup_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(ar, m, c, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
-    if ((e = launch_gateup_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-    if ((e = launch_down_pf(ar, m, c, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
-    if (side_used && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
+    if ((e = prefill_expert_launches(ar, m, c, w, s)) != hipSuccess) return hip_fail(e, "experts_pf");
+    if (ss && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
     if ((e = launch_combine(m, c, w, bf16 ? w.sd : nullptr, o, s)) != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
   }
@@ -527,20 +528,10 @@ int moe_experts_prefill(const moe_cfg* cfg, const uint16_t* x, int32_t m, const 
   int32_t* grp = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.grp);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  std::unique_lock<std::mutex> hold;
-  const SideStream* ss = side_stream(hold);
-  if (!ss) return fail(MOE_EHIP, "could not create the prefill side stream%s%lld");
   if ((e = launch_router_pf(x, m, nullptr, *cfg, w, nullptr, s)) != hipSuccess) return hip_fail(e, "quant_pf");
   if ((e = launch_group(header, m, *cfg, w, grp, 0, s)) != hipSuccess) return hip_fail(e, "group");
-  // (inter = 256: one down kernel takes every expert, so both gate/up parts stay on the caller's stream)
-  const hipStream_t big = cfg->inter / 256 > 1 ? ss->s : s;
   const XArena ar = arena_of(*experts, cfg->n_routed, nullptr);
-  if (big != s && (e = fork_join(ss->plan, s, big)) != hipSuccess) return hip_fail(e, "fork");
-  if ((e = launch_gateup_pf(ar, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "gateup_pf");
-  if ((e = launch_down_pf(ar, m, *cfg, w, 1, big)) != hipSuccess) return hip_fail(e, "down_pf");
-  if ((e = launch_gateup_pf(ar, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "gateup_pf");
-  if ((e = launch_down_pf(ar, m, *cfg, w, 0, s)) != hipSuccess) return hip_fail(e, "down_pf");
-  if (big != s && (e = fork_join(ss->done, ss->s, s)) != hipSuccess) return hip_fail(e, "join");
+  if ((e = prefill_expert_launches(ar, m, *cfg, w, s)) != hipSuccess) return hip_fail(e, "experts_pf");
   if ((e = launch_combine(m, *cfg, w, nullptr, LayerOut{y_routed, nullptr, nullptr, nullptr}, s)) != hipSuccess)
     return hip_fail(e, "combine");
   return MOE_OK;
