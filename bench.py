@@ -416,9 +416,9 @@ def prefill_bench(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     k_ms = {k: np.array([ev.elapsed_ms(evs[k][2 * j], evs[k][2 * j + 1]) for j in range(nt)]) for k, _ in kinds}
-    # the expert stage: its four launches run on two streams (the experts with at most 8 pairs on the caller's,
-    # the others on the library's second stream), so its time is the span from the first launch's start to the
-    # last one's end, each taken against the router's start in the same step
+    # the expert stage: its four launches (the experts with more than 8 pairs, then the others, on the caller's
+    # stream), timed as the span from the first launch's start to the last one's end, each taken against the
+    # router's start in the same step
     def at(k, j, end):
         return ev.elapsed_ms(evs["router"][2 * j], evs[k][2 * j + end])
     span_ms = np.array([max(at(k, j, 1) for k in ("gateup", "gateup2", "down", "down2")) -
@@ -475,7 +475,7 @@ def prefill_bench(args):
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("expert stage", "hbm_traffic_prefill_m512_dim4096.md",
                                                  PREFILL_SOURCES) if m == 512 and not shq else None,
-                     "kernel": "expert stage (k_gateup_pf_small, k_gateup_pf, k_down_pf_small, k_down_pf on two streams)",
+                     "kernel": "expert stage (k_gateup_pf, k_down_pf, k_gateup_pf_small, k_down_pf_small)",
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
                      "launch_p10_p90_us": [float(np.percentile(span_ms, 10) * 1e3),
                                            float(np.percentile(span_ms, 90) * 1e3)],
@@ -484,7 +484,8 @@ def prefill_bench(args):
                    "largest_group": int(counts.max()),
                    "step_weight_bytes": step_bytes, "step_gbs": step_bytes / (wall / K) / 1e9,
                    "kernel_us_sum": sum(us.values()), "expert_stage_us": k_avg * 1e6,
-                   "note": "kernels on the two streams overlap: the per-kernel times include the sharing"},
+                   "note": "the bf16 shared expert's GEMMs run on a second stream beside the router and selection: "
+                           "their times include that sharing"},
     }
     if not args.no_cpu:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
@@ -707,7 +708,9 @@ def main():
                    "expert_arena_bytes": s.n_routed * s.expert_stride, "seed": args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (None if shq else measured_traffic(kernel) if m == 1 else
+                     "traffic": (None if glibc else
+                                 measured_traffic(kernel, "hbm_traffic_decode_m1_shared_kquant_dim4096.md")
+                                 if shq and m == 1 else None if shq else measured_traffic(kernel) if m == 1 else
                                  measured_traffic(kernel, "hbm_traffic_decode_m8_dim4096.md", UNION_SOURCES) if m == 8
                                  else None), "kernel": kernel,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": k_avg * 1e6, "timed_launches": int(nt),
