@@ -158,3 +158,15 @@ def test_mode_checked():
     p = ctypes.c_void_p(buf.ctypes.data)
     rc = R.lib().moe_route_select(ctypes.byref(c), p, 1, p, p, None, p, p, buf.size, None)
     assert rc != 0 and "moe_set_score_table" in R.lib().moe_last_error().decode()
+
+
+def test_table_call_checked(table):
+    """The table call reports the count with keys = NULL and refuses a
+    buffer smaller than the count."""
+    n = ctypes.c_int64(0)
+    assert R.lib().moe_glibc_score_table(None, None, None, 0, ctypes.byref(n)) == 0 and n.value == table[0].size
+    small = np.empty(4, np.uint32)
+    idx = np.empty(R.binding.SCORE_INDEX_LEN, np.uint32)
+    rc = R.lib().moe_glibc_score_table(small.ctypes.data, small.ctypes.data, idx.ctypes.data, 4, ctypes.byref(n))
+    assert rc != 0 and "cap" in R.lib().moe_last_error().decode()
+    assert R.lib().moe_glibc_score_table(None, None, None, 0, None) != 0
