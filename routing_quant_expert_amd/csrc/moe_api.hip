@@ -579,6 +579,11 @@ int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_lay
 
 int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream) {
   if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
+  if (flags & 2) {
+    moe_cfg glibc{};
+    glibc.score_mode = MOE_SCORE_GLIBC;
+    if (int r = check_score_mode(glibc)) return r;
+  }
   hipError_t e = launch_scores(logits, n, temp, out, flags, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "scores");
 }

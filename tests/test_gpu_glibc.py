@@ -71,6 +71,8 @@ def test_unregistered_device_refuses(table):
     assert L.moe_set_score_table(None, None, None, 0) == 0
     try:
         with pytest.raises(R.MoeError, match="moe_set_score_table"):
+            _dev_scores(np.zeros(8, np.float32), 1.0, 2)
+        with pytest.raises(R.MoeError, match="moe_set_score_table"):
             x = torch.zeros((1, 512), dtype=torch.uint16, device="cuda")
             gw = torch.zeros((384, 512), dtype=torch.uint16, device="cuda")
             b = torch.zeros(384, dtype=torch.float32, device="cuda")
@@ -203,3 +205,35 @@ def test_full_size_tokens(table, m):
         assert np.array_equal(got[2], want[2])
         for t in range(m):
             assert rel_l2(got[1][t], want[1][t]) <= 1e-3, t
+
+
+def test_expert_cache_routes_in_glibc_mode(table):
+    """The expert cache's routing (against the slot table) in the glibc
+    mode: the first layer's picks and weights equal the oracle's glibc-mode
+    selection on crafted exact logits (and differ from the correctly rounded
+    mode's), and every layer's results equal the resident stack's in the
+    same mode, bit for bit."""
+    from tests.test_gpu_cache import Stack, _run, _same_as_resident
+    sh = synth.SHAPE_TINY
+    stk = Stack(2, seed=43)
+    stk.cfg.score_mode = R.MOE_SCORE_GLIBC
+    m = 1
+    x, gw = _crafted(table, sh, m)
+    bias = np.zeros(sh.n_routed, np.float32)
+    # the first layer gets the crafted router and no bias (gwd and bd stay referenced until the end)
+    gwd, bd = torch.from_numpy(gw.view(np.int16)).cuda(), torch.from_numpy(bias).cuda()
+    L = R.Layer.from_buffer_copy(stk.layers[0])
+    L.gate_w, L.bias = gwd.data_ptr(), bd.data_ptr()
+    stk.layers[0] = L
+    ref = _run(stk, x)
+    cache = stk.cache(n_slots=16, max_m=m)
+    try:
+        got = _run(stk, x, cache=cache)
+    finally:
+        cache.close()
+    _same_as_resident(ref, got, sh.topk)
+    k = sh.topk
+    _, rh = oracle.ref_route_select(glibc(sh), x, gw, bias)
+    _, h0 = oracle.ref_route_select(sh, x, gw, bias)
+    assert np.array_equal(got[2][0][:, 1:1 + 2 * k], rh[:, 1:1 + 2 * k])
+    assert not np.array_equal(got[2][0][:, 1 + k:1 + 2 * k], h0[:, 1 + k:1 + 2 * k])
