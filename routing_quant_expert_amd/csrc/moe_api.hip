@@ -591,9 +591,11 @@ int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t f
 int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags) {
   if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
   if (flags & 2) {
-    const ScoreTable t = host_score_table();
-    for (int64_t i = 0; i < n; ++i) out[i] = score_mode_of(logits[i], temp, t);
-    return MOE_OK;
+    return guarded([&] {
+      const ScoreTable t = host_score_table();
+      for (int64_t i = 0; i < n; ++i) out[i] = score_mode_of(logits[i], temp, t);
+      return MOE_OK;
+    });
   }
   for (int64_t i = 0; i < n; ++i) out[i] = score_of(logits[i], temp, (flags & 1) != 0);
   return MOE_OK;

@@ -223,7 +223,7 @@ int fetch(moe_cache* c, const std::vector<int64_t>& keys, uint64_t protect_from,
 
 extern "C" {
 
-int moe_cache_create(const moe_cfg* cfg, int32_t n_layers, const void* const* host_experts, uint64_t stride,
+static int moe_cache_create_body(const moe_cfg* cfg, int32_t n_layers, const void* const* host_experts, uint64_t stride,
                      uint64_t gate_off, uint64_t up_off, uint64_t down_off, int32_t n_slots, int32_t max_m,
                      moe_cache** out) {
   if (int r = check_cfg(cfg)) return r;
@@ -277,7 +277,7 @@ int moe_cache_destroy(moe_cache* cache) {
   return MOE_OK;
 }
 
-int moe_cache_forward(moe_cache* cache, const moe_cfg* cfg, const moe_layer* layers, int32_t first_layer,
+static int moe_cache_forward_body(moe_cache* cache, const moe_cfg* cfg, const moe_layer* layers, int32_t first_layer,
                       int32_t n_layers, uint16_t* xs, int32_t m, float* out_f32, int32_t* headers, int32_t prefetch_k,
                       void* ws, size_t ws_bytes, void* stream) {
   if (!cache) return fail(MOE_EINVAL, "expert cache is NULL%s%lld");
@@ -375,7 +375,7 @@ int moe_cache_forward(moe_cache* cache, const moe_cfg* cfg, const moe_layer* lay
   return MOE_OK;
 }
 
-int moe_cache_prefetch(moe_cache* cache, int32_t layer, const int32_t* experts, int32_t n, void* stream) {
+static int moe_cache_prefetch_body(moe_cache* cache, int32_t layer, const int32_t* experts, int32_t n, void* stream) {
   if (!cache || (n > 0 && !experts)) return fail(MOE_EINVAL, "expert cache and experts must be non-NULL%s%lld");
   moe_cache* c = cache;
   if (layer < 0 || layer >= c->n_layers) return fail(MOE_EINVAL, "expert cache: layer outside the cache%s (%lld)", "", layer);
@@ -407,7 +407,7 @@ int moe_cache_resident(const moe_cache* cache, int32_t layer, int32_t* slots) {
   return MOE_OK;
 }
 
-int moe_lru_simulate(int32_t n_slots, int64_t n_keys, const int64_t* keys, const int32_t* batch_len,
+static int moe_lru_simulate_body(int32_t n_slots, int64_t n_keys, const int64_t* keys, const int32_t* batch_len,
                      int32_t n_batches, int32_t* slots_out, int32_t* miss_out) {
   if (n_slots < 1 || n_keys < 1 || n_batches < 0 || (n_batches > 0 && (!keys || !batch_len || !slots_out || !miss_out)))
     return fail(MOE_EINVAL, "bad LRU simulation arguments%s%lld");
@@ -429,6 +429,35 @@ int moe_lru_simulate(int32_t n_slots, int64_t n_keys, const int64_t* keys, const
     }
   }
   return MOE_OK;
+}
+
+int moe_cache_create(const moe_cfg* cfg, int32_t n_layers, const void* const* host_experts, uint64_t stride,
+                     uint64_t gate_off, uint64_t up_off, uint64_t down_off, int32_t n_slots, int32_t max_m,
+                     moe_cache** out) {
+  return guarded([&] {
+    return moe_cache_create_body(cfg, n_layers, host_experts, stride, gate_off, up_off, down_off, n_slots, max_m,
+                                 out);
+  });
+}
+
+int moe_cache_forward(moe_cache* cache, const moe_cfg* cfg, const moe_layer* layers, int32_t first_layer,
+                      int32_t n_layers, uint16_t* xs, int32_t m, float* out_f32, int32_t* headers, int32_t prefetch_k,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    return moe_cache_forward_body(cache, cfg, layers, first_layer, n_layers, xs, m, out_f32, headers, prefetch_k, ws,
+                                  ws_bytes, stream);
+  });
+}
+
+int moe_cache_prefetch(moe_cache* cache, int32_t layer, const int32_t* experts, int32_t n, void* stream) {
+  return guarded([&] { return moe_cache_prefetch_body(cache, layer, experts, n, stream); });
+}
+
+int moe_lru_simulate(int32_t n_slots, int64_t n_keys, const int64_t* keys, const int32_t* batch_len,
+                     int32_t n_batches, int32_t* slots_out, int32_t* miss_out) {
+  return guarded([&] {
+    return moe_lru_simulate_body(n_slots, n_keys, keys, batch_len, n_batches, slots_out, miss_out);
+  });
 }
 
 }  // extern "C"

@@ -122,7 +122,7 @@ using namespace moe;
 
 extern "C" {
 
-int moe_glibc_score_table(uint32_t* keys, uint32_t* vals, uint32_t* index, int64_t cap, int64_t* n) {
+static int moe_glibc_score_table_body(uint32_t* keys, uint32_t* vals, uint32_t* index, int64_t cap, int64_t* n) {
   if (!n) return fail(MOE_EINVAL, "n is NULL%s%lld");
   std::call_once(g_host_once, build_host_table);
   const int64_t total = (int64_t)g_host->keys.size();
@@ -147,6 +147,10 @@ int moe_set_score_table(const uint32_t* keys, const uint32_t* vals, const uint32
   std::lock_guard<std::mutex> lk(g_reg_mu);
   g_reg[dev] = keys ? ScoreTable{keys, vals, index} : ScoreTable{nullptr, nullptr, nullptr};
   return MOE_OK;
+}
+
+int moe_glibc_score_table(uint32_t* keys, uint32_t* vals, uint32_t* index, int64_t cap, int64_t* n) {
+  return guarded([&] { return moe_glibc_score_table_body(keys, vals, index, cap, n); });
 }
 
 }  // extern "C"
