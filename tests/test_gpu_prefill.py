@@ -383,3 +383,60 @@ def test_prefill_graph_capture_replays_equal_eager():
         torch.cuda.synchronize()
         assert torch.equal(out32.view(torch.int32), ref32.view(torch.int32)), rep
         assert torch.equal(hdr, refh), rep
+
+
+def _device_tokens(spec, m):
+    """Input rows 0..m-1 of the layer's token recipe, generated on the device
+    (the same bits as synth.tokens, one seeded stream per row)."""
+    from synth.device import normal_bf16_into
+    x = torch.empty((m, spec.shape.dim), dtype=torch.uint16, device="cuda")
+    for t in range(m):
+        normal_bf16_into(x[t], spec.seed, synth.make_tag(synth.K_X, spec.layer, t), synth.SIGMA_X)
+    torch.cuda.synchronize()
+    return x
+
+
+@pytest.mark.parametrize("shape,shared_quant", [(DS41, False), (TINY, True)],
+                         ids=lambda v: f"dim{v.dim}" if hasattr(v, "dim") else f"kquant{int(v)}")
+def test_prefill_maximum_token_count(shape, shared_quant):
+    """The largest accepted batch, 65535 tokens (the combine's grid rows;
+    at dim 4096 the prefill kernels' 32-bit offsets reach 1.9e9), through
+    moe_layer_forward: every header valid (picks distinct and in range,
+    ascending plan, weights summing to route_scale), every bf16 output the
+    rounding of its f32 output, and sampled tokens across the batch (both
+    ends included) bit-exact in the header and within tolerance in the output
+    against the oracle."""
+    m = 65535
+    if shape == DS41:
+        dl = dev_layer(DS41, zipf=True)
+    else:
+        dl = DeviceLayer(synth.LayerSpec(shape, seed=9, zipf_bias=True, shared_quant=shared_quant))
+    spec, c = dl.spec, dl.cfg
+    k = shape.topk
+    say(f"prefill at the maximum token count: dim {shape.dim}, m={m}, shared_quant={shared_quant}")
+    x = _device_tokens(spec, m)
+    ws = workspace(c, m)
+    out = torch.empty((m, shape.dim), dtype=torch.uint16, device="cuda")
+    out32 = torch.empty((m, shape.dim), dtype=torch.float32, device="cuda")
+    hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+    R.layer_forward(c, dl.layer, x, out, ws, out_f32=out32, header=hdr)
+    torch.cuda.synchronize()
+    del ws
+    h = hdr.cpu().numpy()
+    st, picks, wts, plan = oracle.header_fields(h, k)
+    assert np.all(st == 0)
+    assert np.all((picks >= 0) & (picks < shape.n_routed))
+    assert np.all(np.sort(picks, axis=1) == plan) and np.all(np.diff(plan, axis=1) > 0)
+    assert np.all(np.abs(wts.astype(np.float64).sum(axis=1) - shape.route_scale) <= 1e-5)
+    for t0 in range(0, m, 8192):   # the bf16 output is the rounding of the f32 output, every token
+        o32 = out32[t0:t0 + 8192].cpu().numpy()
+        assert np.all(np.isfinite(o32))
+        assert np.array_equal(to_np_u16(out[t0:t0 + 8192]), oracle.f32_to_bf16(o32))
+    toks = [0, 1, 4097, 32767, 65533, 65534]
+    x_np = np.concatenate([synth.tokens(spec, t, 1) for t in toks])
+    assert np.array_equal(to_np_u16(x.view(torch.int16)[toks]), x_np)
+    ref = olayer.layer_forward(spec, x_np)
+    o32 = out32[toks].cpu().numpy()
+    for i, t in enumerate(toks):
+        assert np.array_equal(h[t], ref["header"][i]), t
+        assert rel_l2(o32[i], ref["out_f32"][i]) <= 1e-3 and np.abs(o32[i] - ref["out_f32"][i]).max() <= 1e-2, t
