@@ -376,7 +376,12 @@ def prefill_bench(args):
     dl = DeviceLayer(spec)
     glibc = use_score_mode(args, dl)
     nb = max(1, min(args.tokens, 4))   # distinct batches cycled through
-    xs = torch.from_numpy(synth.tokens(spec, 0, nb * m)).cuda()
+    if nb * m <= 4096:
+        xs = torch.from_numpy(synth.tokens(spec, 0, nb * m)).cuda()
+    else:   # large batches: the same rows generated on the device
+        from synth.device import tokens_into
+        xs = torch.empty((nb * m, s.dim), dtype=torch.uint16, device="cuda")
+        tokens_into(spec, xs)
     ws = torch.empty(R.workspace_bytes(dl.cfg, m), dtype=torch.uint8, device="cuda")
     R.workspace_init(dl.cfg, m, ws)
     out = torch.empty((m, s.dim), dtype=torch.uint16, device="cuda")

@@ -7,8 +7,8 @@ import os
 
 import numpy as np
 
-from . import (K_EXP_DOWN, K_EXP_GATE, K_EXP_UP, K_GATE_W, K_SH_W1, K_SH_W2, K_SH_W3, Q2K_BYTES, Q3K_BYTES,
-               SIGMA_W, LayerSpec, bias, gate_w, shared_w, tokens)
+from . import (K_EXP_DOWN, K_EXP_GATE, K_EXP_UP, K_GATE_W, K_SH_W1, K_SH_W2, K_SH_W3, K_X, Q2K_BYTES, Q3K_BYTES,
+               SIGMA_W, SIGMA_X, LayerSpec, bias, gate_w, make_tag, shared_w, tokens)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsynth.so")
@@ -58,6 +58,13 @@ def fill_arena(spec: LayerSpec, arena, experts=None):
 
 def normal_bf16_into(t, seed: int, tag: int, sigma: float, i0: int = 0):
     _ok(lib().synth_normal_bf16(t.data_ptr(), seed, tag, i0, t.numel(), sigma, _stream()))
+
+
+def tokens_into(spec: LayerSpec, x, t0: int = 0):
+    """Input rows t0.. of the token recipe into the device tensor x [m, dim]
+    (the same bits as synth.tokens, one seeded stream per row)."""
+    for i in range(x.shape[0]):
+        normal_bf16_into(x[i], spec.seed, make_tag(K_X, spec.layer, t0 + i), SIGMA_X)
 
 
 def fill_expert(spec: LayerSpec, buf, e: int):

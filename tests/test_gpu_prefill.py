@@ -386,12 +386,10 @@ def test_prefill_graph_capture_replays_equal_eager():
 
 
 def _device_tokens(spec, m):
-    """Input rows 0..m-1 of the layer's token recipe, generated on the device
-    (the same bits as synth.tokens, one seeded stream per row)."""
-    from synth.device import normal_bf16_into
+    """Input rows 0..m-1 of the layer's token recipe, generated on the device."""
+    from synth.device import tokens_into
     x = torch.empty((m, spec.shape.dim), dtype=torch.uint16, device="cuda")
-    for t in range(m):
-        normal_bf16_into(x[t], spec.seed, synth.make_tag(synth.K_X, spec.layer, t), synth.SIGMA_X)
+    tokens_into(spec, x)
     torch.cuda.synchronize()
     return x
 
