@@ -7,6 +7,7 @@
 #include <mutex>
 #include <string>
 
+#include "moe_host.h"
 #include "moe_internal.h"
 #include "moe_math.h"
 #include "moe_prefill.h"

@@ -27,6 +27,7 @@
 #include <cstring>
 #include <vector>
 
+#include "moe_host.h"
 #include "moe_internal.h"
 
 struct moe_cache;

@@ -7,8 +7,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <new>
-
 #include "../../include/moe.h"
 #include "moe_math.h"
 
@@ -171,18 +169,6 @@ ScoreTable host_score_table();
 
 // ---- argument checks and the error message (moe_api.hip) ----
 int fail(int code, const char* fmt, const char* a = "", long long b = 0);   // fmt takes a %s then a %lld
-// Runs a host-side entry-point body that allocates host memory, turning a C++
-// exception into an error code (nothing may unwind through the C ABI).
-template <class F>
-int guarded(F&& body) {
-  try {
-    return body();
-  } catch (const std::bad_alloc&) {
-    return fail(MOE_EUNSUPPORTED, "host memory exhausted%s%lld");
-  } catch (...) {
-    return fail(MOE_EINVAL, "unexpected host-side error%s%lld");
-  }
-}
 int hip_fail(hipError_t e, const char* where);
 int check_cfg(const moe_cfg* c);
 int check_m(const moe_cfg& c, int64_t m);

@@ -15,6 +15,7 @@
 #include <thread>
 #include <vector>
 
+#include "moe_host.h"
 #include "moe_internal.h"
 
 namespace moe {
