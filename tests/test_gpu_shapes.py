@@ -62,19 +62,23 @@ def test_layer_forward_other_widths(shape):
 ROUTING = [dict(n_routed=100, topk=1, norm_topk_prob=False), dict(n_routed=100, topk=8, norm_topk_prob=True),
            dict(n_routed=1024, topk=8, norm_topk_prob=False), dict(n_routed=1024, topk=5, norm_topk_prob=True),
            dict(n_routed=64, topk=2, norm_topk_prob=True)]
+# the K-quant shared expert at the ends of the topk range: topk 8 gives 9 plan entries per token
+ROUTING_KQ = [dict(n_routed=100, topk=8, norm_topk_prob=True), dict(n_routed=1024, topk=1, norm_topk_prob=False)]
 
 
-@pytest.mark.parametrize("routing", ROUTING, ids=lambda r: f"e{r['n_routed']}_k{r['topk']}_n{int(r['norm_topk_prob'])}")
-def test_layer_forward_other_routing_configs(routing):
+@pytest.mark.parametrize("routing,shared_quant", [(r, False) for r in ROUTING] + [(r, True) for r in ROUTING_KQ],
+                         ids=lambda v: (f"e{v['n_routed']}_k{v['topk']}_n{int(v['norm_topk_prob'])}"
+                                        if isinstance(v, dict) else ("kquant" if v else "bf16")))
+def test_layer_forward_other_routing_configs(routing, shared_quant):
     """The rest of the supported routing set at dim 512: n_routed not a
     multiple of 64 and up to 1024 (the 16-key-per-lane selection), topk 1
     and 8 (topk above 6 takes the multi-token kernels at m = 1, with 64 pairs
-    at m = 8), unnormalised weights; m = 1, 8 and 40, every token against the
-    oracle."""
+    at m = 8), unnormalised weights, and the K-quant shared expert at topk 8
+    and 1; m = 1, 8 and 40, every token against the oracle."""
     import dataclasses
     shape = dataclasses.replace(synth.SHAPE_TINY, **routing)
-    spec = synth.LayerSpec(shape, seed=8)
-    say(f"generating layer e{shape.n_routed} k{shape.topk} norm {shape.norm_topk_prob}")
+    spec = synth.LayerSpec(shape, seed=8, shared_quant=shared_quant)
+    say(f"generating layer e{shape.n_routed} k{shape.topk} norm {shape.norm_topk_prob} shared_quant {shared_quant}")
     dl = DeviceLayer(spec)
     c = dl.cfg
     try:
