@@ -224,9 +224,9 @@ int fetch(moe_cache* c, const std::vector<int64_t>& keys, uint64_t protect_from,
 
 extern "C" {
 
-static int moe_cache_create_body(const moe_cfg* cfg, int32_t n_layers, const void* const* host_experts, uint64_t stride,
-                     uint64_t gate_off, uint64_t up_off, uint64_t down_off, int32_t n_slots, int32_t max_m,
-                     moe_cache** out) {
+static int moe_cache_create_body(const moe_cfg* cfg, int32_t n_layers, const void* const* host_experts,
+                                 uint64_t stride, uint64_t gate_off, uint64_t up_off, uint64_t down_off,
+                                 int32_t n_slots, int32_t max_m, moe_cache** out) {
   if (int r = check_cfg(cfg)) return r;
   if (!out || !host_experts || n_layers < 1 || n_slots < 1)
     return fail(MOE_EINVAL, "expert cache: out, host_experts non-NULL, n_layers >= 1, n_slots >= 1%s%lld");
@@ -279,8 +279,8 @@ int moe_cache_destroy(moe_cache* cache) {
 }
 
 static int moe_cache_forward_body(moe_cache* cache, const moe_cfg* cfg, const moe_layer* layers, int32_t first_layer,
-                      int32_t n_layers, uint16_t* xs, int32_t m, float* out_f32, int32_t* headers, int32_t prefetch_k,
-                      void* ws, size_t ws_bytes, void* stream) {
+                                  int32_t n_layers, uint16_t* xs, int32_t m, float* out_f32, int32_t* headers,
+                                  int32_t prefetch_k, void* ws, size_t ws_bytes, void* stream) {
   if (!cache) return fail(MOE_EINVAL, "expert cache is NULL%s%lld");
   if (int r = check_cfg(cfg)) return r;
   if (int r = check_score_mode(*cfg)) return r;
@@ -409,7 +409,7 @@ int moe_cache_resident(const moe_cache* cache, int32_t layer, int32_t* slots) {
 }
 
 static int moe_lru_simulate_body(int32_t n_slots, int64_t n_keys, const int64_t* keys, const int32_t* batch_len,
-                     int32_t n_batches, int32_t* slots_out, int32_t* miss_out) {
+                                 int32_t n_batches, int32_t* slots_out, int32_t* miss_out) {
   if (n_slots < 1 || n_keys < 1 || n_batches < 0 || (n_batches > 0 && (!keys || !batch_len || !slots_out || !miss_out)))
     return fail(MOE_EINVAL, "bad LRU simulation arguments%s%lld");
   SlotLru lru(n_slots, n_keys);
