@@ -362,22 +362,26 @@ int moe_lru_simulate(int32_t n_slots, int64_t n_keys, const int64_t* keys, const
 int moe_glibc_score_table(uint32_t* keys, uint32_t* vals, uint32_t* index, int64_t cap, int64_t* n);
 
 /* Registers the device copies of the glibc score table (keys, vals [n],
- * index [MOE_SCORE_INDEX_LEN], device pointers owned by the caller and kept
- * alive while the mode is used) for the current device; NULL keys
- * unregisters. Calls that route with MOE_SCORE_GLIBC read the registration of
- * the device current when they are made. */
+ * index [MOE_SCORE_INDEX_LEN]: the arrays moe_glibc_score_table returned,
+ * copied unchanged; device pointers owned by the caller and kept alive while
+ * the mode is used) for the current device; NULL keys unregisters. Calls that
+ * route with MOE_SCORE_GLIBC read the registration of the device current when
+ * they are made; the kernels index the table as given, without checks. */
 int moe_set_score_table(const uint32_t* keys, const uint32_t* vals, const uint32_t* index, int64_t n);
 
 /* The score chain of A3 alone on device data: out[i] = sqrt(softplus(
  * logits[i] / temp)) with correctly rounded exp, log1p, division and sqrt
  * [moe_v41.rs, fn softplus, fn route_from_logits]. flags bit 0 forces the
  * extended-precision path of exp/log1p for every element (checking only);
- * flags bit 1 gives the glibc mode's scores (the registered table). */
+ * flags bit 1 gives the glibc mode's scores (the table registered for the
+ * current device; MOE_EINVAL when there is none). */
 int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream);
 
 /* The same score chain computed on the host CPU by the library's own code
  * (the device functions compiled for the host); for checking the library's
- * arithmetic where no GPU is present. All pointers are host pointers. */
+ * arithmetic where no GPU is present. flags as moe_scores (bit 1: the glibc
+ * mode through the host's copy of the table, built on first use). All
+ * pointers are host pointers. */
 int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags);
 
 /* The clamped SwiGLU of the library on the host: out[i] = silu(min(g,L)) *
