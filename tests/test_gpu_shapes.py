@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import routing_quant_expert_amd as R
 import synth
 from oracle import layer as olayer
@@ -114,3 +115,34 @@ def test_layer_forward_other_routing_configs(routing, shared_quant):
     finally:
         del dl
         torch.cuda.empty_cache()
+
+
+def test_route_select_random_configs():
+    """The routing call over seeded random configurations (n_routed 6..1024,
+    topk 1..8, normalised or not, gate_temp and route_scale away from 1 and
+    2.5, dim 256..4096, m 1..80): logits and headers bit for bit against the
+    oracle's mirror of the same call."""
+    import dataclasses
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        topk = int(rng.integers(1, 9))
+        n_routed = int(rng.integers(max(topk, 6), 1025))
+        dim = int(256 * 2 ** rng.integers(0, 5))
+        shape = dataclasses.replace(synth.SHAPE_TINY, dim=dim, n_routed=n_routed, topk=topk,
+                                    norm_topk_prob=bool(rng.integers(0, 2)),
+                                    gate_temp=float(np.float32(rng.uniform(0.3, 3.0))),
+                                    route_scale=float(np.float32(rng.uniform(0.5, 4.0))))
+        m = int(rng.choice([1, 2, 5, 8, 9, 33, 80]))
+        x = oracle.f32_to_bf16(rng.normal(0, 1, (m, dim)).astype(np.float32))
+        gw = oracle.f32_to_bf16(rng.normal(0, 0.05, (n_routed, dim)).astype(np.float32))
+        bias = rng.uniform(-0.2, 0.2, n_routed).astype(np.float32)
+        say(f"case {case}: e{n_routed} k{topk} dim {dim} m {m} temp {shape.gate_temp:.3f}")
+        c = R.cfg_from_shape(shape)
+        lg = torch.empty((m, n_routed), dtype=torch.float32, device="cuda")
+        hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+        R.route_select(c, torch.from_numpy(x.view(np.int16)).cuda(), torch.from_numpy(gw.view(np.int16)).cuda(),
+                       torch.from_numpy(bias).cuda(), hdr, workspace(c, m), logits=lg)
+        torch.cuda.synchronize()
+        rl, rh = oracle.ref_route_select(shape, x, gw, bias)
+        assert np.array_equal(lg.cpu().numpy().view(np.uint32), rl.view(np.uint32)), case
+        assert np.array_equal(hdr.cpu().numpy(), rh), case
