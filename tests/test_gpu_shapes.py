@@ -146,3 +146,45 @@ def test_route_select_random_configs():
         rl, rh = oracle.ref_route_select(shape, x, gw, bias)
         assert np.array_equal(lg.cpu().numpy().view(np.uint32), rl.view(np.uint32)), case
         assert np.array_equal(hdr.cpu().numpy(), rh), case
+
+
+def test_layer_forward_random_configs():
+    """Whole layers over seeded random configurations (experts, topk,
+    normalisation, temperature, route scale, SwiGLU limit, shared expert kind,
+    dim 512 or 1024) at m = 1, 4 and 20 (the single-token, union and prefill
+    paths): headers bit for bit and outputs within rel-L2 1e-3 and max-abs
+    1e-2 against the oracle."""
+    import dataclasses
+    rng = np.random.default_rng(77)
+    for case in range(6):
+        topk = int(rng.integers(1, 9))
+        dim, inter = ((512, 256), (1024, 512))[int(rng.integers(0, 2))]
+        shape = dataclasses.replace(synth.SHAPE_TINY, dim=dim, inter=inter,
+                                    n_routed=int(rng.integers(max(topk, 8), 600)), topk=topk,
+                                    norm_topk_prob=bool(rng.integers(0, 2)),
+                                    gate_temp=float(np.float32(rng.uniform(0.5, 2.0))),
+                                    route_scale=float(np.float32(rng.uniform(0.5, 4.0))),
+                                    swiglu_limit=float(np.float32(rng.uniform(0.5, 10.0))))
+        shared_quant = bool(rng.integers(0, 2))
+        spec = synth.LayerSpec(shape, seed=100 + case, shared_quant=shared_quant)
+        say(f"case {case}: {shape} shared_quant={shared_quant}")
+        dl = DeviceLayer(spec)
+        c = dl.cfg
+        try:
+            for m in (1, 4, 20):
+                x_np = synth.tokens(spec, 7 * m, m)
+                ws = workspace(c, m)
+                out = torch.empty((m, dim), dtype=torch.uint16, device="cuda")
+                out32 = torch.empty((m, dim), dtype=torch.float32, device="cuda")
+                hdr = torch.empty((m, R.header_words(c)), dtype=torch.int32, device="cuda")
+                R.layer_forward(c, dl.layer, torch.from_numpy(x_np).cuda(), out, ws, out_f32=out32, header=hdr)
+                torch.cuda.synchronize()
+                ref = olayer.layer_forward(spec, x_np)
+                assert np.array_equal(hdr.cpu().numpy(), ref["header"]), (case, m)
+                o = out32.cpu().numpy()
+                for t in range(m):
+                    err = np.abs(o[t] - ref["out_f32"][t])
+                    assert rel_l2(o[t], ref["out_f32"][t]) <= 1e-3 and err.max() <= 1e-2, (case, m, t)
+        finally:
+            del dl
+            torch.cuda.empty_cache()
