@@ -300,7 +300,8 @@ __device__ __forceinline__ void dma_wave(const uint8_t* g, uint8_t* dst) {
     const int i = 64 * k + lane;
     const int src = i < NCH ? i : NCH - 1;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * src),
-                                     (__attribute__((address_space(3))) void*)(dst + 16 * 64 * k), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(dst + 16 * 64 * k), 16, 0,
+                                     kWeightStream);
   }
 }
 

@@ -19,6 +19,12 @@ __device__ inline double fp16_f64(uint32_t bits16) {
 __device__ inline uint16_t f32_to_fp16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 // ---- direct-to-LDS staging --------------------------------------------------
+// Cache policy of the weight streams: the nt (non-temporal) bit. Each weight
+// byte is read once per launch; without the bit those lines push the code,
+// the router rows and the activations out of the L2 between launches (a
+// decode step was 2 us slower).
+constexpr int kWeightStream = 2;
+
 // A tile of rows is copied HBM -> LDS with global_load_lds_dwordx4 (no VGPRs,
 // no wait at issue). Workgroups are 256 threads; wave w copies 16-byte chunks
 // w*64 + 256*k + lane (k < KC), so every wave issues exactly KC instructions
@@ -44,7 +50,7 @@ __device__ __forceinline__ void dma_tile(const uint8_t* g, uint8_t* slot, int nc
     const int src = i < nchunks ? i : nchunks - 1;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * src),
                                      (__attribute__((address_space(3))) void*)(slot + 16 * (w * 64 + 256 * k)), 16,
-                                     0, 0);
+                                     0, kWeightStream);
   }
 }
 
@@ -58,7 +64,8 @@ __device__ __forceinline__ void dma_tile_exact(const uint8_t* g, uint8_t* slot, 
   for (int k = 0; k < KC; ++k) {
     const int base = min(w * 64 + 256 * k, nchunks - 64);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * (base + lane)),
-                                     (__attribute__((address_space(3))) void*)(slot + 16 * base), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(slot + 16 * base), 16, 0,
+                                     kWeightStream);
   }
 }
 
