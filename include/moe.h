@@ -374,14 +374,17 @@ int moe_set_score_table(const uint32_t* keys, const uint32_t* vals, const uint32
  * [moe_v41.rs, fn softplus, fn route_from_logits]. flags bit 0 forces the
  * extended-precision path of exp/log1p for every element (checking only);
  * flags bit 1 gives the glibc mode's scores (the table registered for the
- * current device; MOE_EINVAL when there is none). */
+ * current device; MOE_EINVAL when there is none); flags bit 2 returns the
+ * chain's exp step alone, out[i] = RN32(exp(logits[i] / temp)), the function
+ * the SwiGLU also uses (checking only; not with bit 1). Other bits:
+ * MOE_EINVAL. */
 int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream);
 
 /* The same score chain computed on the host CPU by the library's own code
  * (the device functions compiled for the host); for checking the library's
  * arithmetic where no GPU is present. flags as moe_scores (bit 1: the glibc
- * mode through the host's copy of the table, built on first use). All
- * pointers are host pointers. */
+ * mode through the host's copy of the table, built on first use; bit 2: the
+ * exp step alone). All pointers are host pointers. */
 int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags);
 
 /* The clamped SwiGLU of the library on the host: out[i] = silu(min(g,L)) *

@@ -200,6 +200,11 @@ def scores_host(logits: np.ndarray, temp: float, flags: int = 0) -> np.ndarray:
     return out
 
 
+# flag bits of scores / scores_host
+SCORES_EXTENDED = 1   # every exp/log1p through the extended-precision path
+SCORES_GLIBC = 2      # the glibc mode's scores
+SCORES_EXP_ONLY = 4   # the chain's exp step alone
+
 MOE_SCORE_CR = 0
 MOE_SCORE_GLIBC = 1
 SCORE_INDEX_LEN = (1 << 24) + 1

@@ -578,8 +578,17 @@ int moe_stack_forward(const moe_cfg* cfg, const moe_layer* layers, int32_t n_lay
   return MOE_OK;
 }
 
+// The flag bits of moe_scores and moe_scores_host: 0 the extended path, 1
+// the glibc mode, 2 the exp step alone (not with bit 1).
+static int check_score_flags(int32_t flags) {
+  if ((flags & ~7) || ((flags & 4) && (flags & 2)))
+    return fail(MOE_EINVAL, "score flags: bits 0..2, bit 2 not with bit 1 (got %s%lld)", "", (long long)flags);
+  return MOE_OK;
+}
+
 int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t flags, void* stream) {
   if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
+  if (int r = check_score_flags(flags)) return r;
   if (flags & 2) {
     moe_cfg glibc{};
     glibc.score_mode = MOE_SCORE_GLIBC;
@@ -591,6 +600,12 @@ int moe_scores(const float* logits, int64_t n, float temp, float* out, int32_t f
 
 int moe_scores_host(const float* logits, int64_t n, float temp, float* out, int32_t flags) {
   if (n < 0 || (n > 0 && (!logits || !out))) return fail(MOE_EINVAL, "bad scores arguments%s%lld");
+  if (int r = check_score_flags(flags)) return r;
+  if (flags & 4) {
+    for (int64_t i = 0; i < n; ++i)
+      out[i] = exp_cr(temp == 1.0f ? logits[i] : (float)((double)logits[i] / (double)temp), (flags & 1) != 0);
+    return MOE_OK;
+  }
   if (flags & 2) {
     return guarded([&] {
       const ScoreTable t = host_score_table();

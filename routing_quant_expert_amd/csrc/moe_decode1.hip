@@ -329,6 +329,16 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = blockIdx.x * kDownRows;
   const int n_u = *w.plan.n_u();
+  // The combine's other inputs (the plan's weights, the residual rows) are
+  // loaded first: they arrive with the weight streams instead of costing a
+  // round trip after the last dot product.
+  float pw[kMaxTopk];
+  uint16_t res = 0;
+  if (threadIdx.x < kDownRows) {
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i) pw[i] = i < slots ? w.plan.pair_w()[i] : 0.0f;
+    if (o.next) res = o.resid[row0 + threadIdx.x];
+  }
   if (wave < slots) {
     const int e_slot = w.plan.u_expert()[wave];   // (loaded together with n_u: no dependent round trip)
     const int e = wave < n_u ? e_slot : -1;
@@ -418,12 +428,13 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
   if (threadIdx.x < kDownRows) {
     const int r = threadIdx.x;
     float acc = 0.0f;
-    for (int i = 0; i < slots; ++i)
-      if (i < n_u) acc = fadd(acc, fmul(w.plan.pair_w()[i], ys[i][r]));   // a quantised shared expert last, weight 1
+#pragma unroll
+    for (int i = 0; i < kMaxTopk; ++i)
+      if (i < slots && i < n_u) acc = fadd(acc, fmul(pw[i], ys[i][r]));   // a quantised shared expert last, weight 1
     if (SHARED) acc = fadd(acc, sds[r]);
     if (o.f32) o.f32[row0 + r] = acc;
     if (o.bf16) o.bf16[row0 + r] = bf16_rne(acc);
-    if (o.next) o.next[row0 + r] = bf16_rne(fadd(bf16_f32(o.resid[row0 + r]), acc));
+    if (o.next) o.next[row0 + r] = bf16_rne(fadd(bf16_f32(res), acc));
   }
 }
 

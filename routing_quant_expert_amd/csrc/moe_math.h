@@ -5,11 +5,12 @@
 // Method (own design; the pages only ask that the device selection equal the
 // host reference bit for bit [device_route.rs, module doc]; read here as
 // "every elementary step correctly rounded to f32"):
-//  * fast path: evaluate in float64 with the platform's exp/log1p (error well
-//    under 2 float64 ulps), round to f32, and accept unless the float64 value
-//    lies within 2^-47 (relative) of the midpoint between two f32 neighbours
-//    (Ziv's rounding test: A. Ziv, "Fast evaluation of elementary
-//    mathematical functions with correctly rounded last bit", ACM TOMS 1991);
+//  * fast path: evaluate in float64 with the straight-line estimates exp_est
+//    and log1p_est below (relative error under 2^-50), round to f32, and
+//    accept unless the float64 value lies within 2^-47 (relative) of the
+//    midpoint between two f32 neighbours (Ziv's rounding test: A. Ziv, "Fast
+//    evaluation of elementary mathematical functions with correctly rounded
+//    last bit", ACM TOMS 1991);
 //  * slow path: double-double arithmetic (Dekker 1971 products and Knuth's
 //    two-sum): exp by Cody-Waite reduction x = k ln2 + r with ln2 in three
 //    parts, exp(r/256) by its Taylor series to degree 9, then eight
@@ -69,11 +70,14 @@ __host__ __device__ inline dd inv_factorial(int n) {
   return {hi, lo};
 }
 
+constexpr double kInvLn2 = 0x1.71547652b82fep+0;
+constexpr double kLn2Hi = 0x1.62e42fefa3800p-1;   // ln2 to 42 bits: k*kLn2Hi exact for |k| < 2^11
+constexpr double kLn2Lo = 0x1.ef35793c76730p-45;  // the next 53 bits
+
 // exp(x) for a double x in [-746, 710] as a double-double (relative error < 2^-95).
 __host__ __device__ inline dd exp_dd(double x) {
-  const double kInvLn2 = 0x1.71547652b82fep+0;
-  const double kL1 = 0x1.62e42fefa3800p-1;   // ln2 to 42 bits: k*kL1 exact for |k| < 2^11
-  const double kL2 = 0x1.ef35793c76730p-45;
+  const double kL1 = kLn2Hi;
+  const double kL2 = kLn2Lo;
   const double kL3 = 0x1.f97b57a079a19p-103;
   double k = rint(x * kInvLn2);
   double r1 = x - k * kL1;                    // exact (Sterbenz)
@@ -87,6 +91,68 @@ __host__ __device__ inline dd exp_dd(double x) {
   for (int i = 0; i < 8; ++i) p = dd_mul(p, p);
   int ki = (int)k;
   return {ldexp(p.hi, ki), ldexp(p.lo, ki)};
+}
+
+// The fast paths' float64 estimates: straight-line code (the callers handle
+// the ends of the ranges), relative error below 2^-50, a factor 8 inside
+// Ziv's 2^-47 margin. FMA rounding u = 2^-53 throughout.
+//
+// exp_est(x), |x| <= 745: x = k ln2 + r by Cody-Waite (kLn2Hi*k exact, so
+// r = x - k ln2 up to one rounding of the kLn2Lo term), |r| <= ln2/2; e^r
+// by its Taylor polynomial of degree 13 in Horner form (the omitted terms
+// are below r^14/14! < 2^-57 e^r); then times 2^k. The Horner steps add
+// under 2u relative (each step's rounding is damped by |r|^i), the rounded
+// coefficients under 1.5u and the reduction under u: about 2^-51 in all.
+__host__ __device__ inline double exp_est(double x) {
+  const double k = rint(x * kInvLn2);
+  const double r = __builtin_fma(-k, kLn2Lo, __builtin_fma(-k, kLn2Hi, x));
+  double p = 1.0 / 6227020800.0;   // 1/13!
+  p = __builtin_fma(p, r, 1.0 / 479001600.0);
+  p = __builtin_fma(p, r, 1.0 / 39916800.0);
+  p = __builtin_fma(p, r, 1.0 / 3628800.0);
+  p = __builtin_fma(p, r, 1.0 / 362880.0);
+  p = __builtin_fma(p, r, 1.0 / 40320.0);
+  p = __builtin_fma(p, r, 1.0 / 5040.0);
+  p = __builtin_fma(p, r, 1.0 / 720.0);
+  p = __builtin_fma(p, r, 1.0 / 120.0);
+  p = __builtin_fma(p, r, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p = __builtin_fma(p, r, 1.0);
+  return ldexp(p, (int)k);
+}
+
+// log1p_est(x) for an f32 value x > -1: u = 1 + x is exact (x's last bit
+// is at or above 2^-47 when |x| >= 2^-24, and for x >= 2^53 the rounding of
+// u changes the logarithm by under 2^-58). u = m 2^k with m in
+// [sqrt(1/2), sqrt(2)), f = m - 1 exact (Sterbenz); log(1 + f) = 2 atanh(s)
+// with s = f / (2 + f), |s| <= 0.1716, by its series to s^19 (the omitted
+// terms are below 2^-55 relative); then + k ln2. s carries about 3u
+// (the rounded 2 + f and the division), the series u, the sum with k ln2
+// under u: about 2^-51 in all.
+__host__ __device__ inline double log1p_est(double x) {
+  const double u = 1.0 + x;
+  int k;
+  double m = frexp(u, &k);
+  const bool below = m < 0x1.6a09e667f3bcdp-1;   // sqrt(1/2)
+  m = below ? m + m : m;
+  k = below ? k - 1 : k;
+  const double f = m - 1.0;
+  const double s = f / (2.0 + f);
+  const double s2 = s * s;
+  double q = 2.0 / 19.0;
+  q = __builtin_fma(q, s2, 2.0 / 17.0);
+  q = __builtin_fma(q, s2, 2.0 / 15.0);
+  q = __builtin_fma(q, s2, 2.0 / 13.0);
+  q = __builtin_fma(q, s2, 2.0 / 11.0);
+  q = __builtin_fma(q, s2, 2.0 / 9.0);
+  q = __builtin_fma(q, s2, 2.0 / 7.0);
+  q = __builtin_fma(q, s2, 2.0 / 5.0);
+  q = __builtin_fma(q, s2, 2.0 / 3.0);
+  const double l = __builtin_fma(s * s2, q, 2.0 * s);   // 2s + 2s^3/3 + ... + 2s^19/19
+  const double kd = (double)k;
+  return __builtin_fma(kd, kLn2Hi, __builtin_fma(kd, kLn2Lo, l));
 }
 
 // An f32 value as a double, with the infinity that rounding overflows to
@@ -140,7 +206,7 @@ __host__ __device__ inline float exp_cr(float x, bool force_slow = false) {
   if (isnan(x)) return x;
   if (x > 89.0f) return __builtin_inff();
   if (x < -104.0f) return 0.0f;   // exp(x) < 2^-150: rounds to +0
-  double y = exp((double)x);
+  double y = exp_est((double)x);
   if (!force_slow && !near_midpoint(y)) return (float)y;
   return round_dd_to_f32(exp_dd((double)x));
 }
@@ -151,7 +217,7 @@ __host__ __device__ inline float log1p_cr(float x, bool force_slow = false) {
   if (x < -1.0f) return __builtin_nanf("");
   if (x == -1.0f) return -__builtin_inff();
   if (fabsf(x) < 0x1p-24f) return x;   // |log1p(x) - x| < x^2/2: x is the nearest f32
-  double y0 = log1p((double)x);
+  double y0 = log1p_est((double)x);
   if (!force_slow && !near_midpoint(y0)) return (float)y0;
   // Newton on f(y) = (1+x) e^-y - 1: y1 = y0 + (1+x) e^-y0 - 1
   dd u = two_sum(1.0, (double)x);
@@ -176,9 +242,9 @@ __host__ __device__ inline float fadd(float a, float b) { return a + b; }
 // score = sqrt(softplus(logit / temp)), softplus(z) = z > 20 ? z : log1p(exp(z))
 // [moe_v41.rs, fn softplus, fn route_from_logits]. sqrt and the division are
 // correctly rounded in f32: through float64 (53 >= 2*24+2, so the double
-// rounding is harmless).
+// rounding is harmless); temp = 1 divides exactly, so the division is skipped.
 __host__ __device__ inline float score_of(float logit, float temp, bool force_slow = false) {
-  float z = (float)((double)logit / (double)temp);
+  float z = temp == 1.0f ? logit : (float)((double)logit / (double)temp);
   float sp = z > 20.0f ? z : log1p_cr(exp_cr(z, force_slow), force_slow);
   return (float)sqrt((double)sp);
 }

@@ -287,10 +287,15 @@ __global__ __launch_bounds__(64) void k_plan_small(const int32_t* __restrict__ h
   build_plan<KPER>(picks, wts, tok_ok, m, topk, plan, emap, shq, n_routed);
 }
 
+// flags as moe_scores: bit 0 the extended path, bit 2 the exp step alone
+// (st: the glibc table, with bit 1).
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ lg, int64_t n, float temp,
-                                                float* __restrict__ out, int force_slow, ScoreTable st) {
+                                                float* __restrict__ out, int flags, ScoreTable st) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = st.keys ? score_mode_of(lg[i], temp, st) : score_of(lg[i], temp, force_slow != 0);
+  if (i >= n) return;
+  const bool slow = (flags & 1) != 0;
+  if (flags & 4) out[i] = exp_cr(temp == 1.0f ? lg[i] : (float)((double)lg[i] / (double)temp), slow);
+  else out[i] = st.keys ? score_mode_of(lg[i], temp, st) : score_of(lg[i], temp, slow);
 }
 
 }  // namespace
@@ -353,8 +358,7 @@ hipError_t launch_scores(const float* logits, int64_t n, float temp, float* out,
   moe_cfg glibc{};
   glibc.score_mode = MOE_SCORE_GLIBC;
   const ScoreTable st = (flags & 2) ? score_table_for(glibc) : ScoreTable{nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(k_scores, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, logits, n, temp, out, flags & 1,
-                     st);
+  hipLaunchKernelGGL(k_scores, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, logits, n, temp, out, flags, st);
   return hipGetLastError();
 }
 

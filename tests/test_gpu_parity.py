@@ -125,6 +125,44 @@ def test_score_chain_on_every_f32_input():
     torch.cuda.empty_cache()
 
 
+def test_exp_step_on_every_f32_input():
+    """Every f32 in [-104, 89] (the fast path's domain; the SwiGLU's exp
+    reaches up to 89): the device's exp step (the straight-line float64
+    estimate with Ziv's test) equals its extended-precision path on every
+    input, and on the inputs whose float64 exp lies within 2^-40 of an f32
+    midpoint (the hard cases) it equals the oracle's correctly rounded exp."""
+    n = 1 << 27
+    hard = []
+    checked = 0
+    for c in range(32):
+        v = torch.arange(c * n, (c + 1) * n, dtype=torch.int64, device="cuda")
+        x = (((v + (1 << 31)) % (1 << 32)) - (1 << 31)).to(torch.int32).view(torch.float32)
+        x = x[torch.isfinite(x) & (x >= -104.0) & (x <= 89.0)]
+        if x.numel() == 0:
+            continue
+        a, b = torch.empty_like(x), torch.empty_like(x)
+        R.scores(x, 1.0, a, R.SCORES_EXP_ONLY)
+        R.scores(x, 1.0, b, R.SCORES_EXP_ONLY | R.SCORES_EXTENDED)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), c
+        checked += x.numel()
+        h = _near_f32_midpoint(torch.exp(x.double()), 2.0 ** -40)
+        hard.append(x[h].cpu())
+        del v, x, a, b, h
+    hx = torch.cat(hard).numpy()
+    say(f"exp step: {checked} inputs fast == extended; {hx.size} near-midpoint inputs against the oracle")
+    assert checked > 2_000_000_000 and hx.size > 100
+    want = oracle.exp_cr(hx)
+    xd = torch.from_numpy(hx).cuda()
+    out = torch.empty_like(xd)
+    R.scores(xd, 1.0, out, R.SCORES_EXP_ONLY)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, (hx[bad[:5]], got[bad[:5]], want[bad[:5]])
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- routing
 @pytest.mark.parametrize("shape,m", [(TINY, 1), (TINY, 5), (TINY, 37), (DS41, 1), (DS41, 8)])
 def test_route_select_bit_exact(shape, m):

@@ -114,6 +114,25 @@ def test_library_score_chain_matches_oracle_on_host():
     assert np.array_equal(got.view(np.uint32), oracle.scores(x[:100_000], 0.7).view(np.uint32))
 
 
+def test_library_exp_step_matches_oracle_on_host():
+    """The exp step (flags bit 2) on one input in 2,000 of every f32 in
+    [-104, 89] plus the ends: the straight-line estimate with Ziv's test
+    equals the extended path and the oracle's correctly rounded exp."""
+    lo, hi = np.float32(-104.0).view(np.uint32), np.float32(89.0).view(np.uint32)
+    neg = np.arange(0x80000000, lo + 1, 2000, dtype=np.uint64).astype(np.uint32)
+    pos = np.arange(0, hi + 1, 2000, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([neg.view(np.float32), pos.view(np.float32),
+                        np.array([-104.0, 89.0, 20.0, 20.000002, -87.33655, -0.0, 1e-45, -1e-45], np.float32)])
+    fast = R.scores_host(x, 1.0, R.SCORES_EXP_ONLY)
+    slow = R.scores_host(x, 1.0, R.SCORES_EXP_ONLY | R.SCORES_EXTENDED)
+    assert np.array_equal(fast.view(np.uint32), slow.view(np.uint32))
+    want = oracle.exp_cr(x)
+    bad = np.nonzero(fast.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, (x[bad[:5]], fast[bad[:5]], want[bad[:5]])
+    with pytest.raises(R.MoeError):
+        R.scores_host(x[:4], 1.0, R.SCORES_EXP_ONLY | R.SCORES_GLIBC)
+
+
 def test_library_swiglu_matches_oracle_on_host():
     rng = np.random.default_rng(6)
     g = np.concatenate([rng.normal(0, 2, 200_000), rng.uniform(-120, 20, 50_000)]).astype(np.float32)
