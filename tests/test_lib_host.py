@@ -131,6 +131,10 @@ def test_library_exp_step_matches_oracle_on_host():
     assert bad.size == 0, (x[bad[:5]], fast[bad[:5]], want[bad[:5]])
     with pytest.raises(R.MoeError):
         R.scores_host(x[:4], 1.0, R.SCORES_EXP_ONLY | R.SCORES_GLIBC)
+    # another temperature: the step's input is RN32(logit / temp)
+    lg = np.random.default_rng(8).normal(0, 6, 50_000).astype(np.float32)
+    z = (lg.astype(np.float64) / np.float64(np.float32(0.7))).astype(np.float32)
+    assert np.array_equal(R.scores_host(lg, 0.7, R.SCORES_EXP_ONLY).view(np.uint32), oracle.exp_cr(z).view(np.uint32))
 
 
 def test_library_swiglu_matches_oracle_on_host():
