@@ -21,6 +21,7 @@
 #include "moe_kquant.h"
 #include "moe_math.h"
 #include "moe_select.h"
+#include "moe_wave.h"
 
 namespace moe {
 namespace {
@@ -270,12 +271,10 @@ __global__ __launch_bounds__(256) void k_gateup_m1(GateUp1Args a, Ws w) {
     if (!shared_only && ebl >= 0) {   // q8_1 of the 32 h values (one block), lanes 0..31
       const int slot = blk / (a.inter / 32), grp = blk % (a.inter / 32);
       const int r = lane & 31;
-      float am = fabsf(hv);
-      for (int s = 16; s >= 1; s >>= 1) am = fmaxf(am, __shfl_xor(am, s));
+      const float am = max32(fabsf(hv));
       const float d = (float)((double)am / 127.0);
       const int q = am == 0.0f ? 0 : q8_code(hv, d);
-      int sum = q;
-      for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+      const int sum = sum16(q);
       if (lane < 32) {
         const int64_t row = (int64_t)slot * a.inter + 32 * grp + r;
         w.g[row] = gv;
@@ -413,8 +412,7 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
       }
     }
 #pragma unroll
-    for (int r = 0; r < kR; ++r)
-      for (int s = 32; s >= 1; s >>= 1) p[r] += __shfl_xor(p[r], s);
+    for (int r = 0; r < kR; ++r) p[r] = wave_sum_xor(p[r]);
     if (lane < kR) {
       float v = 0.0f;
 #pragma unroll

@@ -15,6 +15,7 @@
 #include "moe_internal.h"
 #include "moe_kquant.h"
 #include "moe_math.h"
+#include "moe_wave.h"
 
 namespace moe {
 namespace {
@@ -96,12 +97,10 @@ __global__ __launch_bounds__(256) void k_gateup(XArena ex, PlanView plan, const 
     const int pair = first + j;
     float gv = gu[0][j][r], uv = gu[1][j][r];
     float hv = swiglu(gv, uv, L);
-    float a = fabsf(hv);
-    for (int s = 16; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
+    const float a = max32(fabsf(hv));
     float d = (float)((double)a / 127.0);
     int q = a == 0.0f ? 0 : q8_code(hv, d);
-    int sum = q;
-    for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+    const int sum = sum16(q);
     if (lane < 32) {
       const int64_t row = (int64_t)pair * inter + 32 * grp + r;
       g_out[row] = gv;
@@ -208,8 +207,7 @@ __device__ void shared_down_rows(int blk, int m, int dim, int inter, const uint1
   for (int r = 0; r < S::kRw; ++r) {
 #pragma unroll
     for (int t = 0; t < kMaxDecodeTokens; ++t)
-      if (t < m)
-        for (int s = 32; s >= 1; s >>= 1) p[r][t] += __shfl_xor(p[r][t], s);
+      if (t < m) p[r][t] = wave_sum_xor(p[r][t]);
     if (lane < m) {
       float v = 0.0f;
 #pragma unroll

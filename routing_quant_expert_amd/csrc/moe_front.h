@@ -7,6 +7,7 @@
 
 #include "moe_internal.h"
 #include "moe_math.h"
+#include "moe_wave.h"
 
 namespace moe {
 namespace front {
@@ -28,13 +29,11 @@ __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* _
                               uint16_t* __restrict__ xd, int32_t* __restrict__ xs, double* __restrict__ xd64 = nullptr) {
   const int64_t i = (int64_t)blk * 256 + threadIdx.x;   // m*dim is a multiple of 256
   float v = bf16_f32(x[i]);
-  float a = fabsf(v);
-  for (int s = 16; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
+  const float a = max32(fabsf(v));
   float d = (float)((double)a / 127.0);
   int q = a == 0.0f ? 0 : q8_code(v, d);
   xq[i] = (int8_t)q;
-  int sum = q;
-  for (int s = 8; s >= 1; s >>= 1) sum += __shfl_xor(sum, s);
+  const int sum = sum16(q);
   const int lane32 = threadIdx.x & 31;
   if (lane32 == 0) {
     xd[i >> 5] = fp16_bits(d);
@@ -47,8 +46,8 @@ __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* _
 // Router GEMV + scores. One wave64 per expert row, for the tokens
 // [t_lo, t_hi) of the call (default: all of them). Lane l accumulates positions 512*i + 8*l + j (i ascending, j = 0..7) in
 // f32 (product, then add: every bf16 x bf16 product is exact), then the 64
-// partials combine as p += shfl_xor(p, s) for s = 32..1 and lane 0 holds the
-// logit. This per-row order is the same for every m, so a token's logits
+// partials combine as p += shfl_xor(p, s) for s = 32..1 (computed by
+// wave_sum_xor) and lane 0 holds the logit. This per-row order is the same for every m, so a token's logits
 // never depend on the batch it rides in.
 // ---------------------------------------------------------------------------
 constexpr int kRouterTok = 8;
@@ -103,11 +102,8 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
       }
     }
 #pragma unroll
-    for (int t = 0; t < kRouterTok; ++t) {
-      float v = p[t];
-      for (int s = 32; s >= 1; s >>= 1) v = fadd(v, __shfl_xor(v, s));
-      p[t] = v;
-    }
+    for (int t = 0; t < kRouterTok; ++t)
+      if (t < nt) p[t] = wave_sum_xor(p[t]);
     if (lane < nt) {
       float lg = 0.0f;
 #pragma unroll
@@ -168,9 +164,9 @@ __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, i
   }
 #pragma unroll
   for (int t = 0; t < kMaxDecodeTokens; ++t) {
-    for (int s = 32; s >= 1; s >>= 1) {
-      pg[t] += __shfl_xor(pg[t], s);
-      pu[t] += __shfl_xor(pu[t], s);
+    if (t < m) {
+      pg[t] = wave_sum_xor(pg[t]);
+      pu[t] = wave_sum_xor(pu[t]);
     }
   }
   if (lane < m) {
@@ -232,12 +228,8 @@ __device__ inline void shared_gu_sum(const SharedUnitLoads& L, int dim, float& g
       }
     }
   }
-  for (int s = 32; s >= 1; s >>= 1) {
-    pg += __shfl_xor(pg, s);
-    pu += __shfl_xor(pu, s);
-  }
-  g = pg;
-  u = pu;
+  g = wave_sum_xor(pg);
+  u = wave_sum_xor(pu);
 }
 
 __device__ inline void shared_gu_unit(int un, const uint16_t* __restrict__ x, int dim,

@@ -10,6 +10,7 @@
 
 #include "moe_internal.h"
 #include "moe_math.h"
+#include "moe_wave.h"
 
 namespace moe {
 
@@ -197,8 +198,8 @@ __device__ __forceinline__ double seg_sum_f64(double v) {
   if constexpr (NSB >= 4) v = step(v, std::integral_constant<int, 0x4e>{});    // lane ^ 2
   if constexpr (NSB >= 8) v = step(v, std::integral_constant<int, 0x141>{});   // other quad of the half row
   if constexpr (NSB >= 16) v = step(v, std::integral_constant<int, 0x140>{});  // other half of the row
-  if constexpr (NSB >= 32) v += __shfl_xor(v, 16);
-  if constexpr (NSB >= 64) v += __shfl_xor(v, 32);
+  if constexpr (NSB >= 32) v = sum_xor16_f64(v);
+  if constexpr (NSB >= 64) v = sum_xor32_f64(v);
   return v;
 }
 

@@ -7,10 +7,12 @@
 // "every elementary step correctly rounded to f32"):
 //  * fast path: evaluate in float64 with the straight-line estimates exp_est
 //    and log1p_est below (relative error under 2^-50), round to f32, and
-//    accept unless the float64 value lies within 2^-47 (relative) of the
+//    accept unless the float64 value may lie within 2^-47 (relative) of the
 //    midpoint between two f32 neighbours (Ziv's rounding test: A. Ziv, "Fast
 //    evaluation of elementary mathematical functions with correctly rounded
-//    last bit", ACM TOMS 1991);
+//    last bit", ACM TOMS 1991), read off the estimate's bits (ziv_reject);
+//    the fast paths are straight-line code (selects, no branches) and only
+//    the rare rejected inputs branch to the slow path;
 //  * slow path: double-double arithmetic (Dekker 1971 products and Knuth's
 //    two-sum): exp by Cody-Waite reduction x = k ln2 + r with ln2 in three
 //    parts, exp(r/256) by its Taylor series to degree 9, then eight
@@ -174,14 +176,18 @@ __host__ __device__ inline double midpoint_toward(float f, double y) {
   return 0.5 * (f32_as_double(f) + f32_as_double(nb));
 }
 
-// Ziv's test: true when the double estimate y (relative error < 2^-50) may
-// round differently from the exact value.
-__host__ __device__ inline bool near_midpoint(double y) {
-  float f = (float)y;
-  double fd = f32_as_double(f);
-  if (fd == y) return false;
-  double mid = midpoint_toward(f, y);
-  return fabs(y - mid) <= 0x1p-47 * fabs(y);
+// Ziv's test on the bits of a float64 estimate y (relative error < 2^-50)
+// whose f32 rounding is wanted: true when y may round differently from the
+// exact value. For y in the normal f32 range the rounding discards the low 29
+// bits D of y's significand, and the midpoint between the two f32 neighbours
+// has D = 2^28; |y - mid| = |D - 2^28| ulp64(y) while 2^-47 |y| < 64 ulp64(y),
+// so testing |D - 2^28| <= 64 catches every y within 2^-47 |y| of a midpoint
+// (and a few more, which the slow path rounds just as well). Below 2^-126 the
+// f32 rounding point lies further up the significand: always rejected.
+// NaN and infinite y are the callers' to exclude.
+__host__ __device__ inline bool ziv_reject(double y) {
+  const uint32_t d = (uint32_t)__builtin_bit_cast(uint64_t, y) & 0x1FFFFFFFu;
+  return d - 0x0FFFFFC0u <= 128u || fabs(y) < 0x1p-126;
 }
 
 // Correct f32 rounding of a normalised double-double.
@@ -201,25 +207,43 @@ __host__ __device__ inline float round_dd_to_f32(dd v) {
   return toward_nb_side ? nb : f;
 }
 
+// The fast path of exp_cr for any f32 x: the estimate rounded to f32 (or the
+// exact value of a special input) and whether Ziv's test rejects it.
+__host__ __device__ inline float exp_fast(float x, bool& reject) {
+  const bool in = x >= -104.0f && x <= 89.0f;   // false for NaN
+  const double y = exp_est((double)(in ? x : 0.0f));
+  reject = in && ziv_reject(y);
+  // exp(x) < 2^-150 below -104 (rounds to +0); above 89 it overflows; NaN stays
+  const float sp = x > 89.0f ? __builtin_inff() : (x < -104.0f ? 0.0f : x);
+  return in ? (float)y : sp;
+}
+
 // RN32(exp(x)) for any f32 x.
 __host__ __device__ inline float exp_cr(float x, bool force_slow = false) {
-  if (isnan(x)) return x;
-  if (x > 89.0f) return __builtin_inff();
-  if (x < -104.0f) return 0.0f;   // exp(x) < 2^-150: rounds to +0
-  double y = exp_est((double)x);
-  if (!force_slow && !near_midpoint(y)) return (float)y;
+  bool reject;
+  const float f = exp_fast(x, reject);
+  if (!(reject || force_slow) || !(x >= -104.0f && x <= 89.0f)) return f;
   return round_dd_to_f32(exp_dd((double)x));
+}
+
+// The fast path of log1p_cr for any f32 x, as exp_fast.
+__host__ __device__ inline float log1p_fast(float x, bool& reject) {
+  const bool in = fabsf(x) >= 0x1p-24f && x > -1.0f && x < __builtin_inff();   // false for NaN
+  const double y = log1p_est((double)(in ? x : 1.0f));
+  reject = in && ziv_reject(y);
+  // |x| < 2^-24: |log1p(x) - x| < x^2/2, x is the nearest f32; +inf and NaN
+  // stay; -1 gives -inf, below -1 NaN
+  const float sp = x == -1.0f ? -__builtin_inff() : (x < -1.0f ? __builtin_nanf("") : x);
+  return in ? (float)y : sp;
 }
 
 // RN32(log1p(x)) for f32 x >= -1 (NaN for x < -1).
 __host__ __device__ inline float log1p_cr(float x, bool force_slow = false) {
-  if (isnan(x) || isinf(x)) return x > 0.0f ? x : (isnan(x) ? x : __builtin_nanf(""));
-  if (x < -1.0f) return __builtin_nanf("");
-  if (x == -1.0f) return -__builtin_inff();
-  if (fabsf(x) < 0x1p-24f) return x;   // |log1p(x) - x| < x^2/2: x is the nearest f32
-  double y0 = log1p_est((double)x);
-  if (!force_slow && !near_midpoint(y0)) return (float)y0;
+  bool reject;
+  const float f = log1p_fast(x, reject);
+  if (!(reject || force_slow) || !(fabsf(x) >= 0x1p-24f && x > -1.0f && x < __builtin_inff())) return f;
   // Newton on f(y) = (1+x) e^-y - 1: y1 = y0 + (1+x) e^-y0 - 1
+  const double y0 = log1p_est((double)x);
   dd u = two_sum(1.0, (double)x);
   dd e = exp_dd(-y0);
   dd p = dd_mul(u, e);
@@ -243,9 +267,15 @@ __host__ __device__ inline float fadd(float a, float b) { return a + b; }
 // [moe_v41.rs, fn softplus, fn route_from_logits]. sqrt and the division are
 // correctly rounded in f32: through float64 (53 >= 2*24+2, so the double
 // rounding is harmless); temp = 1 divides exactly, so the division is skipped.
+// Both fast paths run straight through; if either rejects (or force_slow),
+// the chain is redone on the slow paths.
 __host__ __device__ inline float score_of(float logit, float temp, bool force_slow = false) {
-  float z = temp == 1.0f ? logit : (float)((double)logit / (double)temp);
-  float sp = z > 20.0f ? z : log1p_cr(exp_cr(z, force_slow), force_slow);
+  const float z = temp == 1.0f ? logit : (float)((double)logit / (double)temp);
+  bool r1, r2;
+  const float e = exp_fast(z, r1);
+  float sp = log1p_fast(e, r2);
+  if (!(z > 20.0f) && (r1 || r2 || force_slow)) sp = log1p_cr(exp_cr(z, true), true);
+  sp = z > 20.0f ? z : sp;
   return (float)sqrt((double)sp);
 }
 

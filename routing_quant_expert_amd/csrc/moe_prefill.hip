@@ -32,6 +32,7 @@
 #include "moe_internal.h"
 #include "moe_kquant.h"
 #include "moe_math.h"
+#include "moe_wave.h"
 #include "moe_prefill.h"
 
 namespace moe {
@@ -115,11 +116,7 @@ __device__ void router_rows4(int e0, int t0, const uint16_t* __restrict__ x, int
 #pragma unroll
   for (int r = 0; r < kRpRows; ++r)
 #pragma unroll
-    for (int t = 0; t < kRpTok; ++t) {
-      float v = p[r][t];
-      for (int s = 32; s >= 1; s >>= 1) v = fadd(v, __shfl_xor(v, s));
-      p[r][t] = v;
-    }
+    for (int t = 0; t < kRpTok; ++t) p[r][t] = wave_sum_xor(p[r][t]);
   // lane 8r + t writes (row e0 + r, token t0 + t)
   if (lane < kRpRows * kRpTok) {
     const int r = lane >> 3, t = lane & 7;
@@ -547,12 +544,10 @@ __device__ __forceinline__ void gateup_pf_body(const GateUpPfArgs& a, uint8_t* l
       const bool live = tt < nt;
       const float gv = gu[0][tt][unit], uv = gu[1][tt][unit];
       const float hv = live ? swiglu(gv, uv, a.L) : 0.0f;
-      float am = fabsf(hv);
-      for (int sh = 16; sh >= 1; sh >>= 1) am = fmaxf(am, __shfl_xor(am, sh));
+      const float am = max32(fabsf(hv));
       const float d = (float)((double)am / 127.0);
       const int q = am == 0.0f ? 0 : q8_code(hv, d);
-      int sum = q;
-      for (int sh = 8; sh >= 1; sh >>= 1) sum += __shfl_xor(sum, sh);
+      const int sum = sum16(q);
       if (live) {
         const int64_t pair = first + c0 + tt;
         const int64_t o = pair * a.inter + 64 * grp + unit;
