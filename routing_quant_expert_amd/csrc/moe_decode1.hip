@@ -398,19 +398,9 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
       for (int r = 0; r < kR; ++r) wv[r][c] = in ? load_nt16(w2 + (int64_t)(rbase + r) * inter + k) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int c = 0; c < kCh; ++c) {
-      float hv[8];
-      const uint32_t hh[4] = {hvv[c].x, hvv[c].y, hvv[c].z, hvv[c].w};
+    for (int c = 0; c < kCh; ++c)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hv[j] = bf16_f32((uint16_t)(hh[j >> 1] >> (16 * (j & 1))));
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const uint32_t ww[4] = {wv[r][c].x, wv[r][c].y, wv[r][c].z, wv[r][c].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          p[r] = __builtin_fmaf(bf16_f32((uint16_t)(ww[j >> 1] >> (16 * (j & 1)))), hv[j], p[r]);
-      }
-    }
+      for (int r = 0; r < kR; ++r) p[r] = dot8_bf16(wv[r][c], hvv[c], p[r]);
 #pragma unroll
     for (int r = 0; r < kR; ++r) p[r] = wave_sum_xor(p[r]);
     if (lane < kR) {

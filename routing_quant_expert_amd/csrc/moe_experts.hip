@@ -131,16 +131,11 @@ struct DownGeom {
   static constexpr int kSlotBytes = kKC * 4096;
 };
 
-__device__ inline void bf16x8(uint4 v, float (&f)[8]) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
-}
-
 // Shared expert down rows for the m tokens: every token's sh is staged in LDS
 // once per workgroup; a wave computes kRw rows with all of their weight loads
-// in flight at once. Lane l sums positions 8l + 512c + (0..7) (c ascending) by
-// FMA for each token, then the 64 lanes combine by a butterfly.
+// in flight at once. Lane l sums positions 8l + 512c + (0..7) (c ascending),
+// two products per v_dot2_f32_bf16, for each token, then the 64 lanes combine
+// by wave_sum_xor.
 template <int NSB>
 struct SharedDownGeom {
   static constexpr int kCh = NSB >= 2 ? NSB / 2 : 1;    // 16-byte chunks of a row per lane (inter = 256*NSB)
@@ -187,18 +182,12 @@ __device__ void shared_down_rows(int blk, int m, int dim, int inter, const uint1
   for (int c = 0; c < S::kCh; ++c) {
     const int k = 8 * lane + 512 * c;
     if (k < inter) {
-      float a[S::kRw][8];
-#pragma unroll
-      for (int r = 0; r < S::kRw; ++r) bf16x8(wv[r][c], a[r]);
 #pragma unroll
       for (int t = 0; t < kMaxDecodeTokens; ++t) {
         if (t < m) {
-          float hv[8];
-          bf16x8(*reinterpret_cast<const uint4*>(shl + t * inter + k), hv);
+          const uint4 hv = *reinterpret_cast<const uint4*>(shl + t * inter + k);
 #pragma unroll
-          for (int r = 0; r < S::kRw; ++r)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[r][t] = __builtin_fmaf(a[r][j], hv[j], p[r][t]);
+          for (int r = 0; r < S::kRw; ++r) p[r][t] = dot8_bf16(wv[r][c], hv, p[r][t]);
         }
       }
     }

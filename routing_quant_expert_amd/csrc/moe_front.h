@@ -14,12 +14,6 @@ namespace front {
 
 __device__ inline uint16_t fp16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-__device__ inline void bf16x8(uint4 v, float (&f)[8]) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = bf16_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
-}
-
 // ---------------------------------------------------------------------------
 // q8_1 of bf16 rows: one thread per value, a q8_1 block = 32 consecutive
 // lanes. d = amax/127, code = roundf(x/d) (half away from zero), stored scale
@@ -120,6 +114,8 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
 // Shared expert gate/up (m <= 8): one wave per hidden unit i: sg = W1s[i].x,
 // su = W3s[i].x (f32, any order), sh = bf16(swiglu(sg, su)) [moe_v41.rs,
 // module doc: the shared expert is resident bf16 on the dense GEMM/GEMV].
+// A lane sums its chunks in order, two products per v_dot2_f32_bf16; then
+// the lanes' partials by wave_sum_xor.
 __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, int dim, int inter,
                                const uint16_t* __restrict__ w1, const uint16_t* __restrict__ w3,
                                float* __restrict__ sg, float* __restrict__ su, uint16_t* __restrict__ sh, float L) {
@@ -148,15 +144,9 @@ __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, i
         for (int c = 0; c < kLoadAhead; ++c) {
           const int k = 512 * (c0 + c) + 8 * lane;
           if (c0 + c < nch && k < dim) {
-            float a[8], b[8], xv[8];
-            bf16x8(av[c], a);
-            bf16x8(bv[c], b);
-            bf16x8(*reinterpret_cast<const uint4*>(x + (int64_t)t * dim + k), xv);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              pg[t] = __builtin_fmaf(a[j], xv[j], pg[t]);
-              pu[t] = __builtin_fmaf(b[j], xv[j], pu[t]);
-            }
+            const uint4 xv = *reinterpret_cast<const uint4*>(x + (int64_t)t * dim + k);
+            pg[t] = dot8_bf16(av[c], xv, pg[t]);
+            pu[t] = dot8_bf16(bv[c], xv, pu[t]);
           }
         }
       }
@@ -185,7 +175,7 @@ __device__ void shared_gu_rows(int blk, const uint16_t* __restrict__ x, int m, i
 }
 
 // Shared expert gate/up of ONE token for hidden unit `un`, by one wave: the
-// same per-lane summation order and butterfly as shared_gu_rows, so the
+// same per-lane summation order and lane reduction as shared_gu_rows, so the
 // values equal the multi-token ones. Every lane gets (g, u). dim <= 4096.
 // In two parts, so that a caller can put other loads in flight between the
 // issue of the unit's loads and their use.
@@ -217,15 +207,8 @@ __device__ inline void shared_gu_sum(const SharedUnitLoads& L, int dim, float& g
   for (int c = 0; c < SharedUnitLoads::kC; ++c) {
     const int k = 512 * c + 8 * lane;
     if (c < nch && k < dim) {
-      float fa[8], fb[8], fx[8];
-      bf16x8(L.a[c], fa);
-      bf16x8(L.b[c], fb);
-      bf16x8(L.x[c], fx);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pg = __builtin_fmaf(fa[j], fx[j], pg);
-        pu = __builtin_fmaf(fb[j], fx[j], pu);
-      }
+      pg = dot8_bf16(L.a[c], L.x[c], pg);
+      pu = dot8_bf16(L.b[c], L.x[c], pu);
     }
   }
   g = wave_sum_xor(pg);

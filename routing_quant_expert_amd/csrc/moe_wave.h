@@ -108,4 +108,20 @@ __device__ __forceinline__ double sum_xor32_f64(double v) {
   return __builtin_bit_cast(double, ((uint64_t)ha << 32) | la) + __builtin_bit_cast(double, ((uint64_t)hb << 32) | lb);
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi for two pairs of packed bf16 (v_dot2_f32_bf16):
+// two products of the shared expert's f32 sums per instruction, with no
+// conversions (those sums are in any order).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// dot2_bf16 over the four words of two 16-byte chunks (8 bf16 each).
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float acc) {
+  acc = dot2_bf16(a.x, b.x, acc);
+  acc = dot2_bf16(a.y, b.y, acc);
+  acc = dot2_bf16(a.z, b.z, acc);
+  return dot2_bf16(a.w, b.w, acc);
+}
+
 }  // namespace moe
