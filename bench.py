@@ -33,10 +33,10 @@ HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0   # dense int8 MFMA
 # a kernel's source file and every header it includes (the counters are tied to these)
 KERNEL_SOURCES = ("moe_decode1.hip", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h", "moe_select.h",
-                  "../../include/moe.h")
-UNION_SOURCES = ("moe_experts.hip", "moe_kquant.h", "moe_math.h", "moe_internal.h", "../../include/moe.h")
+                  "moe_wave.h", "../../include/moe.h")
+UNION_SOURCES = ("moe_experts.hip", "moe_kquant.h", "moe_math.h", "moe_internal.h", "moe_wave.h", "../../include/moe.h")
 PREFILL_SOURCES = ("moe_prefill.hip", "moe_prefill.h", "moe_front.h", "moe_kquant.h", "moe_math.h", "moe_internal.h",
-                   "../../include/moe.h")
+                   "moe_wave.h", "../../include/moe.h")
 
 
 def source_text_key(text: bytes) -> bytes:
