@@ -7,11 +7,12 @@
 //    q8_1 activation in LDS, then runs one 32-row group of one picked
 //    expert's Q2_K gate/up rows + SwiGLU + q8_1 of h. The first of them also
 //    writes the header and the plan tables.
-//  * k_down_m1: one workgroup per 16 output rows: one wave per picked expert
-//    streams that expert's Q3_K down rows into LDS and dots them with its
-//    q8_1(h); two more waves compute the shared expert's down rows; then the
-//    combine in plan order adds them up [moe_v41.rs, Kernels: accumulate,
-//    finish; fn shared_side].
+//  * k_down_m1: one workgroup per 16 output rows: each picked expert's rows
+//    are split over waves of 64 (row, super-block) items; a wave streams its
+//    rows' Q3_K blocks into LDS and dots them with the expert's q8_1(h); four
+//    more waves compute the shared expert's down rows; then the combine in
+//    plan order adds them up [moe_v41.rs, Kernels: accumulate, finish; fn
+//    shared_side].
 // The arithmetic is that of the general kernels (same dot-product and
 // combine order), so the results are bit-identical to them.
 #include <hip/hip_runtime.h>
@@ -304,30 +305,39 @@ __device__ __forceinline__ void dma_wave(const uint8_t* g, uint8_t* dst) {
   }
 }
 
-template <int NSB, int ROWS>
+// A routed wave takes kRows rows of one pick (64 (row, super-block) items,
+// one per lane; all 16 of the block's rows when they make at most 64 items).
+template <int NSB>
 struct DownM1Geom {
+  static constexpr int kRows = 16 * NSB > 64 ? 64 / NSB : 16;   // rows of one pick per routed wave
+  static constexpr int kParts = 16 / kRows;                     // routed waves per pick
   static constexpr int kRowBytes = NSB * kQ3KBytes;
-  static constexpr int kChunks = ROWS * kRowBytes / 16;
+  static constexpr int kChunks = kRows * kRowBytes / 16;
   static constexpr int kWaveBytes = ((kChunks + 63) / 64) * 1024;
-  static constexpr int kItems = ROWS * NSB;            // per wave
-  static constexpr int kIters = (kItems + 63) / 64;
+  static constexpr int kItems = kRows * NSB;                    // per routed wave, <= 64
 };
 
 constexpr int kDownRows = 16;
+constexpr int kSharedDownWaves = 4;   // bf16 shared expert: kDownRows / 4 rows per wave
+constexpr int kMaxDownWaves = 16;
 
-// slots: one wave per plan entry (the picks, and a quantised shared expert as
-// the last, weight 1); SHARED: two more waves for the bf16 shared expert's rows.
+// slots: the plan entries (the picks, and a quantised shared expert as the
+// last, weight 1), each taken by kParts routed waves; SHARED: four more waves
+// for the bf16 shared expert's rows. Waves w and w + 4 share a SIMD, so with
+// six picks at two waves each and the four shared waves every SIMD holds three
+// routed waves and one shared wave; a routed wave's latency is one item.
 template <int NSB, bool SHARED>
-__global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int inter, int slots,
-                                                 const uint16_t* __restrict__ w2, LayerOut o) {
-  using G = DownM1Geom<NSB, kDownRows>;
+__global__ __launch_bounds__(1024) void k_down_m1(XArena ex, Ws w, int dim, int inter, int slots,
+                                                  const uint16_t* __restrict__ w2, LayerOut o) {
+  using G = DownM1Geom<NSB>;
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ __align__(16) uint8_t act_lds[kMaxTopk][ActLds<NSB>::kBytes];
+  __shared__ __align__(16) uint8_t act_lds[kMaxDownWaves][ActLds<NSB>::kBytes];
   __shared__ float ys[kMaxTopk][kDownRows];
   __shared__ float sds[kDownRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = blockIdx.x * kDownRows;
   const int n_u = *w.plan.n_u();
+  const int nrw = slots * G::kParts;
   // The combine's other inputs (the plan's weights, the residual rows) are
   // loaded first: they arrive with the weight streams instead of costing a
   // round trip after the last dot product.
@@ -338,22 +348,23 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
     for (int i = 0; i < kMaxTopk; ++i) pw[i] = i < slots ? w.plan.pair_w()[i] : 0.0f;
     if (o.next) res = o.resid[row0 + threadIdx.x];
   }
-  if (wave < slots) {
-    const int e_slot = w.plan.u_expert()[wave];   // (loaded together with n_u: no dependent round trip)
-    const int e = wave < n_u ? e_slot : -1;
+  if (wave < nrw) {
+    const int pk = wave % slots, r0 = G::kRows * (wave / slots);
+    const int e_slot = w.plan.u_expert()[pk];   // (loaded together with n_u: no dependent round trip)
+    const int e = pk < n_u ? e_slot : -1;
     if (e >= 0) {
       const int sb = lane % NSB;
       uint8_t* mine = lds + wave * G::kWaveBytes;
       // the rows, then this expert's q8_1(h) into registers: every load is in
       // flight at once, and one wait covers them all
-      dma_wave<G::kChunks>(ex.down(e) + (uint64_t)row0 * G::kRowBytes, mine);
+      dma_wave<G::kChunks>(ex.down(e) + (uint64_t)(row0 + r0) * G::kRowBytes, mine);
       constexpr int kAP = (ActLds<NSB>::kChunks + 63) / 64;
       u32x4 piece[kAP];
 #pragma unroll
       for (int k = 0; k < kAP; ++k) {
         const int i = min(lane + 64 * k, ActLds<NSB>::kChunks - 1);
         piece[k] = *reinterpret_cast<const u32x4*>(act_piece_src<NSB>(
-            w.hq + (int64_t)wave * inter, w.hs + (int64_t)wave * (inter / 16), w.hd + (int64_t)wave * (inter / 32), i));
+            w.hq + (int64_t)pk * inter, w.hs + (int64_t)pk * (inter / 16), w.hd + (int64_t)pk * (inter / 32), i));
       }
       uint8_t* al = act_lds[wave];
       wait_vmcnt<0>();
@@ -364,26 +375,22 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
           *reinterpret_cast<u32x4*>(act_piece_dst<NSB>(al, lane + 64 * k)) = piece[k];
       Act A;
       load_act_lds<NSB>(A, al, sb);
-#pragma unroll
-      for (int it = 0; it < G::kIters; ++it) {
-        const int i = it * 64 + lane;
-        const bool act = i < G::kItems;
-        const int row = i / NSB;
-        double part = act ? dot_q3k(mine + row * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
-        part = seg_sum_f64<NSB>(part);
-        if (act && sb == 0) {
-          ys[wave][row] = (float)part;
-          w.y[(int64_t)wave * dim + row0 + row] = (float)part;
-        }
+      const bool act = lane < G::kItems;
+      const int row = lane / NSB;
+      double part = act ? dot_q3k(mine + row * G::kRowBytes + kQ3KBytes * sb, A) : 0.0;
+      part = seg_sum_f64<NSB>(part);
+      if (act && sb == 0) {
+        ys[pk][r0 + row] = (float)part;
+        w.y[(int64_t)pk * dim + row0 + r0 + row] = (float)part;
       }
-    } else if (lane < kDownRows) {
-      ys[wave][lane] = 0.0f;
+    } else if (lane < G::kRows) {
+      ys[pk][r0 + lane] = 0.0f;
     }
-  } else if (SHARED && wave < slots + 2) {
-    // shared expert down rows: half of the block's rows per wave, f32
-    constexpr int kR = kDownRows / 2;
+  } else if (SHARED && wave < nrw + kSharedDownWaves) {
+    // shared expert down rows: a quarter of the block's rows per wave, f32
+    constexpr int kR = kDownRows / kSharedDownWaves;
     constexpr int kCh = NSB >= 2 ? NSB / 2 : 1;   // 16-byte chunks of a row per lane (inter = 256*NSB)
-    const int rbase = row0 + kR * (wave - slots);
+    const int rbase = row0 + kR * (wave - nrw);
     float p[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) p[r] = 0.0f;
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(512) void k_down_m1(XArena ex, Ws w, int dim, int i
 #pragma unroll
       for (int r = 0; r < kR; ++r)
         if (r == lane) v = p[r];
-      sds[kR * (wave - slots) + lane] = v;
+      sds[kR * (wave - nrw) + lane] = v;
       w.sd[rbase + lane] = v;
     }
   }
@@ -449,16 +456,18 @@ hipError_t launch_gateup_m1_t(const GateUp1Args& a, const moe_cfg& c, const Ws& 
 template <int NSB>
 hipError_t launch_down_m1_t(const XArena& ex, const moe_cfg& c, const Ws& w, const uint16_t* w2, const LayerOut& o,
                             hipStream_t s) {
-  using G = DownM1Geom<NSB, kDownRows>;
+  using G = DownM1Geom<NSB>;
   const int slots = c.topk + ex.has_shared();
-  size_t shm = (size_t)slots * G::kWaveBytes;
-  const int threads = 64 * (slots + (w2 ? 2 : 0));
+  const size_t shm = (size_t)slots * G::kParts * G::kWaveBytes;
+  const int waves = slots * G::kParts + (w2 ? kSharedDownWaves : 0);
+  if (waves > kMaxDownWaves) return hipErrorInvalidValue;   // (shapes the single-token path does not take)
+  const int threads = 64 * waves;
   auto kern = w2 ? k_down_m1<NSB, true> : k_down_m1<NSB, false>;
   static bool attr_set[2] = {false, false};
   const int ai = w2 ? 1 : 0;
   if (!attr_set[ai]) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(kMaxTopk * G::kWaveBytes));
+                                       (int)(kMaxDownWaves * G::kWaveBytes));
     if (e != hipSuccess) return e;
     attr_set[ai] = true;
   }
