@@ -37,8 +37,9 @@ __device__ void quant_x_block(int blk, const uint16_t* __restrict__ x, int8_t* _
 }
 
 // ---------------------------------------------------------------------------
-// Router GEMV + scores. One wave64 per expert row, for the tokens
-// [t_lo, t_hi) of the call (default: all of them). Lane l accumulates positions 512*i + 8*l + j (i ascending, j = 0..7) in
+// Router GEMV + scores. One wave64 per expert row (three rows per workgroup
+// of four waves), for the tokens [t_lo, t_hi) of the call (default: all of
+// them). Lane l accumulates positions 512*i + 8*l + j (i ascending, j = 0..7) in
 // f32 (product, then add: every bf16 x bf16 product is exact), then the 64
 // partials combine as p += shfl_xor(p, s) for s = 32..1 (computed by
 // wave_sum_xor) and lane 0 holds the logit. This per-row order is the same for every m, so a token's logits
@@ -51,7 +52,10 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
                             const uint16_t* __restrict__ gate_w, int n_routed, float temp, float* __restrict__ logits,
                             float* __restrict__ scores, float* __restrict__ logits_out, const ScoreTable& st,
                             int t_lo = 0, int t_hi = -1) {
-  const int e = blk * 4 + (threadIdx.x >> 6);
+  // waves 0..2 take a row each; wave 3 runs the same code on no data at once,
+  // which brings it into the instruction cache before the others need it
+  const bool warm = (threadIdx.x >> 6) == 3;
+  const int e = blk * 3 + (warm ? 0 : (threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (e >= n_routed) return;
   const uint16_t* wr = gate_w + (int64_t)e * dim;
@@ -67,7 +71,7 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
 #pragma unroll
       for (int c = 0; c < kLoadAhead; ++c) {
         const int k = 512 * (c0 + c) + 8 * lane;
-        wv[c] = (c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
+        wv[c] = (!warm && c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(wr + k) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int t = 0; t < kRouterTok; ++t) {
@@ -76,7 +80,7 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
 #pragma unroll
           for (int c = 0; c < kLoadAhead; ++c) {
             const int k = 512 * (c0 + c) + 8 * lane;
-            xv[c] = (c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + t) * dim + k)
+            xv[c] = (!warm && c0 + c < nch && k < dim) ? *reinterpret_cast<const uint4*>(x + (int64_t)(t0 + t) * dim + k)
                                               : make_uint4(0, 0, 0, 0);
           }
           float acc = p[t];
@@ -104,9 +108,12 @@ __device__ void router_rows(int blk, const uint16_t* __restrict__ x, int m, int 
       for (int t = 0; t < kRouterTok; ++t)
         if (t == lane) lg = p[t];
       const int64_t o = (int64_t)(t0 + lane) * n_routed + e;
-      logits[o] = lg;
-      if (logits_out) logits_out[o] = lg;
-      scores[o] = score_mode_of(lg, temp, st);
+      const float sc = score_mode_of(lg, temp, st);
+      if (!warm) {
+        logits[o] = lg;
+        if (logits_out) logits_out[o] = lg;
+        scores[o] = sc;
+      }
     }
   }
 }

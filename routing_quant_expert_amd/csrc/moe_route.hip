@@ -319,7 +319,7 @@ hipError_t launch_front(const uint16_t* x, int m, const uint16_t* gate_w, const 
   a.w1 = w1;
   a.w3 = w3;
   a.logits_out = logits_out;
-  a.router_blocks = gate_w ? (c.n_routed + 3) / 4 : 0;
+  a.router_blocks = gate_w ? (c.n_routed + 2) / 3 : 0;
   a.shared_blocks = w1 ? (c.inter + 3) / 4 : 0;
   a.shq = sel ? sel->shq : 0;
   a.st = score_table_for(c);
