@@ -183,6 +183,16 @@ __device__ __forceinline__ void load_act_lds(Act& A, const uint8_t* lds, int sb)
 
 __device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
 
+// sdot4(a, b, 0) in the VOP3 form with an inline zero: the compiler otherwise
+// picks the VOP2 form and zeroes a register first (one instruction more per
+// accumulator; the routed gate/up tiles are issue-bound where two routed
+// workgroups share a CU).
+__device__ __forceinline__ int dot4_zero(int a, int b) {
+  int r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Sum of v over aligned groups of NSB lanes (every lane of a group gets the
 // group's sum; the same fixed order on every run).
 template <int NSB>
@@ -224,10 +234,11 @@ __device__ inline double dot_q2k(const uint8_t* p, const Act& A) {
     const uint32_t v2 = w & 0x30303030u;           // 16 * code
     const uint32_t v3 = (w >> 6) & 0x03030303u;    // 1 * code
     int* Ih = I + 8 * h + half;
-    Ih[0] = __builtin_amdgcn_sdot4((int)v0, (int)A.a[32 * h + t4], Ih[0], false);
-    Ih[2] = __builtin_amdgcn_sdot4((int)v1, (int)A.a[32 * h + 8 + t4], Ih[2], false);
-    Ih[4] = __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
-    Ih[6] = __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
+    const bool first = (t4 & 3) == 0;   // each accumulator's first product: the VOP3 form with a zero addend
+    Ih[0] = first ? dot4_zero((int)v0, (int)A.a[32 * h + t4]) : __builtin_amdgcn_sdot4((int)v0, (int)A.a[32 * h + t4], Ih[0], false);
+    Ih[2] = first ? dot4_zero((int)v1, (int)A.a[32 * h + 8 + t4]) : __builtin_amdgcn_sdot4((int)v1, (int)A.a[32 * h + 8 + t4], Ih[2], false);
+    Ih[4] = first ? dot4_zero((int)v2, (int)A.a[32 * h + 16 + t4]) : __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
+    Ih[6] = first ? dot4_zero((int)v3, (int)A.a[32 * h + 24 + t4]) : __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
   }
   double accS = 0.0, accM = 0.0;
 #pragma unroll
@@ -277,10 +288,11 @@ __device__ inline double dot_q3k(const uint8_t* p, const Act& A) {
     const uint32_t v2 = (w & 0x30303030u) | ((4 * h + 2 >= 6 ? (m >> (4 * h + 2 - 6)) : (m << (6 - 4 * h - 2))) & 0x40404040u);
     const uint32_t v3 = ((w >> 6) & 0x03030303u) | ((4 * h + 3 >= 2 ? (m >> (4 * h + 3 - 2)) : (m << (2 - 4 * h - 3))) & 0x04040404u);
     int* Ih = I + 8 * h + half;
-    Ih[0] = __builtin_amdgcn_sdot4((int)v0, (int)A.a[32 * h + t4], Ih[0], false);
-    Ih[2] = __builtin_amdgcn_sdot4((int)v1, (int)A.a[32 * h + 8 + t4], Ih[2], false);
-    Ih[4] = __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
-    Ih[6] = __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
+    const bool first = (t4 & 3) == 0;   // each accumulator's first product: the VOP3 form with a zero addend
+    Ih[0] = first ? dot4_zero((int)v0, (int)A.a[32 * h + t4]) : __builtin_amdgcn_sdot4((int)v0, (int)A.a[32 * h + t4], Ih[0], false);
+    Ih[2] = first ? dot4_zero((int)v1, (int)A.a[32 * h + 8 + t4]) : __builtin_amdgcn_sdot4((int)v1, (int)A.a[32 * h + 8 + t4], Ih[2], false);
+    Ih[4] = first ? dot4_zero((int)v2, (int)A.a[32 * h + 16 + t4]) : __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
+    Ih[6] = first ? dot4_zero((int)v3, (int)A.a[32 * h + 24 + t4]) : __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
   }
   double acc = 0.0;
 #pragma unroll
