@@ -22,8 +22,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-command-line-argument"]
 SOURCES = ["moe_api.hip", "moe_route.hip", "moe_experts.hip", "moe_decode1.hip", "moe_prefill.hip",
            "moe_shared_pf.hip", "moe_cache.hip", "moe_score_table.hip"]
-# the prefill kernels consume MFMA results in VALU code: keep them in VGPRs (no accvgpr copies)
-EXTRA = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# the prefill kernels consume MFMA results in VALU code: keep them in VGPRs (no accvgpr copies);
+# the single-token kernels' leading scalar arguments are preloaded into SGPRs at wave launch
+EXTRA = {"moe_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "moe_decode1.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _run(cmd, verbose):

@@ -321,14 +321,20 @@ constexpr int kDownRows = 16;
 constexpr int kSharedDownWaves = 4;   // bf16 shared expert: kDownRows / 4 rows per wave
 constexpr int kMaxDownWaves = 16;
 
+// The leading scalar arguments are what the first loads need (the plan's
+// words, and the routed arena's base, stride and down offset; pbase = nullptr
+// when the arena is a cache's slot pool): the build has the hardware preload
+// them into SGPRs at wave launch (-amdgpu-kernarg-preload-count), so the plan
+// and row loads do not wait for a load of the argument block first.
 // slots: the plan entries (the picks, and a quantised shared expert as the
 // last, weight 1), each taken by kParts routed waves; SHARED: four more waves
 // for the bf16 shared expert's rows. Waves w and w + 4 share a SIMD, so with
 // six picks at two waves each and the four shared waves every SIMD holds three
 // routed waves and one shared wave; a routed wave's latency is one item.
 template <int NSB, bool SHARED>
-__global__ __launch_bounds__(1024) void k_down_m1(XArena ex, Ws w, int dim, int inter, int slots,
-                                                  const uint16_t* __restrict__ w2, LayerOut o) {
+__global__ __launch_bounds__(1024) void k_down_m1(const int32_t* __restrict__ pplan, const uint8_t* __restrict__ pbase,
+                                                  uint64_t pstride, uint64_t pdoff, int pnr, XArena ex, Ws w, int dim,
+                                                  int inter, int slots, const uint16_t* __restrict__ w2, LayerOut o) {
   using G = DownM1Geom<NSB>;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ __align__(16) uint8_t act_lds[kMaxDownWaves][ActLds<NSB>::kBytes];
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(1024) void k_down_m1(XArena ex, Ws w, int dim, int 
   __shared__ float sds[kDownRows];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = blockIdx.x * kDownRows;
-  const int n_u = *w.plan.n_u();
+  const int n_u = pplan[0];
   const int nrw = slots * G::kParts;
   // The combine's other inputs (the plan's weights, the residual rows) are
   // loaded first: they arrive with the weight streams instead of costing a
@@ -350,14 +356,15 @@ __global__ __launch_bounds__(1024) void k_down_m1(XArena ex, Ws w, int dim, int 
   }
   if (wave < nrw) {
     const int pk = wave % slots, r0 = G::kRows * (wave / slots);
-    const int e_slot = w.plan.u_expert()[pk];   // (loaded together with n_u: no dependent round trip)
+    const int e_slot = pplan[2 + pk];   // (loaded together with n_u: no dependent round trip)
     const int e = pk < n_u ? e_slot : -1;
     if (e >= 0) {
       const int sb = lane % NSB;
       uint8_t* mine = lds + wave * G::kWaveBytes;
       // the rows, then this expert's q8_1(h) into registers: every load is in
       // flight at once, and one wait covers them all
-      dma_wave<G::kChunks>(ex.down(e) + (uint64_t)(row0 + r0) * G::kRowBytes, mine);
+      const uint8_t* dsrc = (pbase && e < pnr) ? pbase + (uint64_t)e * pstride + pdoff : ex.down(e);
+      dma_wave<G::kChunks>(dsrc + (uint64_t)(row0 + r0) * G::kRowBytes, mine);
       constexpr int kAP = (ActLds<NSB>::kChunks + 63) / 64;
       u32x4 piece[kAP];
 #pragma unroll
@@ -471,8 +478,8 @@ hipError_t launch_down_m1_t(const XArena& ex, const moe_cfg& c, const Ws& w, con
     if (e != hipSuccess) return e;
     attr_set[ai] = true;
   }
-  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, ex, w, c.dim, c.inter, slots, w2,
-             o);
+  MOE_LAUNCH(MOE_K_DOWN, kern, dim3(c.dim / kDownRows), dim3(threads), shm, s, w.plan.base,
+             ex.slot_of ? nullptr : ex.base, ex.stride, ex.down_off, ex.n_routed, ex, w, c.dim, c.inter, slots, w2, o);
   return hipGetLastError();
 }
 
