@@ -44,10 +44,11 @@ __device__ __forceinline__ void block_sync_lds() {
 
 template <int KC>
 __device__ __forceinline__ void dma_tile(const uint8_t* g, uint8_t* slot, int nchunks) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the source chunk per lane, the LDS destination per wave (uniform: m0 from scalar arithmetic)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
-    const int i = w * 64 + 256 * k + lane;
+    const int i = (int)threadIdx.x + 256 * k;
     const int src = i < nchunks ? i : nchunks - 1;
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + 16 * src),
                                      (__attribute__((address_space(3))) void*)(slot + 16 * (w * 64 + 256 * k)), 16,
@@ -60,7 +61,7 @@ __device__ __forceinline__ void dma_tile(const uint8_t* g, uint8_t* slot, int nc
 // last 64 chunks instead (the same bytes again to the same place).
 template <int KC>
 __device__ __forceinline__ void dma_tile_exact(const uint8_t* g, uint8_t* slot, int nchunks) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     const int base = min(w * 64 + 256 * k, nchunks - 64);
@@ -193,6 +194,14 @@ __device__ __forceinline__ int dot4_zero(int a, int b) {
   return r;
 }
 
+// The two signed 16-bit halves of a and b multiplied pairwise and summed
+// (v_dot2_i32_i16, VOP3 form with an inline zero addend).
+__device__ __forceinline__ int dot2_zero(uint32_t a, uint32_t b) {
+  int r;
+  asm("v_dot2_i32_i16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Sum of v over aligned groups of NSB lanes (every lane of a group gets the
 // group's sum; the same fixed order on every run).
 template <int NSB>
@@ -200,8 +209,9 @@ __device__ __forceinline__ double seg_sum_f64(double v) {
   auto step = [](double x, auto ctrl_tag) -> double {
     constexpr int CTRL = decltype(ctrl_tag)::value;
     const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xf, 0xf, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+    // every lane has a source under these controls, so the old value is never read: no zeroed register
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
     return x + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
   };
   if constexpr (NSB >= 2) v = step(v, std::integral_constant<int, 0xb1>{});    // lane ^ 1
@@ -241,13 +251,18 @@ __device__ inline double dot_q2k(const uint8_t* p, const Act& A) {
     Ih[6] = first ? dot4_zero((int)v3, (int)A.a[32 * h + 24 + t4]) : __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
   }
   double accS = 0.0, accM = 0.0;
+  uint32_t mins[4];   // the 4-bit mins of sub-blocks 4i..4i+3 as bytes
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mins[i] = (sc[i] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const uint32_t word = sc[t >> 1] >> (16 * (t & 1));
-    const int sa = (int)(word & 15u), ma = (int)((word >> 4) & 15u);
-    const int sb_ = (int)((word >> 8) & 15u), mb = (int)((word >> 12) & 15u);
+    const int sa = (int)(word & 15u), sb_ = (int)((word >> 8) & 15u);
     const int S = mad24(sa, I[2 * t], __mul24(sb_, I[2 * t + 1]));
-    const int M = mad24(ma, A.Q[2 * t], __mul24(mb, A.Q[2 * t + 1]));
+    // ma*Q[2t] + mb*Q[2t+1] in one signed 16-bit pair product (|Q| <= 16*127)
+    const uint32_t mp = __builtin_amdgcn_perm(0u, mins[t >> 1], (t & 1) ? 0x0C030C02u : 0x0C010C00u);
+    const uint32_t qp = __builtin_amdgcn_perm((uint32_t)A.Q[2 * t + 1], (uint32_t)A.Q[2 * t], 0x05040100u);
+    const int M = dot2_zero(mp, qp);
     const int j = t & 3;
     const double fj = j == 1 ? 0.25 : (j == 2 ? 0.0625 : 1.0);   // undo the in-place 4^j
     accS = __builtin_fma(A.D8[t] * fj, (double)S, accS);
