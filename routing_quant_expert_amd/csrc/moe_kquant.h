@@ -309,24 +309,31 @@ __device__ inline double dot_q3k(const uint8_t* p, const Act& A) {
     Ih[4] = first ? dot4_zero((int)v2, (int)A.a[32 * h + 16 + t4]) : __builtin_amdgcn_sdot4((int)v2, (int)A.a[32 * h + 16 + t4], Ih[4], false);
     Ih[6] = first ? dot4_zero((int)v3, (int)A.a[32 * h + 24 + t4]) : __builtin_amdgcn_sdot4((int)v3, (int)A.a[32 * h + 24 + t4], Ih[6], false);
   }
+  // The 6-bit scales u of sub-blocks 4k..4k+3 as the signed bytes 4*(u - 32) of
+  // one word: the low nibble (bytes 0-3 of scales[], low nibbles for k < 2,
+  // high for k >= 2) to bits 2-5, its two high bits (bits 2k, 2k+1 of bytes
+  // 8-11) to bits 6-7, then bit 7 flipped (4u - 128 in two's complement).
+  uint32_t P[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = (k < 2 ? (sc[k & 1] << 2) : (sc[k & 1] >> 2)) & 0x3C3C3C3Cu;
+    const uint32_t hi = sc[2] << (6 - 2 * k);
+    P[k] = ((hi & 0xC0C0C0C0u) | lo) ^ 0x80808080u;
+  }
   double acc = 0.0;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int j = t & 3;
     const int fj = j == 1 ? 4 : (j == 2 ? 16 : 1);
-    int S = 0;
+    int S4 = 0;   // 4 * the sub-block pair's integer sum
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int s = 2 * t + k;
-      const uint32_t lo_b = (sc[(s & 7) >> 2] >> (8 * (s & 3))) & 0xFFu;   // byte s (s<8) or s-8
-      const uint32_t lo = s < 8 ? (lo_b & 15u) : (lo_b >> 4);
-      const uint32_t hi_b = (sc[2] >> (8 * (s & 3))) & 0xFFu;               // byte 8 + s%4
-      const uint32_t hi = (hi_b >> (2 * (s >> 2))) & 3u;
-      const int us = (int)(lo | (hi << 4)) - 32;
-      S = mad24(us, I[s] - 4 * fj * A.Q[s], S);
+      const int sc4 = (int)(int8_t)(P[s >> 2] >> (8 * (s & 3)));
+      S4 = mad24(sc4, I[s] - 4 * fj * A.Q[s], S4);
     }
     const double fjd = j == 1 ? 0.25 : (j == 2 ? 0.0625 : 1.0);
-    acc = __builtin_fma(A.D8[t] * fjd, (double)S, acc);
+    acc = __builtin_fma(A.D8[t] * (0.25 * fjd), (double)S4, acc);   // the power of two exactly undone
   }
   return fp16_f64(dbits) * acc;
 }
