@@ -3,9 +3,9 @@ oracle on the same bytes: Q2_K sub-block scales and mins of 15 (every byte
 0xFF, or random scales under mins of 15), Q3_K 6-bit scales of 63 and 0 (the
 signed extremes +31 and -32) or random, hmask all clear or all set, and
 tokens whose q8_1 codes are +127 throughout (per-16 code sums of 2,032, the
-largest the activation sums take) or +-127 with random signs. Both the
-single-token kernels (m = 1) and the multi-token ones (m = 5) run
-[k-quant block formats: Q2_K 84 bytes (scales[16], qs[64], d, dmin), Q3_K
+largest the activation sums take) or +-127 with random signs. The
+single-token kernels (m = 1), the multi-token ones (m = 5) and the prefill
+ones (m = 40) all run [k-quant block formats: Q2_K 84 bytes (scales[16], qs[64], d, dmin), Q3_K
 110 bytes (hmask[32], qs[64], scales[12], d)]."""
 import numpy as np
 import pytest
@@ -67,7 +67,7 @@ def crafted_layer():
     return sh, dl, host, gw, rng
 
 
-@pytest.mark.parametrize("m", [1, 5])
+@pytest.mark.parametrize("m", [1, 5, 40])
 def test_layer_on_kquant_range_ends(crafted_layer, m):
     sh, dl, host, gw, rng = crafted_layer
     x = _tokens(sh, m, rng)
